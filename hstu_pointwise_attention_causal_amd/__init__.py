@@ -1,0 +1,20 @@
+"""MI355X (gfx950) HSTU hot path: causal pointwise aggregated attention over
+jagged sequences, its backward, and one HSTU layer, behind the C ABI of
+``libhstu.so`` (declared in ``include/hstu.h``).
+
+The Python functions below only marshal torch tensors into that ABI. The
+library is loaded on first use and its absence is an error: there is no CPU
+or PyTorch fallback.
+"""
+
+from ._lib import HstuError, load  # noqa: F401
+from .ops import (  # noqa: F401
+    attn_bwd,
+    attn_fwd,
+    attn_workspace_size,
+    layer_fwd,
+    make_layer_params,
+)
+
+__all__ = ["HstuError", "load", "attn_fwd", "attn_bwd", "attn_workspace_size", "layer_fwd",
+           "make_layer_params"]

@@ -1,0 +1,51 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hstu {
+
+// ---------------------------------------------------------------- work list
+struct WorklistLayout {
+  int num_levels = 0;   // ceil(T/BM) + 1
+  int64_t capacity = 0; // upper bound on the number of items
+  size_t hdr_off = 0, hist_off = 0, level_start_off = 0, fill_off = 0, tile_base_off = 0,
+         items_off = 0;
+  size_t bytes = 0;
+};
+
+WorklistLayout worklist_layout(int B, int64_t T, int H, int BM);
+hipError_t launch_build_worklist(const int64_t* off, int B, int H, int BM, const WorklistLayout& L,
+                                 char* ws, hipStream_t stream);
+
+// Query-tile height shared by every attention kernel and the work list.
+constexpr int kAttnBM = 128;
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t ldq, ldk, ldv;
+  void* o;         // forward output
+  int64_t ldo;
+  const int64_t* off;
+  const int64_t* ts;        // may be NULL
+  const float* pos_table;   // may be NULL
+  int pos_buckets;
+  const float* time_table;  // may be NULL
+  int time_buckets;
+  float alpha;
+  float divisor;
+  int num_heads;
+  const void* items;        // WorkItem list
+  const int* item_count;
+  int64_t capacity;
+};
+
+hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, int dqk, int dv, hipStream_t stream);
+
+}  // namespace hstu

@@ -1,0 +1,175 @@
+// Per-tile work list of the jagged attention kernels.
+//
+// A work item is one (sequence b, head h, query tile qt) with qt < ceil(n_b/BM).
+// Key tiles above the diagonal of a query tile are never visited by the
+// attention kernels (their loop stops at the diagonal), so fully masked
+// upper-triangle tiles cost nothing. Items are emitted longest-first: the cost
+// of query tile qt is proportional to qt + 1 key tiles, so the list is ordered
+// by qt descending ("levels"). The hardware dispatcher hands blocks to compute
+// units in block order, which makes this a longest-processing-time-first
+// schedule over a dynamic pool of compute units.
+//
+// The builder runs as ONE workgroup, on the stream of the attention call,
+// entirely on device: the host never reads the offsets.
+#include "common.h"
+#include "launch.h"
+
+namespace hstu {
+
+namespace {
+
+constexpr int kBuildThreads = 1024;
+
+// Inclusive scan over the block (kBuildThreads threads); returns the inclusive
+// prefix of `v` and writes the block total to *total.
+__device__ int block_inclusive_scan(int v, int* total) {
+  __shared__ int wave_sums[kBuildThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wave_sums[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int s = lane < kBuildThreads / 64 ? wave_sums[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(s, o, 64);
+      if (lane >= o) s += y;
+    }
+    if (lane < kBuildThreads / 64) wave_sums[lane] = s;
+  }
+  __syncthreads();
+  int prefix = wave > 0 ? wave_sums[wave - 1] : 0;
+  *total = wave_sums[kBuildThreads / 64 - 1];
+  __syncthreads();
+  return x + prefix;
+}
+
+__global__ __launch_bounds__(kBuildThreads) void build_worklist_kernel(
+    const int64_t* __restrict__ off, int B, int H, int BM, int num_levels,
+    int* __restrict__ hdr, int* __restrict__ hist, int* __restrict__ level_start,
+    int* __restrict__ fill, int* __restrict__ tile_base, WorkItem* __restrict__ items) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i <= num_levels; i += kBuildThreads) {
+    hist[i] = 0;
+    fill[i] = 0;
+  }
+  __syncthreads();
+
+  // 1. tiles per sequence, histogram of tile counts, and the exclusive scan of
+  //    tile counts over sequences (tile_base) for the flat pass below.
+  int carry = 0;
+  for (int b0 = 0; b0 < B; b0 += kBuildThreads) {
+    int b = b0 + tid;
+    int nt = 0;
+    if (b < B) {
+      int64_t n = off[b + 1] - off[b];
+      nt = n <= 0 ? 0 : static_cast<int>((n + BM - 1) / BM);
+      nt = min(nt, num_levels);
+      atomicAdd(&hist[nt], 1);
+    }
+    int chunk_total;
+    int incl = block_inclusive_scan(nt, &chunk_total);
+    if (b < B) tile_base[b] = carry + incl - nt;
+    carry += chunk_total;
+  }
+  const int total_tiles = carry;
+  if (tid == 0) tile_base[B] = total_tiles;
+  __syncthreads();
+
+  // 2. cnt[qt] = #sequences with more than qt tiles = sum_{m > qt} hist[m];
+  //    level_start[qt] = H * sum_{qt' > qt} cnt[qt'] (levels laid out from the
+  //    top level down). Two suffix scans, done as prefix scans over the
+  //    reversed level index r = num_levels - 1 - qt.
+  carry = 0;
+  for (int r0 = 0; r0 < num_levels; r0 += kBuildThreads) {
+    int r = r0 + tid;
+    int qt = num_levels - 1 - r;
+    int h = (r < num_levels)
+                ? __hip_atomic_load(&hist[qt + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                : 0;
+    int chunk_total;
+    int incl = block_inclusive_scan(h, &chunk_total);
+    if (r < num_levels) level_start[qt] = carry + incl;  // cnt[qt], stored temporarily
+    carry += chunk_total;
+  }
+  __syncthreads();
+  carry = 0;
+  for (int r0 = 0; r0 < num_levels; r0 += kBuildThreads) {
+    int r = r0 + tid;
+    int qt = num_levels - 1 - r;
+    int c = (r < num_levels) ? level_start[qt] : 0;
+    int chunk_total;
+    int incl = block_inclusive_scan(c, &chunk_total);
+    __syncthreads();
+    if (r < num_levels) level_start[qt] = H * (carry + incl - c);
+    carry += chunk_total;
+  }
+  __syncthreads();
+
+  // 3. flat pass over all (sequence, tile) pairs: place the H items of each.
+  for (int f = tid; f < total_tiles; f += kBuildThreads) {
+    int lo = 0, hi = B;  // largest b with tile_base[b] <= f
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (tile_base[mid] <= f) lo = mid; else hi = mid;
+    }
+    // skip empty sequences that share tile_base with the next one
+    int b = lo;
+    int qt = f - tile_base[b];
+    int slot = atomicAdd(&fill[qt], 1);
+    int base = level_start[qt] + slot * H;
+    for (int h = 0; h < H; ++h) {
+      WorkItem w;
+      w.seq = b;
+      w.packed = qt | (h << 20);
+      items[base + h] = w;
+    }
+  }
+  if (tid == 0) {
+    hdr[0] = total_tiles * H;
+    hdr[1] = 0;
+  }
+}
+
+}  // namespace
+
+WorklistLayout worklist_layout(int B, int64_t T, int H, int BM) {
+  WorklistLayout L;
+  int64_t levels = (T + BM - 1) / BM + 1;
+  int64_t cap_tiles = (T + static_cast<int64_t>(B) * (BM - 1)) / BM + 1;
+  L.num_levels = static_cast<int>(levels);
+  L.capacity = cap_tiles * H;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  L.hdr_off = take(16);
+  L.hist_off = take(sizeof(int) * (levels + 1));
+  L.level_start_off = take(sizeof(int) * (levels + 1));
+  L.fill_off = take(sizeof(int) * (levels + 1));
+  L.tile_base_off = take(sizeof(int) * (static_cast<size_t>(B) + 1));
+  L.items_off = take(sizeof(WorkItem) * static_cast<size_t>(L.capacity));
+  L.bytes = off;
+  return L;
+}
+
+hipError_t launch_build_worklist(const int64_t* off, int B, int H, int BM, const WorklistLayout& L,
+                                 char* ws, hipStream_t stream) {
+  hipLaunchKernelGGL(build_worklist_kernel, dim3(1), dim3(kBuildThreads), 0, stream, off, B, H, BM,
+                     L.num_levels - 1, reinterpret_cast<int*>(ws + L.hdr_off),
+                     reinterpret_cast<int*>(ws + L.hist_off),
+                     reinterpret_cast<int*>(ws + L.level_start_off),
+                     reinterpret_cast<int*>(ws + L.fill_off),
+                     reinterpret_cast<int*>(ws + L.tile_base_off),
+                     reinterpret_cast<WorkItem*>(ws + L.items_off));
+  return hipGetLastError();
+}
+
+}  // namespace hstu

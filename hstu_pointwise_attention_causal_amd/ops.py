@@ -1,0 +1,194 @@
+"""Thin PyTorch binding over the C ABI (argument marshalling only).
+
+PyTorch provides device memory and the current stream; every step of the
+computation runs in the HIP kernels of libhstu.so. Functions keep the names
+of the C entry points without the ``hstu_`` prefix.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DT = {torch.bfloat16: _lib.HSTU_BF16, torch.float32: _lib.HSTU_F32}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _token_view(name: str, t: torch.Tensor, H: int):
+    """Check a [T, H, d] view whose head/feature axes are contiguous; return (d, ld)."""
+    if t.dim() != 3 or t.shape[1] != H:
+        raise ValueError(f"{name} must be [T, {H}, d], got {tuple(t.shape)}")
+    d = t.shape[2]
+    if t.shape[0] == 0:
+        return d, H * d
+    if t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != d):
+        raise ValueError(f"{name}: heads and features must be contiguous inside a token row")
+    return d, t.stride(0)
+
+
+def _jagged(seq_offsets: torch.Tensor, total_tokens: int, timestamps: Optional[torch.Tensor]):
+    if seq_offsets.dtype != torch.int64 or not seq_offsets.is_contiguous():
+        raise ValueError("seq_offsets must be a contiguous int64 tensor")
+    if timestamps is not None and (timestamps.dtype != torch.int64 or not timestamps.is_contiguous()):
+        raise ValueError("timestamps must be a contiguous int64 tensor")
+    j = _lib.Jagged()
+    j.num_seqs = seq_offsets.numel() - 1
+    j.total_tokens = total_tokens
+    j.seq_offsets = seq_offsets.data_ptr() if seq_offsets.numel() else None
+    j.timestamps = timestamps.data_ptr() if timestamps is not None else None
+    return j
+
+
+def _bias(pos_table: Optional[torch.Tensor], time_table: Optional[torch.Tensor]):
+    b = _lib.Bias()
+    for t, name in ((pos_table, "pos_table"), (time_table, "time_table")):
+        if t is not None and (t.dtype != torch.float32 or t.dim() != 2 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 [H, buckets] tensor")
+    if pos_table is not None:
+        b.pos_table = pos_table.data_ptr()
+        b.pos_buckets = pos_table.shape[1]
+    if time_table is not None:
+        b.time_table = time_table.data_ptr()
+        b.time_buckets = time_table.shape[1]
+    return b
+
+
+def _desc(H, dqk, dv, dtype, alpha, divisor):
+    d = _lib.AttnDesc()
+    d.num_heads, d.dqk, d.dv = H, dqk, dv
+    d.dtype = _DT[dtype]
+    d.qk_scale = float(alpha)
+    d.divisor = float(divisor)
+    return d
+
+
+def attn_workspace_size(num_heads: int, dqk: int, dv: int, dtype: torch.dtype, num_seqs: int,
+                        total_tokens: int, is_bwd: bool = False, pos_buckets: int = 0,
+                        time_buckets: int = 0) -> int:
+    lib = _lib.load()
+    d = _desc(num_heads, dqk, dv, dtype, 1.0, 0.0)
+    j = _lib.Jagged()
+    j.num_seqs, j.total_tokens = num_seqs, total_tokens
+    j.seq_offsets = 16 if num_seqs else None   # only non-NULL-ness is read
+    b = _lib.Bias()
+    if pos_buckets:
+        b.pos_table, b.pos_buckets = 16, pos_buckets
+    if time_buckets:
+        b.time_table, b.time_buckets = 16, time_buckets
+        j.timestamps = 16
+    out = ctypes.c_size_t(0)
+    _lib.check(lib.hstu_attn_workspace_size(ctypes.byref(d), ctypes.byref(j), ctypes.byref(b),
+                                            int(is_bwd), ctypes.byref(out)))
+    return out.value
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets: torch.Tensor, *,
+             timestamps: Optional[torch.Tensor] = None, pos_table: Optional[torch.Tensor] = None,
+             time_table: Optional[torch.Tensor] = None, alpha: float = 1.0, divisor: float = 0.0,
+             out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """hstu_attn_fwd on [T, H, d] tensors (bf16 or fp32) of one jagged batch."""
+    lib = _lib.load()
+    T, H = q.shape[0], q.shape[1]
+    dqk, ldq = _token_view("q", q, H)
+    _, ldk = _token_view("k", k, H)
+    dv, ldv = _token_view("v", v, H)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=v.dtype, device=v.device)
+    _, ldo = _token_view("o", out, H)
+    d = _desc(H, dqk, dv, q.dtype, alpha, divisor)
+    j = _jagged(seq_offsets, T, timestamps)
+    b = _bias(pos_table, time_table)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.hstu_attn_workspace_size(ctypes.byref(d), ctypes.byref(j), ctypes.byref(b), 0,
+                                            ctypes.byref(need)))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
+    _lib.check(lib.hstu_attn_fwd(ctypes.byref(d), ctypes.byref(j), ctypes.byref(b),
+                                 _ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv, _ptr(out), ldo,
+                                 _ptr(workspace), workspace.numel(), _stream_handle(q.device)))
+    return out
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tensor,
+             seq_offsets: torch.Tensor, *, timestamps: Optional[torch.Tensor] = None,
+             pos_table: Optional[torch.Tensor] = None, time_table: Optional[torch.Tensor] = None,
+             alpha: float = 1.0, divisor: float = 0.0, workspace: Optional[torch.Tensor] = None):
+    """hstu_attn_bwd: returns (dq, dk, dv, d_pos_table or None, d_time_table or None)."""
+    lib = _lib.load()
+    T, H = q.shape[0], q.shape[1]
+    dqk, ldq = _token_view("q", q, H)
+    _, ldk = _token_view("k", k, H)
+    dv_, ldv = _token_view("v", v, H)
+    _, lddo = _token_view("d_o", d_o, H)
+    dq = torch.empty((T, H, dqk), dtype=q.dtype, device=q.device)
+    dk = torch.empty((T, H, dqk), dtype=q.dtype, device=q.device)
+    dvv = torch.empty((T, H, dv_), dtype=q.dtype, device=q.device)
+    dP = torch.empty_like(pos_table) if pos_table is not None else None
+    dTt = torch.empty_like(time_table) if time_table is not None else None
+    d = _desc(H, dqk, dv_, q.dtype, alpha, divisor)
+    j = _jagged(seq_offsets, T, timestamps)
+    b = _bias(pos_table, time_table)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.hstu_attn_workspace_size(ctypes.byref(d), ctypes.byref(j), ctypes.byref(b), 1,
+                                            ctypes.byref(need)))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
+    _lib.check(lib.hstu_attn_bwd(ctypes.byref(d), ctypes.byref(j), ctypes.byref(b),
+                                 _ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv, _ptr(d_o), lddo,
+                                 _ptr(dq), dqk * H, _ptr(dk), dqk * H, _ptr(dvv), dv_ * H,
+                                 _ptr(dP), _ptr(dTt), _ptr(workspace), workspace.numel(),
+                                 _stream_handle(q.device)))
+    return dq, dk, dvv, dP, dTt
+
+
+def make_layer_params(embed_dim: int, num_heads: int, dqk: int, dv: int, *, w_uvqk, w_out,
+                      ln_in_gamma, ln_in_beta, ln_out_gamma, ln_out_beta, b_uvqk=None, b_out=None,
+                      pos_table=None, time_table=None, ln_eps: float = 1e-6, alpha: float = 1.0,
+                      divisor: float = 0.0):
+    """Build the hstu_layer_params_t for device tensors (kept alive by the caller)."""
+    p = _lib.LayerParams()
+    p.embed_dim = embed_dim
+    p.attn = _desc(num_heads, dqk, dv, torch.bfloat16, alpha, divisor)
+    p.ln_eps = float(ln_eps)
+    for name, t in (("ln_in_gamma", ln_in_gamma), ("ln_in_beta", ln_in_beta), ("w_uvqk", w_uvqk),
+                    ("b_uvqk", b_uvqk), ("ln_out_gamma", ln_out_gamma), ("ln_out_beta", ln_out_beta),
+                    ("w_out", w_out), ("b_out", b_out)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        setattr(p, name, None if t is None else t.data_ptr())
+    p.bias = _bias(pos_table, time_table)
+    return p
+
+
+def layer_fwd(x: torch.Tensor, seq_offsets: torch.Tensor, params: "_lib.LayerParams", *,
+              timestamps: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+              uvqk_out: Optional[torch.Tensor] = None, o_out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """hstu_layer_fwd on a bf16 [T, D] input; returns X'."""
+    lib = _lib.load()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [T, D] tensor")
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    j = _jagged(seq_offsets, T, timestamps)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.hstu_layer_workspace_size(ctypes.byref(params), ctypes.byref(j), ctypes.byref(need)))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=x.device)
+    _lib.check(lib.hstu_layer_fwd(ctypes.byref(params), ctypes.byref(j), _ptr(x), _ptr(out),
+                                  _ptr(uvqk_out), _ptr(o_out), _ptr(workspace), workspace.numel(),
+                                  _stream_handle(x.device)))
+    return out

@@ -1,0 +1,203 @@
+/*
+ * hstu.h -- C ABI of the MI355X (gfx950) HSTU hot-path library (libhstu.so).
+ *
+ * What is computed (by page title and section):
+ *   - neurarch "HSTU (Generative Recommender)" model card, "Exported PyTorch",
+ *     HSTUBlock: one fused linear map to u|v|q|k (in that order), per-head
+ *     views, and pointwise aggregation: SiLU(q.k^T) divided by the sequence
+ *     length, masked to j <= i after the SiLU, times v. No softmax.
+ *   - briansu.co "HSTU: Hierarchical Sequential Transduction Units", section 3
+ *     "How it works": relative position and relative time biases enter the
+ *     pointwise SiLU attention; a layer is projection, aggregation, gated
+ *     transformation.
+ *   - daiwk.github.io HSTU reproduction notes, "core formula" and flowchart:
+ *     U,V,Q,K = SiLU(Norm(X) W_uvqk); causal pointwise aggregation with
+ *     relative bias; post-pooling normalisation; U gate; output projection
+ *     with residual.
+ *
+ * For sequence b (tokens off[b] .. off[b+1]-1, length n), head h and
+ * positions i, j inside the sequence:
+ *     S_ij = qk_scale * q_i.k_j + P[h][min(i-j, Bp-1)]
+ *            + Tt[h][min(floor(log2(1 + max(t_i - t_j, 0))), Bt-1)]
+ *     A_ij = SiLU(S_ij) / N  (j <= i),  0 (j > i);   O_i = sum_j A_ij v_j
+ * with N = n (divisor <= 0) or N = divisor (divisor > 0).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer (HBM of the current HIP
+ *     device); descriptors and the size out-parameters are HOST memory.
+ *   - Token-major tensors are row-major [T, H, d]: token t of head h starts at
+ *     element t*ld + h*d, the d elements of a head are contiguous, ld is the
+ *     row stride in elements (ld >= H*d). q, k, v, u may therefore be column
+ *     views of one packed [T, H(2dv+2dqk)] buffer.
+ *   - The caller owns every buffer, including the workspace; the library
+ *     allocates no device memory and keeps no per-call state.
+ *   - Calls are enqueued on `hip_stream` (a hipStream_t, NULL = default
+ *     stream) and return without synchronising. A non-OK status means nothing
+ *     was enqueued, except HSTU_E_HIP (a launch failed; hstu_last_error()
+ *     has the HIP message). Device faults surface at the caller's next sync.
+ *   - No exception or abort crosses the ABI. Calls on distinct streams with
+ *     distinct workspaces and outputs are independent and thread-safe.
+ *   - Outputs must not alias inputs (HSTU_E_ALIAS when the ranges overlap).
+ *   - Alignment: base pointers 16-byte aligned; ld a multiple of 8 elements
+ *     (bf16) or 4 elements (fp32) (HSTU_E_ALIGN).
+ */
+#ifndef HSTU_H_
+#define HSTU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_E_NULL = 1,        /* a required pointer is NULL */
+  HSTU_E_SHAPE = 2,       /* inconsistent or negative sizes */
+  HSTU_E_DTYPE = 3,       /* dtype not supported by this entry point */
+  HSTU_E_ALIGN = 4,       /* pointer or row stride misaligned */
+  HSTU_E_UNSUPPORTED = 5, /* head dims / bucket counts outside what is built */
+  HSTU_E_WORKSPACE = 6,   /* workspace smaller than *_workspace_size reports */
+  HSTU_E_ALIAS = 7,       /* an output overlaps an input */
+  HSTU_E_HIP = 8          /* a HIP call or kernel launch failed */
+} hstu_status_t;
+
+typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype_t;
+
+/* A jagged batch of B sequences packed along the token axis. */
+typedef struct {
+  int32_t num_seqs;           /* B >= 0 */
+  int64_t total_tokens;       /* T; must equal seq_offsets[B] (not checked on the host) */
+  const int64_t* seq_offsets; /* device [B+1]: off[0] = 0, non-decreasing; empty sequences allowed */
+  const int64_t* timestamps;  /* device [T] int64 seconds, or NULL (then no time bias);
+                                 pairwise gaps must fit in int64 */
+} hstu_jagged_t;
+
+/* Relative-attention bias tables (fp32, per head). Either may be NULL. */
+typedef struct {
+  const float* pos_table;     /* device [H, Bp] row-major; bucket min(i-j, Bp-1) */
+  int32_t pos_buckets;        /* Bp >= 1 when pos_table != NULL */
+  const float* time_table;    /* device [H, Bt]; bucket min(floor(log2(1+max(dt,0))), Bt-1);
+                                 needs hstu_jagged_t.timestamps */
+  int32_t time_buckets;       /* Bt >= 1 when time_table != NULL */
+} hstu_bias_t;
+
+typedef struct {
+  int32_t num_heads;          /* H >= 1 */
+  int32_t dqk;                /* attn_dim of the pages; built: 32, 64, 128 */
+  int32_t dv;                 /* linear_dim of the pages; built: dv == dqk */
+  hstu_dtype_t dtype;         /* element type of q, k, v, o (and dO, dq, dk, dv) */
+  float qk_scale;             /* alpha on q.k^T (1.0 in the pages' exported block) */
+  float divisor;              /* <= 0: divide sequence b's rows by its length n_b;
+                                 > 0: divide every row by this constant */
+} hstu_attn_desc_t;
+
+/* ---------------------------------------------------------------------------
+ * hstu_attn_workspace_size -- device workspace bytes needed by
+ * hstu_attn_fwd (is_bwd = 0) or hstu_attn_bwd (is_bwd != 0) for this shape.
+ * `bytes` is a host pointer. Depends only on (desc, num_seqs, total_tokens,
+ * bias bucket counts), never on device data. Errors: HSTU_E_NULL, HSTU_E_SHAPE.
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_attn_workspace_size(const hstu_attn_desc_t* desc, const hstu_jagged_t* jag,
+                                       const hstu_bias_t* bias, int is_bwd, size_t* bytes);
+
+/* ---------------------------------------------------------------------------
+ * hstu_attn_fwd -- causal pointwise aggregated attention over a jagged batch
+ * (neurarch model card, "Exported PyTorch", HSTUBlock.forward aggregation;
+ * briansu.co explainer section 3 for the relative position / time biases).
+ *
+ *   q [T,H,dqk] (row stride ldq), k [T,H,dqk] (ldk), v [T,H,dv] (ldv): inputs,
+ *   o [T,H,dv] (ldo): output, fully overwritten for every token of every
+ *   sequence; dtype per desc->dtype (HSTU_BF16: bf16 inputs, fp32 accumulate,
+ *   bf16 output; HSTU_F32: fp32 throughout). bias may be NULL (no bias).
+ *   workspace: device scratch of at least hstu_attn_workspace_size(...,0,...)
+ *   bytes (holds the per-tile work list); contents on entry are ignored.
+ * Errors: HSTU_E_NULL, HSTU_E_SHAPE, HSTU_E_DTYPE, HSTU_E_ALIGN,
+ *   HSTU_E_UNSUPPORTED, HSTU_E_WORKSPACE, HSTU_E_ALIAS, HSTU_E_HIP.
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_attn_fwd(const hstu_attn_desc_t* desc, const hstu_jagged_t* jag,
+                            const hstu_bias_t* bias,
+                            const void* q, int64_t ldq, const void* k, int64_t ldk,
+                            const void* v, int64_t ldv, void* o, int64_t ldo,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * hstu_attn_bwd -- gradients of sum(O * dO) for hstu_attn_fwd with the same
+ * inputs: with sig = 1/(1+e^-S), SiLU'(S) = sig (1 + S (1 - sig)), over pairs
+ * j <= i: dA_ij = dO_i.v_j, dS_ij = dA_ij SiLU'(S_ij)/N, dv_j = sum_i A_ij dO_i,
+ * dq_i = alpha sum_j dS_ij k_j, dk_j = alpha sum_i dS_ij q_i, and each bias
+ * table entry receives the sum of dS over the pairs that read it. (Derived from
+ * the forward definition above; the pages train all positions generatively,
+ * daiwk reproduction notes, core formula.)
+ *
+ *   d_o [T,H,dv] (lddo): upstream gradient (dtype per desc).
+ *   dq [T,H,dqk] (lddq), dk (lddk), dv [T,H,dv] (lddv): overwritten.
+ *   d_pos_table [H,Bp], d_time_table [H,Bt]: fp32, overwritten (not
+ *   accumulated); each must be non-NULL exactly when its table is.
+ *   workspace: at least hstu_attn_workspace_size(...,1,...) bytes.
+ * Errors: as hstu_attn_fwd. Results are deterministic run to run.
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_attn_bwd(const hstu_attn_desc_t* desc, const hstu_jagged_t* jag,
+                            const hstu_bias_t* bias,
+                            const void* q, int64_t ldq, const void* k, int64_t ldk,
+                            const void* v, int64_t ldv, const void* d_o, int64_t lddo,
+                            void* dq, int64_t lddq, void* dk, int64_t lddk,
+                            void* dv, int64_t lddv,
+                            float* d_pos_table, float* d_time_table,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Parameters of one HSTU layer (bf16 weights, fp32 norms and biases). Weight
+ * matrices use the nn.Linear layout [out_features, in_features] of the
+ * neurarch exported block (row-major, contiguous). */
+typedef struct {
+  int32_t embed_dim;          /* D; built: D % 64 == 0, D <= 4096 */
+  hstu_attn_desc_t attn;      /* dtype must be HSTU_BF16; dqk == dv == 128 built */
+  float ln_eps;               /* epsilon of both LayerNorms (1e-6 in the workloads) */
+  const float* ln_in_gamma;   /* device [D] */
+  const float* ln_in_beta;    /* device [D] */
+  const void* w_uvqk;         /* device bf16 [H(2dv+2dqk), D]; rows u | v | q | k, head-major inside */
+  const float* b_uvqk;        /* device [H(2dv+2dqk)] or NULL */
+  const float* ln_out_gamma;  /* device [H dv] */
+  const float* ln_out_beta;   /* device [H dv] */
+  const void* w_out;          /* device bf16 [D, H dv] */
+  const float* b_out;         /* device [D] or NULL */
+  hstu_bias_t bias;           /* this layer's relative-bias tables */
+} hstu_layer_params_t;
+
+/* ---------------------------------------------------------------------------
+ * hstu_layer_workspace_size -- device workspace bytes for hstu_layer_fwd.
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_layer_workspace_size(const hstu_layer_params_t* params,
+                                        const hstu_jagged_t* jag, size_t* bytes);
+
+/* ---------------------------------------------------------------------------
+ * hstu_layer_fwd -- one HSTU layer over a jagged batch (daiwk reproduction
+ * notes, flowchart and core formula; briansu.co explainer section 3):
+ *   G = SiLU(LN(X) W_uvqk^T + b_uvqk) split u|v|q|k;  O = attention(q,k,v);
+ *   Y = LN(O) * u (norm over the H dv features of a token);
+ *   X' = X + Y W_out^T + b_out.
+ *   x [T,D] bf16 (contiguous): input. y [T,D] bf16: output, must not alias x.
+ *   uvqk_out: optional bf16 [T, H(2dv+2dqk)] copy of G, or NULL.
+ *   o_out: optional bf16 [T, H dv] copy of O, or NULL.
+ *   workspace: at least hstu_layer_workspace_size bytes.
+ * Errors: as hstu_attn_fwd.
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_layer_fwd(const hstu_layer_params_t* params, const hstu_jagged_t* jag,
+                             const void* x, void* y, void* uvqk_out, void* o_out,
+                             void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Static English text of a status code. */
+const char* hstu_status_string(hstu_status_t status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* hstu_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t hstu_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H_ */

@@ -1,0 +1,147 @@
+"""GPU parity of hstu_attn_fwd against the fp64 oracle (through the C ABI)."""
+
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+from tests.helpers import TOL_BF16, TOL_F32, attn_inputs_on_device, rel_err, to_dev
+from workloads import make_workload
+from workloads.generators import _attn_recipe
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hstu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import hstu_pointwise_attention_causal_amd as pkg
+    pkg.load()
+    return pkg
+
+
+def _run(hstu, wl, **kw):
+    import torch
+    d = attn_inputs_on_device(wl)
+    o = hstu.attn_fwd(d["q"], d["k"], d["v"], d["seq_offsets"], timestamps=d["timestamps"],
+                      pos_table=d["pos_table"], time_table=d["time_table"], alpha=wl.alpha,
+                      divisor=wl.divisor, **kw)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy()
+
+
+def _oracle(wl):
+    return orc.attn_fwd(wl.q, wl.k, wl.v, wl.seq_offsets, alpha=wl.alpha, divisor=wl.divisor,
+                        pos_table=wl.pos_table, time_table=wl.time_table, timestamps=wl.timestamps)
+
+
+def test_fp32_workload_n256(hstu):
+    wl = make_workload("c0")
+    err = rel_err(_run(hstu, wl), _oracle(wl))
+    print(f"c0 fp32 rel err {err:.3e}")
+    assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("name", ["c3_small", "c4_small"])
+def test_bf16_reduced_workloads(hstu, name):
+    wl = make_workload(name)
+    err = rel_err(_run(hstu, wl), _oracle(wl))
+    print(f"{name} bf16 rel err {err:.3e}")
+    assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_head_dims_and_options(hstu, d, dtype):
+    wl = _attn_recipe("dims", 100 + d, [300, 5, 129], 2, d, dtype=dtype, Bp=40, Bt=20)
+    wl.alpha, wl.divisor = 0.75, 0.0
+    err = rel_err(_run(hstu, wl), _oracle(wl))
+    assert err <= (TOL_BF16 if dtype == "bf16" else TOL_F32), err
+    wl.divisor = 77.0
+    err = rel_err(_run(hstu, wl), _oracle(wl))
+    assert err <= (TOL_BF16 if dtype == "bf16" else TOL_F32), err
+
+
+def test_no_bias_and_large_position_table(hstu):
+    wl = _attn_recipe("nobias", 7, [700, 260], 2, 128, time=False, pos=False)
+    assert rel_err(_run(hstu, wl), _oracle(wl)) <= TOL_BF16
+    # more than 1024 position buckets: entries past the LDS-staged part come from HBM
+    wl = _attn_recipe("bigpos", 8, [1500], 1, 64, time=True, Bp=2000, Bt=200, table_std=0.5)
+    assert rel_err(_run(hstu, wl), _oracle(wl)) <= TOL_BF16
+
+
+def test_empty_and_single_token_sequences(hstu):
+    wl = _attn_recipe("edge", 9, [0, 1, 0, 0, 2, 0], 3, 64)
+    assert rel_err(_run(hstu, wl), _oracle(wl)) <= TOL_BF16
+    wl = _attn_recipe("allempty", 9, [0, 0], 3, 64)
+    out = _run(hstu, wl)
+    assert out.shape == (0, 3, 64)
+
+
+def test_nan_in_neighbour_sequence_does_not_leak(hstu):
+    import torch
+    wl = _attn_recipe("nan", 10, [200, 150, 90], 2, 128)
+    d = attn_inputs_on_device(wl)
+    for name in ("q", "k", "v"):
+        d[name][200:350] = float("nan")
+    o = hstu.attn_fwd(d["q"], d["k"], d["v"], d["seq_offsets"], timestamps=d["timestamps"],
+                      pos_table=d["pos_table"], time_table=d["time_table"])
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    ref = _oracle(wl)
+    keep = np.r_[0:200, 350:440]
+    assert np.all(np.isfinite(o[keep]))
+    assert rel_err(o[keep], ref[keep]) <= TOL_BF16
+
+
+def test_causality_bitwise_and_determinism(hstu):
+    import torch
+    wl = _attn_recipe("causal", 11, [500], 2, 128)
+    d = attn_inputs_on_device(wl)
+    args = dict(timestamps=d["timestamps"], pos_table=d["pos_table"], time_table=d["time_table"])
+    base = hstu.attn_fwd(d["q"], d["k"], d["v"], d["seq_offsets"], **args).clone()
+    again = hstu.attn_fwd(d["q"], d["k"], d["v"], d["seq_offsets"], **args)
+    torch.cuda.synchronize()
+    assert torch.equal(base, again)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    for cut in (0, 63, 200, 383):
+        q, k, v = d["q"].clone(), d["k"].clone(), d["v"].clone()
+        ts = d["timestamps"].clone()
+        sl = slice(cut + 1, 500)
+        for t in (q, k, v):
+            t[sl] += (torch.randn(t[sl].shape, generator=g) * 3).to(t.device, t.dtype)
+        ts[sl] += torch.randint(0, 10**6, ts[sl].shape, generator=g).to(ts.device)
+        o = hstu.attn_fwd(q, k, v, d["seq_offsets"], timestamps=ts, pos_table=d["pos_table"],
+                          time_table=d["time_table"])
+        torch.cuda.synchronize()
+        assert torch.equal(o[:cut + 1], base[:cut + 1]), cut
+
+
+def _sampled_rows(n, rng, extra=6):
+    fixed = [0, 1, 63, 64, 127, 128, 129, n // 2, n - 2, n - 1]
+    rows = sorted(set([r for r in fixed if 0 <= r < n] + list(rng.integers(0, n, size=extra))))
+    return rows
+
+
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_full_size_sampled_rows(hstu, name):
+    """Full-size workloads in the launch configuration the benchmark times;
+    sampled output rows of every (sequence, head) are recomputed one by one."""
+    wl = make_workload(name)
+    o = _run(hstu, wl)
+    rng = np.random.default_rng(0)
+    off = wl.seq_offsets
+    got, ref = [], []
+    seqs = range(wl.num_seqs) if wl.num_seqs <= 8 else rng.choice(wl.num_seqs, 8, replace=False)
+    for b in seqs:
+        n = int(off[b + 1] - off[b])
+        rows = _sampled_rows(n, rng)
+        for h in range(wl.num_heads):
+            ref.append(orc.attn_fwd_rows(wl.q, wl.k, wl.v, off, int(b), h, rows, alpha=wl.alpha,
+                                         divisor=wl.divisor, pos_table=wl.pos_table,
+                                         time_table=wl.time_table, timestamps=wl.timestamps))
+            got.append(o[off[b] + np.array(rows), h])
+    err = rel_err(np.concatenate(got), np.concatenate(ref))
+    print(f"{name} sampled rel err {err:.3e}")
+    assert err <= TOL_BF16
+    assert np.all(np.isfinite(o))
