@@ -61,6 +61,11 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # every kernel launched from host code must have its host stub in the library
+    nm = subprocess.run(["nm", "-C", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.strip() for ln in nm.stdout.splitlines() if "hstu::" in ln]
+    if missing:
+        raise RuntimeError("undefined library symbols after link:\n" + "\n".join(missing))
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH} from {len(srcs)} sources", file=sys.stderr)

@@ -159,6 +159,9 @@ hstu_status_t hstu_attn_fwd(const hstu_attn_desc_t* desc, const hstu_jagged_t* j
   a.items = ws + L.items_off;
   a.item_count = reinterpret_cast<const int*>(ws + L.hdr_off);
   a.capacity = L.capacity;
+  a.tile_base = reinterpret_cast<const int*>(ws + L.tile_base_off);
+  a.meta = ws + L.meta_off;
+  a.meta_blocks = L.meta_blocks;
   e = dt == HSTU_BF16 ? hstu::launch_attn_fwd_bf16(a, desc->dqk, desc->dv, stream)
                       : hstu::launch_attn_fwd_f32(a, desc->dqk, desc->dv, stream);
   if (e != hipSuccess) return hip_fail(e, "attention forward launch");

@@ -65,76 +65,133 @@ __device__ __forceinline__ float time_bias(const BiasLds& s, const AttnArgs& a, 
 // bf16 MFMA kernel
 // ============================================================================
 //
+// Data movement. K and V tiles go from HBM straight into LDS with
+// buffer_load ... lds (16 bytes per lane, no VGPR staging); a buffer resource
+// per tile bounds the reads to the sequence, so rows past its end arrive as
+// zeros. K rows are stored with their 16-byte chunks XOR-swizzled by the row
+// index (conflict-free ds_read_b128 of the MFMA A operand). V stays row-major,
+// chunks XOR-swizzled by 4 (row mod 4) so that the 4 rows x 4 chunks read by
+// 32 lanes fall in 16 distinct bank groups, and the B operand of P.V is read with
+// ds_read_b64_tr_b16: in each 16-lane group, lane 4k+q names 4 consecutive
+// dims of key row k and lane i receives that column (dim i) of all 4 rows, so
+// one transpose read yields 4 keys of one output column per lane.
+//
 // Relative bias per (wave, 32-key block). The wave's 32 query rows and the
-// block's 32 keys bound every pair's distance i - j and timestamp gap
-// t_i - t_j, so before touching the 1024 scores the wave classifies the block:
-//   kUniform  - one position bucket and one time bucket for every pair: the
-//               bias is a single constant c (most blocks away from the diagonal);
-//   kTwoTime  - one position bucket, time buckets c and c+1 only: bucket c+1
-//               exactly when t_i - t_j >= 2^(c+1) - 1, a compare and select;
-//   kGeneral  - per-pair position and time buckets looked up in LDS (blocks
-//               near the diagonal, the diagonal itself and sequence tails).
-// Every path adds the same fp32 bias value to the same fp32 score, so the
-// choice of path never changes a result bit (bitwise causality holds).
-// Scores and bias tables are pre-multiplied by log2(e) so that the SiLU is
-// x' / (1 + 2^-x') with one exp2 and one reciprocal; the factor is removed in
-// the output scale.
-enum BlockPath { kUniform = 0, kTwoTime = 1, kGeneral = 2, kGeneral64 = 3 };
+// block's 32 keys bound every pair's distance i - j and timestamp gap, so the
+// wave classifies the block from per-block metadata before touching scores:
+//   kUniform  - one position bucket and one time bucket: a constant bias;
+//   kTwoTime  - one position bucket, time buckets c and c+1: bucket c+1
+//               exactly when t_i - t_j >= 2^(c+1) - 1 (compare and select);
+//   kGeneral  - per-pair buckets looked up in LDS, plus the causal / sequence
+//               mask (diagonal and near-diagonal blocks, sequence tails).
+// All paths add the same fp32 bias value to the same fp32 score.
+//
+// SiLU. Scores and bias are pre-multiplied by log2(e): with x' = log2(e) x
+// the kernel needs g(x') = log2(e) SiLU(x) = x' / (1 + 2^-x'). Exactly, that
+// is one exp2 and one reciprocal (both quarter-rate on gfx950). When a row's
+// scores in an unmasked block are provably small -- |alpha| |q_i| max_j |k_j|
+// + max |bias table| <= 1.95 (Cauchy-Schwarz) -- g is evaluated as 0.5 x' + y P(y), y = x'^2,
+// with a cubic P fitted on |x| <= 2 (max error 2.8e-5 in x' units, two orders
+// of magnitude below the bf16 rounding of P); six full-rate FMA-class
+// operations instead. The choice is
+// made per query row from that row's own norm, the norms of keys before it and
+// a bound over the whole bias table, so a row's result never depends on later
+// tokens.
+enum BlockPath { kUniform = 0, kTwoTime = 1, kGeneral = 2 };
+enum PolyMode { kPolyAll = 0, kPolyNone = 1, kPolyMixed = 2 };
 
 constexpr int kPosLdsFast = 1024;
-constexpr int kInt32Max = 0x7fffffff;
+constexpr float kPolyC0 = 1.731778037e-01f, kPolyC1 = -6.804446619e-03f, kPolyC2 = 2.799578346e-04f,
+                kPolyC3 = -6.863766511e-06f;
+constexpr float kPolyBound = 1.95f * kLog2e;   // in x' units; fit range is 2 log2(e)
+constexpr int kRsrcFlags = 0x00020000;
 
-struct TileTime {
-  int32_t rel[kBN];         // min(t_k - kvmin(block of k), 2^31 - 1); 0 past the sequence
-  int64_t raw[kBN];         // t_k (for the 64-bit fallback)
-  int64_t kmin[kBN / 32];   // per 32-key block, over keys inside the sequence
-  int64_t kmax[kBN / 32];
-};
+__device__ __forceinline__ float silu2_exact(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x));
+}
+__device__ __forceinline__ float silu2_poly(float x) {
+  const float y = x * x;
+  float p = fmaf(y, kPolyC3, kPolyC2);
+  p = fmaf(y, p, kPolyC1);
+  p = fmaf(y, p, kPolyC0);
+  return fmaf(x, 0.5f, y * p);
+}
 
-__device__ __forceinline__ int64_t wave_min64(int64_t x, int width) {
-  for (int o = width / 2; o > 0; o >>= 1) {
-    int64_t y = __shfl_xor(x, o, width);
-    x = y < x ? y : x;
-  }
-  return x;
-}
-__device__ __forceinline__ int64_t wave_max64(int64_t x, int width) {
-  for (int o = width / 2; o > 0; o >>= 1) {
-    int64_t y = __shfl_xor(x, o, width);
-    x = y > x ? y : x;
-  }
-  return x;
-}
-__device__ __forceinline__ int uniform_int(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
-  uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
-  uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
   return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ lds_ptr_t to_lds(void* p) { return (lds_ptr_t)(p); }
+
+__device__ __forceinline__ bf16x4_t tr_read(const char* p) {
+  s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(bf16x4_t, r);
+}
+
+__device__ __forceinline__ uint32_t clamp_records(int64_t bytes) {
+  return bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes));
+}
+
+// Direct HBM -> LDS loads of one key tile (K, V and key timestamps). Kept out
+// of the kernel body as a device-only function (the LDS address-space
+// pointers have no host meaning).
+template <int KINST, int VINST>
+__device__ __forceinline__ void issue_tile_loads(const char* kbase, const char* vbase, const int64_t* tsbase,
+                                                 bool has_time, int64_t ldk, int64_t ldv, int n, int k0, int w,
+                                                 int lane, const uint32_t* koff, const uint32_t* voff, char* sk,
+                                                 char* sv, int64_t* st) {
+  __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(kbase + static_cast<int64_t>(k0) * ldk * 2), 0,
+      static_cast<int>(clamp_records(static_cast<int64_t>(n - k0) * ldk * 2)), kRsrcFlags);
+  __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(vbase + static_cast<int64_t>(k0) * ldv * 2), 0,
+      static_cast<int>(clamp_records(static_cast<int64_t>(n - k0) * ldv * 2)), kRsrcFlags);
+#pragma unroll
+  for (int i = 0; i < KINST; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(sk + (w * KINST + i) * 1024), 16, koff[i], 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < VINST; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(sv + (w * VINST + i) * 1024), 16, voff[i], 0, 0, 0);
+  if (has_time && w == 0 && lane < kBN / 2) {
+    __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int64_t*>(tsbase + k0), 0, static_cast<int>(clamp_records(static_cast<int64_t>(n - k0) * 8)),
+        kRsrcFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (lds_ptr_t)(st), 16, lane * 16, 0, 0, 0);
+  }
 }
 
 template <int DQK, int DV>
 struct FwdSmem {
-  static constexpr int KLD = DQK + 8;   // K row stride (bf16): rows shift by 16 B
-  static constexpr int VLD = kBN + 4;   // V^T row stride (bf16): rows shift by 8 B
-  __bf16 k[2][kBN * KLD];
-  __bf16 vt[2][DV * VLD];
-  TileTime tt[2];
+  __attribute__((aligned(16))) char k[2][kBN * DQK * 2];
+  __attribute__((aligned(16))) char v[2][kBN * DV * 2];
+  __attribute__((aligned(16))) int64_t t[2][kBN];
   float pos[kPosLdsFast];   // log2(e) * P[h][0 .. min(Bp, 1024))
   float time[kTimeLds];     // log2(e) * Tt[h][0 .. min(Bt, 64))
 };
 
+// Per-(wave, 32-key block) bias record. A wave classifies 64 key blocks at
+// once (one per lane) and each tile reads its two records back into scalar
+// registers with v_readlane, so the tile loop carries no LDS or memory round
+// trip for the classification. info bits: [1:0] BlockPath, [2] polynomial SiLU
+// valid for every row of the wave, [8:3] lower time bucket of a kTwoTime block.
+constexpr int kInfoPolyAll = 4;
+constexpr int kInfoMasked = 1 << 9;
+
 template <int DQK, int DV>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
-  static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims");
-  constexpr int KB = DQK / 16;   // k-blocks of the QK^T product
-  constexpr int NB = DV / 32;    // 32-wide column blocks of O
+  static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims");
+  constexpr int KB = DQK / 16;            // k-blocks of QK^T
+  constexpr int NB = DV / 32;             // 32-wide column blocks of O
+  constexpr int KCH = DQK / 8;            // 16-byte chunks per K row
+  constexpr int VCH = DV / 8;             // 16-byte chunks per V row
+  constexpr int KINST = KCH / 4;          // direct loads per wave per K tile (64 lanes x 16 B)
+  constexpr int VINST = VCH / 4;
   using Smem = FwdSmem<DQK, DV>;
-  constexpr int KLD = Smem::KLD, VLD = Smem::VLD;
-  constexpr int KCH = DQK / 8;                   // 16-byte chunks per K row
-  constexpr int KCH_PER_THREAD = kBN * KCH / kThreads;
-  constexpr int VCH = (kBN / 4) * (DV / 8);      // (4 keys x 8 dims) chunks of V
-  static_assert(kBN * KCH % kThreads == 0, "K tile split");
-  static_assert(VCH <= kThreads, "V tile split");
 
   const int item_idx = blockIdx.x;
   if (item_idx >= *a.item_count) return;
@@ -144,255 +201,358 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) 
   const int n = static_cast<int>(a.off[b + 1] - seq0);
   const int q0 = qt * kAttnBM;
 
-  __shared__ __align__(16) Smem sm;
+  __shared__ Smem sm;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, lr = l & 31, lh = l >> 5;
-  const int qa = q0 + w * 32;                 // first query row of this wave
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+  const int qa = q0 + 32 * w;                 // first query row of this wave
   const int qrow = qa + lr;                   // this lane's query column of S^T
-  const int wave_qmax = qa + 31;
   const bool has_time = a.time_table != nullptr;
   const bool has_pos = a.pos_table != nullptr;
   const int Bp = a.pos_buckets, Bt = a.time_buckets;
+  const bool pos_in_lds = Bp <= kPosLdsFast;
+  // metadata row of (head h, sequence b): 32-key blocks of the sequence start at 4 * tile_base[b]
+  const BlockMeta* meta_row = static_cast<const BlockMeta*>(a.meta) + h * a.meta_blocks + 4ll * a.tile_base[b];
 
-  // bias tables of head h, pre-multiplied by log2(e)
   if (has_pos) {
     for (int i = tid; i < min(Bp, kPosLdsFast); i += kThreads) sm.pos[i] = kLog2e * a.pos_table[h * Bp + i];
   }
   if (has_time) {
     for (int i = tid; i < min(Bt, kTimeLds); i += kThreads) sm.time[i] = kLog2e * a.time_table[h * Bt + i];
   }
+  const float pos_last = has_pos ? kLog2e * a.pos_table[h * Bp + Bp - 1] : 0.f;   // bias of far pairs
+  // |bias| <= cmax for every pair: max |L P[h][.]| + max |L Tt[h][.]| (NaN propagates)
+  float pmax = 0.f, tmax_ = 0.f;
+  bool bad = false;
+  if (has_pos)
+    for (int i = lane; i < Bp; i += 64) {
+      const float x = fabsf(kLog2e * a.pos_table[h * Bp + i]);
+      pmax = fmaxf(pmax, x);
+      bad |= !(x == x);
+    }
+  if (has_time)
+    for (int i = lane; i < min(Bt, kTimeLds); i += 64) {
+      const float x = fabsf(kLog2e * a.time_table[h * Bt + i]);
+      tmax_ = fmaxf(tmax_, x);
+      bad |= !(x == x);
+    }
+  for (int o = 1; o < 64; o <<= 1) {
+    pmax = fmaxf(pmax, __shfl_xor(pmax, o, 64));
+    tmax_ = fmaxf(tmax_, __shfl_xor(tmax_, o, 64));
+  }
+  const float cmax = __builtin_amdgcn_ballot_w64(bad) ? __builtin_nanf("") : pmax + tmax_;
 
   const __bf16* qp = static_cast<const __bf16*>(a.q);
-  const __bf16* kp = static_cast<const __bf16*>(a.k);
-  const __bf16* vp = static_cast<const __bf16*>(a.v);
-
   bf16x8_t qf[KB];
+  float qsq = 0.f;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     qf[kb] = qrow < n ? *reinterpret_cast<const bf16x8_t*>(qp + (seq0 + qrow) * a.ldq + h * DQK + kb * 16 + lh * 8)
                       : bf16x8_t{};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qsq = fmaf(static_cast<float>(qf[kb][i]), static_cast<float>(qf[kb][i]), qsq);
   }
-  // query timestamps: this lane's, and the wave's min / max over rows inside the sequence
-  int64_t tq = 0, wq_min = 0, wq_max = 0;
-  if (has_time) {
-    tq = qrow < n ? a.ts[seq0 + qrow] : 0;
-    wq_min = wave_min64(qrow < n ? tq : INT64_MAX, 64);
-    wq_max = wave_max64(qrow < n ? tq : INT64_MIN, 64);
-    wq_min = uniform_i64(wq_min);
-    wq_max = uniform_i64(wq_max);
+  qsq += __shfl_xor(qsq, 32, 64);
+  const float alpha_l = a.alpha * kLog2e;
+  const float qbound = fabsf(alpha_l) * __builtin_sqrtf(qsq);   // |alpha| log2(e) |q_i|
+  float qbound_max = qbound;
+  for (int o = 1; o < 64; o <<= 1) qbound_max = fmaxf(qbound_max, __shfl_xor(qbound_max, o, 64));
+  if (__builtin_amdgcn_ballot_w64(qbound != qbound)) qbound_max = __builtin_nanf("");
+  const int64_t tq = (has_time && qrow < n) ? a.ts[seq0 + qrow] : 0;
+  int64_t wq_min = 0, wq_max = 0;   // timestamps of this wave's query rows (metadata of its block)
+  if (has_time && qa < n) {
+    wq_min = uniform_i64(meta_row[qa / 32].tmin);
+    wq_max = uniform_i64(meta_row[qa / 32].tmax);
   }
 
   f32x16_t oacc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16_t{};
 
-  const float alpha_l = a.alpha * kLog2e;
   const int kv_end = min(n, q0 + kAttnBM);
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
-  // ---- register staging of one K/V tile (global -> registers -> LDS)
-  bf16x8_t kreg[KCH_PER_THREAD];
-  bf16x8_t vreg[4];
-  int64_t treg = 0;
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * kBN;
+  // ---- per-lane offsets of the direct loads (constant over tiles)
+  uint32_t koff[KINST], voff[VINST];
 #pragma unroll
-    for (int i = 0; i < KCH_PER_THREAD; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / KCH, c8 = c % KCH;
-      kreg[i] = (k0 + r < n) ? *reinterpret_cast<const bf16x8_t*>(kp + (seq0 + k0 + r) * a.ldk + h * DQK + c8 * 8)
-                             : bf16x8_t{};
-    }
-    if (tid < VCH) {
-      const int kq = tid % (kBN / 4), d0 = (tid / (kBN / 4)) * 8;
+  for (int i = 0; i < KINST; ++i) {
+    const int s = (w * KINST + i) * 64 + lane;
+    const int r = s / KCH, c = (s % KCH) ^ (r & (KCH - 1));
+    koff[i] = static_cast<uint32_t>(r * a.ldk * 2 + c * 16);
+  }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kv = k0 + kq * 4 + r;
-        vreg[r] = kv < n ? *reinterpret_cast<const bf16x8_t*>(vp + (seq0 + kv) * a.ldv + h * DV + d0) : bf16x8_t{};
-      }
-    }
-    if (has_time && tid < kBN) treg = (k0 + tid < n) ? a.ts[seq0 + k0 + tid] : 0;
+  for (int i = 0; i < VINST; ++i) {
+    const int s = (w * VINST + i) * 64 + lane;
+    const int r = s / VCH, c = (s % VCH) ^ ((4 * r) & (VCH - 1));
+    voff[i] = static_cast<uint32_t>(r * a.ldv * 2 + c * 16);
+  }
+  const char* kbase = static_cast<const char*>(a.k) + (seq0 * a.ldk + h * DQK) * 2;
+  const char* vbase = static_cast<const char*>(a.v) + (seq0 * a.ldv + h * DV) * 2;
+
+  auto issue_tile = [&] __device__(int kt, int buf) {
+    issue_tile_loads<KINST, VINST>(kbase, vbase, a.ts ? a.ts + seq0 : nullptr, has_time, a.ldk, a.ldv, n, kt * kBN,
+                                   w, lane, koff, voff, sm.k[buf], sm.v[buf], sm.t[buf]);
   };
-  auto store_tile = [&](int kt, int buf) {
-    const int k0 = kt * kBN;
+
+  // ---- LDS byte offsets of this lane's operand fragments inside one buffer
+  uint32_t k_lds[KB];                       // K row (kvb*32 + lr): + kvb * 32 * KCH * 16
 #pragma unroll
-    for (int i = 0; i < KCH_PER_THREAD; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / KCH, c8 = c % KCH;
-      *reinterpret_cast<bf16x8_t*>(&sm.k[buf][r * KLD + c8 * 8]) = kreg[i];
-    }
-    if (tid < VCH) {
-      const int kq = tid % (kBN / 4), d0 = (tid / (kBN / 4)) * 8;
+  for (int kb = 0; kb < KB; ++kb) k_lds[kb] = (lr * KCH + ((2 * kb + lh) ^ (lr & (KCH - 1)))) * 16;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  uint32_t v_lds[NB];                       // V row r1 = 4 lh + i16/4 (+ kvb*32 + kk*16, + 8 for the 2nd read)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        bf16x4_t col = {vreg[0][i], vreg[1][i], vreg[2][i], vreg[3][i]};
-        *reinterpret_cast<bf16x4_t*>(&sm.vt[buf][(d0 + i) * VLD + kq * 4]) = col;
-      }
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r1 = 4 * lh + (i16 >> 2);
+    const int c = nb * 4 + (g16 & 1) * 2 + ((i16 & 3) >> 1);
+    v_lds[nb] = (r1 * VCH + (c ^ ((4 * r1) & (VCH - 1)))) * 16 + (i16 & 1) * 8;
+  }
+
+  auto qk_block = [&] __device__(int buf, int kvb) {
+    f32x16_t s = f32x16_t{};
+    const char* kb0 = sm.k[buf] + kvb * 32 * KCH * 16;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kb0 + k_lds[kb]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], s, 0, 0, 0);
     }
-    if (has_time && tid < kBN) {  // wave 0: one key per lane, 32-key blocks = lane halves
-      const bool inside = k0 + tid < n;
-      const int64_t kmin = wave_min64(inside ? treg : INT64_MAX, 32);
-      const int64_t kmax = wave_max64(inside ? treg : INT64_MIN, 32);
-      const int64_t rel = treg - kmin;
-      sm.tt[buf].rel[tid] = inside ? static_cast<int32_t>(rel < kInt32Max ? rel : kInt32Max) : 0;
-      sm.tt[buf].raw[tid] = treg;
-      if ((tid & 31) == 0) {
-        sm.tt[buf].kmin[tid >> 5] = kmin;
-        sm.tt[buf].kmax[tid >> 5] = kmax;
+    return s;
+  };
+  auto pv_block = [&] __device__(int buf, int kvb, const float* p) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t pa;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pa[i] = static_cast<__bf16>(p[kk * 8 + i]);
+      const char* vb0 = sm.v[buf] + (kvb * 32 + kk * 16) * VCH * 16;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const bf16x4_t v0 = tr_read(vb0 + v_lds[nb]);
+        const bf16x4_t v1 = tr_read(vb0 + v_lds[nb] + 8 * VCH * 16);
+        const bf16x8_t vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, oacc[nb], 0, 0, 0);
       }
     }
   };
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0, 0);
-  }
+  // ---- classification of 64 key blocks (one per lane) for this wave's rows
+  int rec_info = kGeneral;
+  float rec_clo = 0.f, rec_chi = 0.f, rec_kmax = 0.f;
+  auto classify_window = [&] __device__(int win) {
+    const int ka = (win * 64 + lane) * 32;
+    int info = kGeneral;
+    float clo = 0.f, chi = 0.f, km = 0.f;
+    if (ka < n && ka <= qa + 31) {
+      const BlockMeta m = meta_row[win * 64 + lane];
+      km = m.kmax;
+      const bool need_mask = (ka + 31 > qa) || (ka + 31 >= n);
+      const bool pos_uniform = !has_pos || (qa - (ka + 31) >= Bp - 1);
+      int path = kGeneral, blo = 0;
+      clo = chi = pos_last;
+      if (!need_mask && pos_uniform) {
+        if (!has_time) {
+          path = kUniform;
+        } else {
+          blo = time_bucket64(wq_min - m.tmax, Bt);
+          const int bhi = time_bucket64(wq_max - m.tmin, Bt);
+          if (blo == bhi) {
+            path = kUniform;
+            clo = chi = pos_last + sm.time[blo];
+          } else if (bhi == blo + 1) {
+            path = kTwoTime;
+            clo = pos_last + sm.time[blo];
+            chi = pos_last + sm.time[bhi];
+          }
+        }
+      }
+      const bool polyall = !need_mask && fmaf(qbound_max, km, cmax) <= kPolyBound;
+      info = path | (polyall ? kInfoPolyAll : 0) | (blo << 3) | (need_mask ? kInfoMasked : 0);
+    }
+    rec_info = info;
+    rec_clo = clo;
+    rec_chi = chi;
+    rec_kmax = km;
+  };
+
+  // ---- scores -> P for one block (paths other than the fast tile)
+  auto eval_block = [&] __device__(const f32x16_t& s, int info, float c_lo, float c_hi, float kmax, int kt, int kvb,
+                                   int buf, float* p) {
+    // Polynomial or exact SiLU, decided per row from that row's norm, the
+    // block's largest key norm and the bias bound of the whole table -- never
+    // from the bias path, so a block's path (which may depend on later rows'
+    // timestamps) cannot change a row's result. Masked blocks (which hold
+    // keys after some rows) always take the exact form.
+    const int path = info & 3;
+    int mode = kPolyNone;
+    bool mine = false;
+    if (info & kInfoPolyAll) {
+      mode = kPolyAll;
+    } else if (!(info & kInfoMasked)) {
+      mine = fmaf(qbound, kmax, cmax) <= kPolyBound;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(mine);
+      mode = bal == 0 ? kPolyNone : kPolyMixed;
+    }
+    if (path != kGeneral) {
+      int64_t lim = 0;
+      if (path == kTwoTime) lim = tq - ((int64_t(1) << (((info >> 3) & 63) + 1)) - 1);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float c = c_lo;
+          if (path == kTwoTime) c = sm.t[buf][kvb * 32 + 8 * g + 4 * lh + e] <= lim ? c_hi : c_lo;
+          const float x = fmaf(s[4 * g + e], alpha_l, c);
+          float r;
+          if (mode == kPolyAll) r = silu2_poly(x);
+          else if (mode == kPolyNone) r = silu2_exact(x);
+          else r = mine ? silu2_poly(x) : silu2_exact(x);
+          p[4 * g + e] = r;
+        }
+      }
+    } else {
+      const int k0 = kt * kBN;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kvl = kvb * 32 + 8 * g + 4 * lh + e;
+          const int kv = k0 + kvl;
+          float c = 0.f;
+          if (has_pos) {
+            const int pb = min(max(qrow - kv, 0), Bp - 1);
+            c = pos_in_lds ? sm.pos[pb] : (pb < kPosLdsFast ? sm.pos[pb] : kLog2e * a.pos_table[h * Bp + pb]);
+          }
+          if (has_time) c += sm.time[time_bucket64(tq - sm.t[buf][kvl], Bt)];
+          const float x = fmaf(s[4 * g + e], alpha_l, c);
+          float r;
+          if (mode == kPolyAll) r = silu2_poly(x);
+          else if (mode == kPolyNone) r = silu2_exact(x);
+          else r = mine ? silu2_poly(x) : silu2_exact(x);
+          p[4 * g + e] = (kv <= qrow && kv < n) ? r : 0.0f;
+        }
+      }
+    }
+  };
+
+  // scores -> P for block kvb of tile kt, record in lane `rl` of the window
+  auto eval_tile_block = [&] __device__(const f32x16_t& s, bool active, int rl, int kt, int kvb, int buf,
+                                        float* p) {
+    const int info = __builtin_amdgcn_readlane(rec_info, rl);
+    const float clo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_clo), rl));
+    if (!active) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) p[j] = 0.f;
+    } else if ((info & 7) == (kUniform | kInfoPolyAll)) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) p[j] = silu2_poly(fmaf(s[j], alpha_l, clo));
+    } else {
+      const float chi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_chi), rl));
+      const float km = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_kmax), rl));
+      eval_block(s, info, clo, chi, km, kt, kvb, buf, p);
+    }
+  };
+
+  if (ntiles > 0) issue_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
     const int buf = kt & 1;
     const int k0 = kt * kBN;
-    if (kt + 1 < ntiles) load_tile(kt + 1);
+    if ((kt & 31) == 0) classify_window(kt >> 5);
+    if (kt + 1 < ntiles) issue_tile(kt + 1, buf ^ 1);
 
-    if (qa < n && k0 <= wave_qmax) {
-#pragma unroll
-      for (int kvb = 0; kvb < kBN / 32; ++kvb) {
-        const int ka = k0 + kvb * 32;
-        if (ka > wave_qmax || ka >= n) break;
-
-        // ---- classify the block (wave-uniform)
-        int path = kUniform;
-        float c_lo = 0.f, c_hi = 0.f;
-        int32_t lim = 0;      // kTwoTime: key rel <= lim  <=>  gap >= threshold
-        int32_t tq_rel = 0;   // kGeneral: clamp(t_q - kvmin, -1, 2^31 - 1)
-        int64_t kvmin = 0;
-        const bool need_mask = (ka + 31 > qa) || (ka + 31 >= n);
-        const bool pos_uniform = !has_pos || (qa - (ka + 31) >= Bp - 1);
-        if (has_pos) c_lo = (Bp - 1 < kPosLdsFast) ? sm.pos[Bp - 1] : kLog2e * a.pos_table[h * Bp + Bp - 1];
-        c_hi = c_lo;
-        if (has_time) {
-          kvmin = sm.tt[buf].kmin[kvb];
-          const int64_t kvmax = sm.tt[buf].kmax[kvb];
-          const int64_t dlo = wq_min - kvmax, dhi = wq_max - kvmin;
-          const int blo = time_bucket64(dlo, Bt), bhi = time_bucket64(dhi, Bt);
-          if (!pos_uniform || need_mask) {
-            path = dhi < int64_t(kInt32Max) - 1 ? kGeneral : kGeneral64;
-          } else if (blo == bhi) {
-            path = kUniform;
-            c_lo += sm.time[blo];
-            c_hi = c_lo;
-          } else if (bhi == blo + 1) {
-            path = kTwoTime;
-            const float base = c_lo;
-            c_lo = base + sm.time[blo];
-            c_hi = base + sm.time[bhi];
-            const int64_t thr = (int64_t(1) << (blo + 1)) - 1;     // gap >= thr <=> bucket bhi
-            const int64_t lim64 = tq - kvmin - thr;                  // per lane
-            lim = static_cast<int32_t>(lim64 < -1 ? -1 : (lim64 > kInt32Max - 1 ? kInt32Max - 1 : lim64));
-          } else {
-            path = dhi < int64_t(kInt32Max) - 1 ? kGeneral : kGeneral64;
-          }
-          const int64_t trel = tq - kvmin;
-          tq_rel = static_cast<int32_t>(trel < -1 ? -1 : (trel > kInt32Max ? kInt32Max : trel));
-        } else if (!pos_uniform || need_mask) {
-          path = kGeneral;
-        }
-        path = uniform_int(path);
-
-        // ---- S^T block = K Q^T
-        f32x16_t s = f32x16_t{};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&sm.k[buf][(kvb * 32 + lr) * KLD + kb * 16 + lh * 8]);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], s, 0, 0, 0);
-        }
-        // s[j] = S^T[key ka + 8(j/4) + 4 lh + j%4][query qrow]
-        float p[16];
-        if (path == kUniform) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float x = fmaf(s[j], alpha_l, c_lo);
-            p[j] = x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x));
-          }
-        } else if (path == kTwoTime) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int4 rk = *reinterpret_cast<const int4*>(&sm.tt[buf].rel[kvb * 32 + 8 * g + 4 * lh]);
-            const int32_t rr[4] = {rk.x, rk.y, rk.z, rk.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float c = rr[e] <= lim ? c_hi : c_lo;
-              const float x = fmaf(s[4 * g + e], alpha_l, c);
-              p[4 * g + e] = x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x));
-            }
-          }
-        } else {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            int32_t rr[4] = {0, 0, 0, 0};
-            if (has_time) {
-              const int4 rk = *reinterpret_cast<const int4*>(&sm.tt[buf].rel[kvb * 32 + 8 * g + 4 * lh]);
-              rr[0] = rk.x; rr[1] = rk.y; rr[2] = rk.z; rr[3] = rk.w;
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int kvl = kvb * 32 + 8 * g + 4 * lh + e;
-              const int kv = k0 + kvl;
-              float c = 0.f;
-              if (has_pos) {
-                const int pb = min(max(qrow - kv, 0), Bp - 1);
-                c = pb < kPosLdsFast ? sm.pos[pb] : kLog2e * a.pos_table[h * Bp + pb];
-              }
-              if (has_time) {
-                int tb;
-                if (path == kGeneral) {
-                  const int32_t dt = max(tq_rel - rr[e], 0);
-                  tb = min(31 - __clz(dt + 1), Bt - 1);
-                } else {
-                  tb = time_bucket64(tq - sm.tt[buf].raw[kvl], Bt);
-                }
-                c += sm.time[tb];
-              }
-              const float x = fmaf(s[4 * g + e], alpha_l, c);
-              const float pv = x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x));
-              p[4 * g + e] = (kv <= qrow && kv < n) ? pv : 0.0f;
-            }
-          }
-        }
-
-        // ---- O += P V  (A = P from the S^T registers, B = V^T from LDS)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          bf16x8_t pa;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) pa[i] = static_cast<__bf16>(p[kk * 8 + i]);
-          const int kbase = kvb * 32 + kk * 16;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const __bf16* vrow = &sm.vt[buf][(nb * 32 + lr) * VLD + kbase + 4 * lh];
-            const bf16x4_t v0 = *reinterpret_cast<const bf16x4_t*>(vrow);
-            const bf16x4_t v1 = *reinterpret_cast<const bf16x4_t*>(vrow + 8);
-            const bf16x8_t vb = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-            oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, oacc[nb], 0, 0, 0);
-          }
-        }
-      }
+    if (qa < n && k0 <= qa + 31) {
+      // Only the score -> P evaluation branches; both QK^T and P.V products are
+      // straight-line code, so O's accumulators never cross a branch merge.
+      // A block with no work for this wave (past its rows or past the
+      // sequence) takes P = 0.
+      const int l0 = (2 * kt) & 63;
+      const bool act0 = k0 < n;                               // k0 <= qa + 31 already holds
+      const bool act1 = (k0 + 32 <= qa + 31) && (k0 + 32 < n);
+      const f32x16_t s0 = qk_block(buf, 0);
+      const f32x16_t s1 = qk_block(buf, 1);
+      float p0[16], p1[16];
+      eval_tile_block(s0, act0, l0, kt, 0, buf, p0);
+      pv_block(buf, 0, p0);
+      eval_tile_block(s1, act1, l0 + 1, kt, 1, buf, p1);
+      pv_block(buf, 1, p1);
     }
-    if (kt + 1 < ntiles) store_tile(kt + 1, buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   // ---- epilogue: oacc[nb][j] = log2(e) * N * O[qa + 8(j/4) + 4 lh + j%4][nb*32 + lr]
   const float scale = (a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n)) / kLog2e;
-  __bf16* op = static_cast<__bf16*>(a.o);
+  __bf16* op = static_cast<__bf16*>(a.o) + (seq0 + qa) * a.ldo + h * DV + lr;
+  if (qa + 31 < n) {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int qpos = qa + 8 * (j >> 2) + 4 * lh + (j & 3);
-      if (qpos < n) op[(seq0 + qpos) * a.ldo + h * DV + nb * 32 + lr] = static_cast<__bf16>(oacc[nb][j] * scale);
+      for (int j = 0; j < 16; ++j)
+        op[(8 * (j >> 2) + 4 * lh + (j & 3)) * a.ldo + nb * 32] = static_cast<__bf16>(oacc[nb][j] * scale);
+  } else if (qa < n) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = 8 * (j >> 2) + 4 * lh + (j & 3);
+        if (qa + r < n) op[r * a.ldo + nb * 32] = static_cast<__bf16>(oacc[nb][j] * scale);
+      }
+  }
+}
+
+// ============================================================================
+// per-(head, 32-key block) metadata: max |k_j| and the timestamp range
+// ============================================================================
+template <int DQK>
+__global__ __launch_bounds__(256) void attn_block_meta_kernel(AttnArgs a) {
+  const int item_idx = blockIdx.x;
+  if (item_idx >= *a.item_count) return;
+  const WorkItem item = reinterpret_cast<const WorkItem*>(a.items)[item_idx];
+  const int b = item.seq, qt = item_qtile(item), h = item_head(item);
+  const int64_t seq0 = a.off[b];
+  const int n = static_cast<int>(a.off[b + 1] - seq0);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int jb = qt * 4 + w;                  // 32-key block of this wave
+  const int key = jb * 32 + (lane >> 1);      // two lanes per key, half the dims each
+  if (jb * 32 >= n) return;
+  const bool inside = key < n;
+  float sq = 0.f;
+  if (inside) {
+    const __bf16* kp = static_cast<const __bf16*>(a.k) + (seq0 + key) * a.ldk + h * DQK + (lane & 1) * (DQK / 2);
+#pragma unroll
+    for (int c = 0; c < DQK / 16; ++c) {
+      const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(kp + c * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sq = fmaf(static_cast<float>(x[i]), static_cast<float>(x[i]), sq);
     }
+  }
+  sq += __shfl_xor(sq, 1, 64);
+  float kn = __builtin_sqrtf(sq);
+  for (int o = 2; o < 64; o <<= 1) kn = fmaxf(kn, __shfl_xor(kn, o, 64));
+  // a NaN norm must keep the polynomial path off: max() drops NaN, so propagate it explicitly
+  const uint64_t nan_lanes = __builtin_amdgcn_ballot_w64(sq != sq);
+  if (nan_lanes) kn = __builtin_nanf("");
+  int64_t tmin = INT64_MAX, tmax = INT64_MIN;
+  if (a.ts) {
+    const int64_t t = inside ? a.ts[seq0 + key] : 0;
+    tmin = inside ? t : INT64_MAX;
+    tmax = inside ? t : INT64_MIN;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y0 = __shfl_xor(tmin, o, 64), y1 = __shfl_xor(tmax, o, 64);
+      tmin = y0 < tmin ? y0 : tmin;
+      tmax = y1 > tmax ? y1 : tmax;
+    }
+  }
+  if (lane == 0) {
+    BlockMeta m;
+    m.kmax = kn;
+    m.pad0 = 0.f;
+    m.tmin = tmin;
+    m.tmax = tmax;
+    m.pad1 = 0;
+    static_cast<BlockMeta*>(a.meta)[h * a.meta_blocks + 4ll * a.tile_base[b] + jb] = m;
   }
 }
 
@@ -479,7 +639,16 @@ hipError_t launch_items(K kernel, const AttnArgs& a, int threads, hipStream_t st
 
 }  // namespace
 
+hipError_t launch_attn_block_meta(const AttnArgs& a, int dqk, hipStream_t stream) {
+  if (dqk == 128) return launch_items(attn_block_meta_kernel<128>, a, 256, stream);
+  if (dqk == 64) return launch_items(attn_block_meta_kernel<64>, a, 256, stream);
+  if (dqk == 32) return launch_items(attn_block_meta_kernel<32>, a, 256, stream);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, hipStream_t stream) {
+  hipError_t e = launch_attn_block_meta(a, dqk, stream);
+  if (e != hipSuccess) return e;
   if (dqk == 128 && dv == 128) return launch_items(attn_fwd_bf16_kernel<128, 128>, a, kThreads, stream);
   if (dqk == 64 && dv == 64) return launch_items(attn_fwd_bf16_kernel<64, 64>, a, kThreads, stream);
   if (dqk == 32 && dv == 32) return launch_items(attn_fwd_bf16_kernel<32, 32>, a, kThreads, stream);

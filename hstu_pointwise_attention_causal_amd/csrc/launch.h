@@ -13,6 +13,9 @@ struct WorklistLayout {
   int64_t capacity = 0; // upper bound on the number of items
   size_t hdr_off = 0, hist_off = 0, level_start_off = 0, fill_off = 0, tile_base_off = 0,
          items_off = 0;
+  // per-(head, 32-key block) metadata of the bf16 forward: 4 blocks per query tile
+  size_t meta_off = 0;
+  int64_t meta_blocks = 0;   // blocks per head (row stride of the metadata array)
   size_t bytes = 0;
 };
 
@@ -43,7 +46,21 @@ struct AttnArgs {
   const void* items;        // WorkItem list
   const int* item_count;
   int64_t capacity;
+  const int* tile_base;     // [B+1] exclusive scan of query tiles per sequence
+  void* meta;               // BlockMeta [H][meta_blocks]
+  int64_t meta_blocks;
 };
+
+// Metadata of one 32-key block of one head: the largest key norm and the
+// timestamp range of the keys inside the sequence (32 bytes, DMA-friendly).
+struct BlockMeta {
+  float kmax;
+  float pad0;
+  int64_t tmin;
+  int64_t tmax;
+  int64_t pad1;
+};
+static_assert(sizeof(BlockMeta) == 32, "BlockMeta layout");
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int dqk, int dv, hipStream_t stream);

@@ -78,6 +78,17 @@ def test_empty_and_single_token_sequences(hstu):
     assert out.shape == (0, 3, 64)
 
 
+def test_large_and_mixed_score_ranges(hstu):
+    """Scores far outside the polynomial SiLU range (exact path), and a batch
+    where only some rows are large (per-row choice between the two forms)."""
+    wl = _attn_recipe("large", 12, [400, 77], 2, 128, qkv_std=1.0, table_std=1.0)
+    assert rel_err(_run(hstu, wl), _oracle(wl)) <= TOL_BF16
+    wl = _attn_recipe("mixed", 13, [640], 2, 128)
+    wl.q = wl.q.copy()
+    wl.q[::7] *= 4.0                         # every 7th row has a 4x larger norm
+    assert rel_err(_run(hstu, wl), _oracle(wl)) <= TOL_BF16
+
+
 def test_nan_in_neighbour_sequence_does_not_leak(hstu):
     import torch
     wl = _attn_recipe("nan", 10, [200, 150, 90], 2, 128)
