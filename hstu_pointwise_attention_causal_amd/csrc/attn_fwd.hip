@@ -8,7 +8,7 @@
 // aggregation; briansu.co explainer section 3 for the two relative biases).
 // There is no softmax, hence no running row maximum and no rescaling.
 //
-// bf16 kernel (MFMA): 4 waves, each owning 32 query rows. Per 64-key tile:
+// bf16 kernel (MFMA): 8 waves, each owning 32 query rows. Per 64-key tile:
 //   S^T[kv][q] = K Q^T       v_mfma_f32_32x32x16_bf16, A = K tile (LDS),
 //                            B = Q^T (registers, loaded once per item)
 //   P = mask(SiLU(S + bias)) in fp32 registers, packed to bf16
@@ -31,8 +31,9 @@ namespace hstu {
 namespace {
 
 constexpr int kBN = 64;            // keys per LDS tile
-constexpr int kWaves = 4;          // 32 query rows each
+constexpr int kWaves = kAttnBM / 32;   // 32 query rows each
 constexpr int kThreads = kWaves * 64;
+constexpr int kBufs = 4;           // K/V tiles in flight: loads run 3 tiles ahead
 constexpr int kPosLds = 1024;      // position-table entries staged in LDS
 constexpr int kTimeLds = 64;       // time buckets reachable with int64 gaps: 0..62
 
@@ -139,12 +140,16 @@ __device__ __forceinline__ uint32_t clamp_records(int64_t bytes) {
 
 // Direct HBM -> LDS loads of one key tile (K, V and key timestamps). Kept out
 // of the kernel body as a device-only function (the LDS address-space
-// pointers have no host meaning).
-template <int KINST, int VINST>
+// pointers have no host meaning). A tile of KCH (VCH) 1 KB instructions is
+// spread over the waves, instruction i issued by wave i % kWaves; wave 0 also
+// loads the timestamps. Every tile issues the same instructions, also a tile
+// past the sequence (all lanes out of range: zeros), so each wave's count of
+// loads per tile is a constant.
+template <int KCH, int VCH>
 __device__ __forceinline__ void issue_tile_loads(const char* kbase, const char* vbase, const int64_t* tsbase,
-                                                 bool has_time, int64_t ldk, int64_t ldv, int n, int k0, int w,
-                                                 int lane, const uint32_t* koff, const uint32_t* voff, char* sk,
-                                                 char* sv, int64_t* st) {
+                                                 int64_t ldk, int64_t ldv, int n, int k0, int w, int lane,
+                                                 const uint32_t* koff, const uint32_t* voff, char* sk, char* sv,
+                                                 int64_t* st) {
   __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(kbase + static_cast<int64_t>(k0) * ldk * 2), 0,
       static_cast<int>(clamp_records(static_cast<int64_t>(n - k0) * ldk * 2)), kRsrcFlags);
@@ -152,24 +157,72 @@ __device__ __forceinline__ void issue_tile_loads(const char* kbase, const char* 
       const_cast<char*>(vbase + static_cast<int64_t>(k0) * ldv * 2), 0,
       static_cast<int>(clamp_records(static_cast<int64_t>(n - k0) * ldv * 2)), kRsrcFlags);
 #pragma unroll
-  for (int i = 0; i < KINST; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(sk + (w * KINST + i) * 1024), 16, koff[i], 0, 0, 0);
+  for (int j = 0; j < (KCH + kWaves - 1) / kWaves; ++j) {
+    const int i = w + j * kWaves;
+    if (i < KCH) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(sk + i * 1024), 16, koff[j], 0, 0, 0);
+  }
 #pragma unroll
-  for (int i = 0; i < VINST; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(sv + (w * VINST + i) * 1024), 16, voff[i], 0, 0, 0);
-  if (has_time && w == 0 && lane < kBN / 2) {
+  for (int j = 0; j < (VCH + kWaves - 1) / kWaves; ++j) {
+    const int i = w + j * kWaves;
+    if (i < VCH) __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(sv + i * 1024), 16, voff[j], 0, 0, 0);
+  }
+  if (w == 0 && lane < kBN / 2) {
     __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int64_t*>(tsbase + k0), 0, static_cast<int>(clamp_records(static_cast<int64_t>(n - k0) * 8)),
-        kRsrcFlags);
+        const_cast<int64_t*>(tsbase + k0), 0,
+        tsbase ? static_cast<int>(clamp_records(static_cast<int64_t>(n - k0) * 8)) : 0, kRsrcFlags);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (lds_ptr_t)(st), 16, lane * 16, 0, 0, 0);
   }
 }
 
+// Workgroup barrier of the tile loop. __syncthreads() would add a release
+// fence, i.e. wait for every outstanding memory operation of the wave --
+// including the direct loads of tiles that are meant to stay in flight. Here
+// the caller waits for exactly the loads it needs (wait_vmcnt), this function
+// waits for the wave's own LDS reads (their buffer is refilled after the
+// barrier) and the empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited on
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct loads this wave issues per tile (see issue_tile_loads).
+template <int KCH, int VCH>
+__device__ __forceinline__ int loads_per_tile(int w) {
+  int c = 0;
+  for (int i = w; i < KCH; i += kWaves) ++c;
+  for (int i = w; i < VCH; i += kWaves) ++c;
+  return c + (w == 0 ? 1 : 0);
+}
+
+// s_waitcnt vmcnt(n) (no wait on the other counters) for a wave-uniform n.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+#define HSTU_VMCNT(c) __builtin_amdgcn_s_waitcnt(((c) & 15) | 0x70 | 0xF00 | (((c) >> 4) << 14))
+  switch (n) {
+    case 0: HSTU_VMCNT(0); break;
+    case 1: HSTU_VMCNT(1); break;
+    case 2: HSTU_VMCNT(2); break;
+    case 3: HSTU_VMCNT(3); break;
+    case 4: HSTU_VMCNT(4); break;
+    case 5: HSTU_VMCNT(5); break;
+    case 6: HSTU_VMCNT(6); break;
+    case 7: HSTU_VMCNT(7); break;
+    case 8: HSTU_VMCNT(8); break;
+    case 9: HSTU_VMCNT(9); break;
+    case 10: HSTU_VMCNT(10); break;
+    case 11: HSTU_VMCNT(11); break;
+    default: HSTU_VMCNT(0); break;
+  }
+#undef HSTU_VMCNT
+}
+
 template <int DQK, int DV>
 struct FwdSmem {
-  __attribute__((aligned(16))) char k[2][kBN * DQK * 2];
-  __attribute__((aligned(16))) char v[2][kBN * DV * 2];
-  __attribute__((aligned(16))) int64_t t[2][kBN];
+  __attribute__((aligned(16))) char k[kBufs][kBN * DQK * 2];
+  __attribute__((aligned(16))) char v[kBufs][kBN * DV * 2];
+  __attribute__((aligned(16))) int64_t t[kBufs][kBN];
   float pos[kPosLdsFast];   // log2(e) * P[h][0 .. min(Bp, 1024))
   float time[kTimeLds];     // log2(e) * Tt[h][0 .. min(Bt, 64))
 };
@@ -183,14 +236,14 @@ constexpr int kInfoPolyAll = 4;
 constexpr int kInfoMasked = 1 << 9;
 
 template <int DQK, int DV>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_kernel(AttnArgs a) {
   static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims");
   constexpr int KB = DQK / 16;            // k-blocks of QK^T
   constexpr int NB = DV / 32;             // 32-wide column blocks of O
   constexpr int KCH = DQK / 8;            // 16-byte chunks per K row
   constexpr int VCH = DV / 8;             // 16-byte chunks per V row
-  constexpr int KINST = KCH / 4;          // direct loads per wave per K tile (64 lanes x 16 B)
-  constexpr int VINST = VCH / 4;
+  constexpr int KINST = (KCH + kWaves - 1) / kWaves;   // direct loads per wave per K tile (64 lanes x 16 B)
+  constexpr int VINST = (VCH + kWaves - 1) / kWaves;
   using Smem = FwdSmem<DQK, DV>;
 
   const int item_idx = blockIdx.x;
@@ -212,8 +265,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) 
   const bool has_pos = a.pos_table != nullptr;
   const int Bp = a.pos_buckets, Bt = a.time_buckets;
   const bool pos_in_lds = Bp <= kPosLdsFast;
-  // metadata row of (head h, sequence b): 32-key blocks of the sequence start at 4 * tile_base[b]
-  const BlockMeta* meta_row = static_cast<const BlockMeta*>(a.meta) + h * a.meta_blocks + 4ll * a.tile_base[b];
+  // metadata row of (head h, sequence b): its 32-key blocks start at kMetaPerTile * tile_base[b]
+  const BlockMeta* meta_row =
+      static_cast<const BlockMeta*>(a.meta) + h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * a.tile_base[b];
 
   if (has_pos) {
     for (int i = tid; i < min(Bp, kPosLdsFast); i += kThreads) sm.pos[i] = kLog2e * a.pos_table[h * Bp + i];
@@ -276,24 +330,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) 
   // ---- per-lane offsets of the direct loads (constant over tiles)
   uint32_t koff[KINST], voff[VINST];
 #pragma unroll
-  for (int i = 0; i < KINST; ++i) {
-    const int s = (w * KINST + i) * 64 + lane;
+  for (int j = 0; j < KINST; ++j) {   // instruction w + j*kWaves fills LDS slots [64 i, 64 i + 64)
+    const int s = (w + j * kWaves) * 64 + lane;
     const int r = s / KCH, c = (s % KCH) ^ (r & (KCH - 1));
-    koff[i] = static_cast<uint32_t>(r * a.ldk * 2 + c * 16);
+    koff[j] = static_cast<uint32_t>(r * a.ldk * 2 + c * 16);
   }
 #pragma unroll
-  for (int i = 0; i < VINST; ++i) {
-    const int s = (w * VINST + i) * 64 + lane;
+  for (int j = 0; j < VINST; ++j) {
+    const int s = (w + j * kWaves) * 64 + lane;
     const int r = s / VCH, c = (s % VCH) ^ ((4 * r) & (VCH - 1));
-    voff[i] = static_cast<uint32_t>(r * a.ldv * 2 + c * 16);
+    voff[j] = static_cast<uint32_t>(r * a.ldv * 2 + c * 16);
   }
   const char* kbase = static_cast<const char*>(a.k) + (seq0 * a.ldk + h * DQK) * 2;
   const char* vbase = static_cast<const char*>(a.v) + (seq0 * a.ldv + h * DV) * 2;
 
-  auto issue_tile = [&] __device__(int kt, int buf) {
-    issue_tile_loads<KINST, VINST>(kbase, vbase, a.ts ? a.ts + seq0 : nullptr, has_time, a.ldk, a.ldv, n, kt * kBN,
-                                   w, lane, koff, voff, sm.k[buf], sm.v[buf], sm.t[buf]);
+  auto issue_tile = [&] __device__(int kt, char* dk, char* dv, int64_t* dt) {
+    issue_tile_loads<KCH, VCH>(kbase, vbase, has_time ? a.ts + seq0 : nullptr, a.ldk, a.ldv, n, kt * kBN, w, lane,
+                               koff, voff, dk, dv, dt);
   };
+  const int per_tile = loads_per_tile<KCH, VCH>(w);
 
   // ---- LDS byte offsets of this lane's operand fragments inside one buffer
   uint32_t k_lds[KB];                       // K row (kvb*32 + lr): + kvb * 32 * KCH * 16
@@ -308,23 +363,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) 
     v_lds[nb] = (r1 * VCH + (c ^ ((4 * r1) & (VCH - 1)))) * 16 + (i16 & 1) * 8;
   }
 
-  auto qk_block = [&] __device__(int buf, int kvb) {
-    f32x16_t s = f32x16_t{};
-    const char* kb0 = sm.k[buf] + kvb * 32 * KCH * 16;
+  // S^T of both 32-key blocks of a tile; the two accumulation chains are
+  // interleaved (a dependent MFMA waits for its predecessor's result).
+  auto qk_tile = [&] __device__(const char* kbuf, f32x16_t& s0, f32x16_t& s1) {
+    s0 = f32x16_t{};
+    s1 = f32x16_t{};
+    const char* kb1 = kbuf + 32 * KCH * 16;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kb0 + k_lds[kb]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], s, 0, 0, 0);
+      const bf16x8_t k0f = *reinterpret_cast<const bf16x8_t*>(kbuf + k_lds[kb]);
+      const bf16x8_t k1f = *reinterpret_cast<const bf16x8_t*>(kb1 + k_lds[kb]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[kb], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[kb], s1, 0, 0, 0);
     }
-    return s;
   };
-  auto pv_block = [&] __device__(int buf, int kvb, const float* p) {
+  auto pv_block = [&] __device__(const char* vbuf, int kvb, const float* p) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       bf16x8_t pa;
 #pragma unroll
       for (int i = 0; i < 8; ++i) pa[i] = static_cast<__bf16>(p[kk * 8 + i]);
-      const char* vb0 = sm.v[buf] + (kvb * 32 + kk * 16) * VCH * 16;
+      const char* vb0 = vbuf + (kvb * 32 + kk * 16) * VCH * 16;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const bf16x4_t v0 = tr_read(vb0 + v_lds[nb]);
@@ -338,7 +397,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) 
   // ---- classification of 64 key blocks (one per lane) for this wave's rows
   int rec_info = kGeneral;
   float rec_clo = 0.f, rec_chi = 0.f, rec_kmax = 0.f;
-  auto classify_window = [&] __device__(int win) {
+  auto classify_window = [&] __device__(int win, const float* stime) {
     const int ka = (win * 64 + lane) * 32;
     int info = kGeneral;
     float clo = 0.f, chi = 0.f, km = 0.f;
@@ -357,11 +416,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) 
           const int bhi = time_bucket64(wq_max - m.tmin, Bt);
           if (blo == bhi) {
             path = kUniform;
-            clo = chi = pos_last + sm.time[blo];
+            clo = chi = pos_last + stime[blo];
           } else if (bhi == blo + 1) {
             path = kTwoTime;
-            clo = pos_last + sm.time[blo];
-            chi = pos_last + sm.time[bhi];
+            clo = pos_last + stime[blo];
+            chi = pos_last + stime[bhi];
           }
         }
       }
@@ -376,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) 
 
   // ---- scores -> P for one block (paths other than the fast tile)
   auto eval_block = [&] __device__(const f32x16_t& s, int info, float c_lo, float c_hi, float kmax, int kt, int kvb,
-                                   int buf, float* p) {
+                                   const int64_t* tbuf, const float* spos, const float* stime, float* p) {
     // Polynomial or exact SiLU, decided per row from that row's norm, the
     // block's largest key norm and the bias bound of the whole table -- never
     // from the bias path, so a block's path (which may depend on later rows'
@@ -400,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float c = c_lo;
-          if (path == kTwoTime) c = sm.t[buf][kvb * 32 + 8 * g + 4 * lh + e] <= lim ? c_hi : c_lo;
+          if (path == kTwoTime) c = tbuf[kvb * 32 + 8 * g + 4 * lh + e] <= lim ? c_hi : c_lo;
           const float x = fmaf(s[4 * g + e], alpha_l, c);
           float r;
           if (mode == kPolyAll) r = silu2_poly(x);
@@ -420,9 +479,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) 
           float c = 0.f;
           if (has_pos) {
             const int pb = min(max(qrow - kv, 0), Bp - 1);
-            c = pos_in_lds ? sm.pos[pb] : (pb < kPosLdsFast ? sm.pos[pb] : kLog2e * a.pos_table[h * Bp + pb]);
+            c = pos_in_lds ? spos[pb] : (pb < kPosLdsFast ? spos[pb] : kLog2e * a.pos_table[h * Bp + pb]);
           }
-          if (has_time) c += sm.time[time_bucket64(tq - sm.t[buf][kvl], Bt)];
+          if (has_time) c += stime[time_bucket64(tq - tbuf[kvl], Bt)];
           const float x = fmaf(s[4 * g + e], alpha_l, c);
           float r;
           if (mode == kPolyAll) r = silu2_poly(x);
@@ -435,8 +494,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) 
   };
 
   // scores -> P for block kvb of tile kt, record in lane `rl` of the window
-  auto eval_tile_block = [&] __device__(const f32x16_t& s, bool active, int rl, int kt, int kvb, int buf,
-                                        float* p) {
+  auto eval_tile_block = [&] __device__(const f32x16_t& s, bool active, int rl, int kt, int kvb,
+                                        const int64_t* tbuf, const float* spos, const float* stime, float* p) {
     const int info = __builtin_amdgcn_readlane(rec_info, rl);
     const float clo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_clo), rl));
     if (!active) {
@@ -448,20 +507,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) 
     } else {
       const float chi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_chi), rl));
       const float km = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_kmax), rl));
-      eval_block(s, info, clo, chi, km, kt, kvb, buf, p);
+      eval_block(s, info, clo, chi, km, kt, kvb, tbuf, spos, stime, p);
     }
   };
 
-  if (ntiles > 0) issue_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
+  // One tile step. Every LDS buffer it touches comes in through a __restrict__
+  // parameter: the buffers being read (tile kt) and the ones the direct loads
+  // are filling (tile kt + kBufs - 1) are then known to be disjoint, so the
+  // compiler does not wait for the in-flight loads before reading LDS.
+  auto tile_step = [&] __device__(const char* __restrict__ rk, const char* __restrict__ rv,
+                                  const int64_t* __restrict__ rt, char* __restrict__ dk, char* __restrict__ dv,
+                                  int64_t* __restrict__ dt, const float* __restrict__ spos,
+                                  const float* __restrict__ stime, int kt) {
     const int k0 = kt * kBN;
-    if ((kt & 31) == 0) classify_window(kt >> 5);
-    if (kt + 1 < ntiles) issue_tile(kt + 1, buf ^ 1);
-
+    if ((kt & 31) == 0) classify_window(kt >> 5, stime);
+    // tile kt + kBufs - 1 reuses the buffer of tile kt - 1, released by the last barrier
+    issue_tile(kt + kBufs - 1, dk, dv, dt);
     if (qa < n && k0 <= qa + 31) {
       // Only the score -> P evaluation branches; both QK^T and P.V products are
       // straight-line code, so O's accumulators never cross a branch merge.
@@ -470,17 +531,31 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) 
       const int l0 = (2 * kt) & 63;
       const bool act0 = k0 < n;                               // k0 <= qa + 31 already holds
       const bool act1 = (k0 + 32 <= qa + 31) && (k0 + 32 < n);
-      const f32x16_t s0 = qk_block(buf, 0);
-      const f32x16_t s1 = qk_block(buf, 1);
+      f32x16_t s0, s1;
+      qk_tile(rk, s0, s1);
       float p0[16], p1[16];
-      eval_tile_block(s0, act0, l0, kt, 0, buf, p0);
-      pv_block(buf, 0, p0);
-      eval_tile_block(s1, act1, l0 + 1, kt, 1, buf, p1);
-      pv_block(buf, 1, p1);
+      eval_tile_block(s0, act0, l0, kt, 0, rt, spos, stime, p0);
+      pv_block(rv, 0, p0);
+      eval_tile_block(s1, act1, l0 + 1, kt, 1, rt, spos, stime, p1);
+      pv_block(rv, 1, p1);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  };
+
+  // tiles 0..kBufs-2 in flight, then wait for tile 0
+  if (ntiles > 0) {
+#pragma unroll
+    for (int t = 0; t < kBufs - 1; ++t) issue_tile(t, sm.k[t], sm.v[t], sm.t[t]);
   }
+  wait_vmcnt((kBufs - 2) * per_tile);
+  __syncthreads();   // also publishes the bias tables staged with ordinary LDS stores
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt % kBufs, nxt = (kt + kBufs - 1) % kBufs;
+    tile_step(sm.k[buf], sm.v[buf], sm.t[buf], sm.k[nxt], sm.v[nxt], sm.t[nxt], sm.pos, sm.time, kt);
+    wait_vmcnt((kBufs - 2) * per_tile);   // this wave's loads of tile kt + 1 have landed
+    tile_barrier();                        // ... and every other wave's
+  }
+  wait_vmcnt(0);
 
   // ---- epilogue: oacc[nb][j] = log2(e) * N * O[qa + 8(j/4) + 4 lh + j%4][nb*32 + lr]
   const float scale = (a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n)) / kLog2e;
@@ -506,7 +581,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnArgs a) 
 // per-(head, 32-key block) metadata: max |k_j| and the timestamp range
 // ============================================================================
 template <int DQK>
-__global__ __launch_bounds__(256) void attn_block_meta_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kMetaPerTile * 64) void attn_block_meta_kernel(AttnArgs a) {
   const int item_idx = blockIdx.x;
   if (item_idx >= *a.item_count) return;
   const WorkItem item = reinterpret_cast<const WorkItem*>(a.items)[item_idx];
@@ -514,7 +589,7 @@ __global__ __launch_bounds__(256) void attn_block_meta_kernel(AttnArgs a) {
   const int64_t seq0 = a.off[b];
   const int n = static_cast<int>(a.off[b + 1] - seq0);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int jb = qt * 4 + w;                  // 32-key block of this wave
+  const int jb = qt * kMetaPerTile + w;       // 32-key block of this wave
   const int key = jb * 32 + (lane >> 1);      // two lanes per key, half the dims each
   if (jb * 32 >= n) return;
   const bool inside = key < n;
@@ -552,7 +627,7 @@ __global__ __launch_bounds__(256) void attn_block_meta_kernel(AttnArgs a) {
     m.tmin = tmin;
     m.tmax = tmax;
     m.pad1 = 0;
-    static_cast<BlockMeta*>(a.meta)[h * a.meta_blocks + 4ll * a.tile_base[b] + jb] = m;
+    static_cast<BlockMeta*>(a.meta)[h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * a.tile_base[b] + jb] = m;
   }
 }
 
@@ -640,9 +715,9 @@ hipError_t launch_items(K kernel, const AttnArgs& a, int threads, hipStream_t st
 }  // namespace
 
 hipError_t launch_attn_block_meta(const AttnArgs& a, int dqk, hipStream_t stream) {
-  if (dqk == 128) return launch_items(attn_block_meta_kernel<128>, a, 256, stream);
-  if (dqk == 64) return launch_items(attn_block_meta_kernel<64>, a, 256, stream);
-  if (dqk == 32) return launch_items(attn_block_meta_kernel<32>, a, 256, stream);
+  if (dqk == 128) return launch_items(attn_block_meta_kernel<128>, a, kMetaPerTile * 64, stream);
+  if (dqk == 64) return launch_items(attn_block_meta_kernel<64>, a, kMetaPerTile * 64, stream);
+  if (dqk == 32) return launch_items(attn_block_meta_kernel<32>, a, kMetaPerTile * 64, stream);
   return hipErrorInvalidValue;
 }
 

@@ -156,7 +156,7 @@ WorklistLayout worklist_layout(int B, int64_t T, int H, int BM) {
   L.fill_off = take(sizeof(int) * (levels + 1));
   L.tile_base_off = take(sizeof(int) * (static_cast<size_t>(B) + 1));
   L.items_off = take(sizeof(WorkItem) * static_cast<size_t>(L.capacity));
-  L.meta_blocks = 4 * cap_tiles + 2;   // +2: a tile's pair of blocks may run one block past the last
+  L.meta_blocks = kMetaPerTile * cap_tiles + 2;   // +2: a key tile's pair of blocks may run past the last
   L.meta_off = take(sizeof(BlockMeta) * static_cast<size_t>(L.meta_blocks) * static_cast<size_t>(H));
   L.bytes = off;
   return L;
