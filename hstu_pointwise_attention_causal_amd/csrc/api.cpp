@@ -11,6 +11,7 @@
 
 #include "../../include/hstu.h"
 #include "launch.h"
+#include "layer.h"
 
 namespace {
 
@@ -174,13 +175,140 @@ hstu_status_t hstu_attn_bwd(const hstu_attn_desc_t*, const hstu_jagged_t*, const
   return fail(HSTU_E_UNSUPPORTED, "backward not built yet");
 }
 
-hstu_status_t hstu_layer_workspace_size(const hstu_layer_params_t*, const hstu_jagged_t*, size_t*) {
-  return fail(HSTU_E_UNSUPPORTED, "layer not built yet");
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// layer
+// ---------------------------------------------------------------------------
+namespace {
+
+struct LayerLayout {
+  hstu::WorklistLayout attn;
+  size_t xn_off = 0, g_off = 0, o_off = 0, y_off = 0, bytes = 0;
+};
+
+LayerLayout layer_layout(const hstu_layer_params_t* p, const hstu_jagged_t* j) {
+  LayerLayout L;
+  const int64_t T = j->total_tokens, H = p->attn.num_heads, D = p->embed_dim;
+  const int64_t n1 = H * (2 * p->attn.dv + 2 * p->attn.dqk), hv = H * p->attn.dv;
+  L.attn = hstu::worklist_layout(j->num_seqs, T, static_cast<int>(H), hstu::kAttnBM);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  take(L.attn.bytes);
+  L.xn_off = take(static_cast<size_t>(T * D * 2));
+  L.g_off = take(static_cast<size_t>(T * n1 * 2));
+  L.o_off = take(static_cast<size_t>(T * hv * 2));
+  L.y_off = take(static_cast<size_t>(T * hv * 2));
+  L.bytes = off;
+  return L;
 }
 
-hstu_status_t hstu_layer_fwd(const hstu_layer_params_t*, const hstu_jagged_t*, const void*, void*, void*, void*,
-                             void*, size_t, void*) {
-  return fail(HSTU_E_UNSUPPORTED, "layer not built yet");
+bool ln_width_ok(int64_t w) { return w == 512 || w == 1024 || w == 2048 || w == 4096; }
+
+hstu_status_t check_layer(const hstu_layer_params_t* p, const hstu_jagged_t* j) {
+  if (!p || !j) return fail(HSTU_E_NULL, "layer parameters or jagged batch is NULL");
+  hstu_status_t st = check_attn_common(&p->attn, j, &p->bias);
+  if (st != HSTU_OK) return st;
+  if (p->attn.dtype != HSTU_BF16) return fail(HSTU_E_DTYPE, "the layer runs in bf16");
+  const int64_t H = p->attn.num_heads;
+  if (!ln_width_ok(p->embed_dim) || !ln_width_ok(H * p->attn.dv))
+    return fail(HSTU_E_UNSUPPORTED, "embed_dim and H*dv must be one of 512, 1024, 2048, 4096 (got %d, %lld)",
+                p->embed_dim, (long long)(H * p->attn.dv));
+  if (!p->ln_in_gamma || !p->ln_in_beta || !p->ln_out_gamma || !p->ln_out_beta || !p->w_uvqk || !p->w_out)
+    return fail(HSTU_E_NULL, "a LayerNorm parameter or weight matrix is NULL");
+  if (!aligned16(p->w_uvqk) || !aligned16(p->w_out)) return fail(HSTU_E_ALIGN, "weights must be 16-byte aligned");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status_t hstu_layer_workspace_size(const hstu_layer_params_t* params, const hstu_jagged_t* jag, size_t* bytes) {
+  if (!bytes) return fail(HSTU_E_NULL, "bytes is NULL");
+  hstu_status_t st = check_layer(params, jag);
+  if (st != HSTU_OK) return st;
+  *bytes = layer_layout(params, jag).bytes;
+  return ok();
+}
+
+hstu_status_t hstu_layer_fwd(const hstu_layer_params_t* p, const hstu_jagged_t* jag, const void* x, void* y,
+                             void* uvqk_out, void* o_out, void* workspace, size_t workspace_bytes,
+                             void* hip_stream) {
+  hstu_status_t st = check_layer(p, jag);
+  if (st != HSTU_OK) return st;
+  const int64_t T = jag->total_tokens, H = p->attn.num_heads, D = p->embed_dim;
+  const int64_t dqk = p->attn.dqk, dv = p->attn.dv;
+  const int64_t n1 = H * (2 * dv + 2 * dqk), hv = H * dv;
+  if (T > 0 && (!x || !y)) return fail(HSTU_E_NULL, "x or y is NULL");
+  if (T > 0 && (!aligned16(x) || !aligned16(y))) return fail(HSTU_E_ALIGN, "x and y must be 16-byte aligned");
+  if ((uvqk_out && !aligned16(uvqk_out)) || (o_out && !aligned16(o_out)))
+    return fail(HSTU_E_ALIGN, "uvqk_out and o_out must be 16-byte aligned");
+  const Range rx = view_range(x, T, D, D, 2), ry = view_range(y, T, D, D, 2);
+  if (overlaps(rx, ry)) return fail(HSTU_E_ALIAS, "y overlaps x");
+  if (overlaps(view_range(uvqk_out, T, n1, n1, 2), rx) || overlaps(view_range(uvqk_out, T, n1, n1, 2), ry) ||
+      overlaps(view_range(o_out, T, hv, hv, 2), rx) || overlaps(view_range(o_out, T, hv, hv, 2), ry))
+    return fail(HSTU_E_ALIAS, "uvqk_out or o_out overlaps x or y");
+  const LayerLayout L = layer_layout(p, jag);
+  if (workspace_bytes < L.bytes || (L.bytes > 0 && !workspace))
+    return fail(HSTU_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, L.bytes);
+  if (T == 0 || jag->num_seqs == 0) return ok();
+  if (!aligned16(workspace)) return fail(HSTU_E_ALIGN, "workspace must be 16-byte aligned");
+
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(workspace);
+  void* xn = ws + L.xn_off;
+  void* g = uvqk_out ? uvqk_out : static_cast<void*>(ws + L.g_off);
+  void* o = o_out ? o_out : static_cast<void*>(ws + L.o_off);
+  void* yy = ws + L.y_off;
+  hipError_t e;
+
+  // 1. Xn = LN(X; gamma1, beta1)
+  hstu::LnArgs ln{};
+  ln.x = x; ln.ldx = D; ln.gate = nullptr; ln.ldg = 0; ln.y = xn; ln.ldy = D;
+  ln.gamma = p->ln_in_gamma; ln.beta = p->ln_in_beta; ln.eps = p->ln_eps; ln.rows = T;
+  if ((e = hstu::launch_ln_rows(ln, static_cast<int>(D), stream)) != hipSuccess) return hip_fail(e, "input LayerNorm");
+
+  // 2. G = SiLU(Xn W_uvqk^T + b_uvqk), columns u | v | q | k
+  hstu::GemmArgs g1{};
+  g1.a = xn; g1.lda = D; g1.b = p->w_uvqk; g1.ldb = D; g1.c = g; g1.ldc = n1; g1.bias = p->b_uvqk;
+  g1.M = static_cast<int>(T); g1.N = static_cast<int>(n1); g1.K = static_cast<int>(D);
+  if ((e = hstu::launch_gemm_nt(g1, hstu::kEpiSilu, stream)) != hipSuccess) return hip_fail(e, "UVQK projection");
+
+  // 3. O = attention(q, k, v) on column views of G
+  const __bf16* gb = static_cast<const __bf16*>(g);
+  hstu::WorklistLayout WL = L.attn;
+  if ((e = hstu::launch_build_worklist(jag->seq_offsets, jag->num_seqs, static_cast<int>(H), hstu::kAttnBM, WL, ws,
+                                       stream)) != hipSuccess)
+    return hip_fail(e, "work-list launch");
+  hstu::AttnArgs a = make_args(&p->attn, jag, &p->bias, gb + 2 * hv, n1, gb + 2 * hv + H * dqk, n1, gb + hv, n1);
+  a.o = o;
+  a.ldo = hv;
+  a.items = ws + WL.items_off;
+  a.item_count = reinterpret_cast<const int*>(ws + WL.hdr_off);
+  a.capacity = WL.capacity;
+  a.tile_base = reinterpret_cast<const int*>(ws + WL.tile_base_off);
+  a.meta = ws + WL.meta_off;
+  a.meta_blocks = WL.meta_blocks;
+  if ((e = hstu::launch_attn_fwd_bf16(a, static_cast<int>(dqk), static_cast<int>(dv), stream)) != hipSuccess)
+    return hip_fail(e, "attention forward launch");
+
+  // 4. Y = LN(O; gamma2, beta2) * U
+  hstu::LnArgs lo{};
+  lo.x = o; lo.ldx = hv; lo.gate = g; lo.ldg = n1; lo.y = yy; lo.ldy = hv;
+  lo.gamma = p->ln_out_gamma; lo.beta = p->ln_out_beta; lo.eps = p->ln_eps; lo.rows = T;
+  if ((e = hstu::launch_ln_rows(lo, static_cast<int>(hv), stream)) != hipSuccess) return hip_fail(e, "post-pooling LayerNorm");
+
+  // 5. X' = X + Y W_out^T + b_out
+  hstu::GemmArgs g2{};
+  g2.a = yy; g2.lda = hv; g2.b = p->w_out; g2.ldb = hv; g2.c = y; g2.ldc = D; g2.bias = p->b_out;
+  g2.r = x; g2.ldr = D; g2.M = static_cast<int>(T); g2.N = static_cast<int>(D); g2.K = static_cast<int>(hv);
+  if ((e = hstu::launch_gemm_nt(g2, hstu::kEpiResidual, stream)) != hipSuccess) return hip_fail(e, "output projection");
+  return ok();
 }
 
 const char* hstu_status_string(hstu_status_t s) {

@@ -8,7 +8,7 @@
 // aggregation; briansu.co explainer section 3 for the two relative biases).
 // There is no softmax, hence no running row maximum and no rescaling.
 //
-// bf16 kernel (MFMA): 8 waves, each owning 32 query rows. Per 64-key tile:
+// bf16 kernel (MFMA): 4 waves, each owning 32 query rows. Per 64-key tile:
 //   S^T[kv][q] = K Q^T       v_mfma_f32_32x32x16_bf16, A = K tile (LDS),
 //                            B = Q^T (registers, loaded once per item)
 //   P = mask(SiLU(S + bias)) in fp32 registers, packed to bf16
@@ -33,7 +33,7 @@ namespace {
 constexpr int kBN = 64;            // keys per LDS tile
 constexpr int kWaves = kAttnBM / 32;   // 32 query rows each
 constexpr int kThreads = kWaves * 64;
-constexpr int kBufs = 4;           // K/V tiles in flight: loads run 3 tiles ahead
+constexpr int kBufs = 2;           // K/V tiles in flight (2 workgroups per CU fit in LDS)
 constexpr int kPosLds = 1024;      // position-table entries staged in LDS
 constexpr int kTimeLds = 64;       // time buckets reachable with int64 gaps: 0..62
 

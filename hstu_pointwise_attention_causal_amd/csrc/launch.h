@@ -24,7 +24,7 @@ hipError_t launch_build_worklist(const int64_t* off, int B, int H, int BM, const
                                  char* ws, hipStream_t stream);
 
 // Query-tile height shared by every attention kernel and the work list.
-constexpr int kAttnBM = 256;
+constexpr int kAttnBM = 128;
 // 32-key metadata blocks per query tile
 constexpr int kMetaPerTile = kAttnBM / 32;
 

@@ -16,6 +16,7 @@ from .oracle import (  # noqa: F401
     attn_fwd,
     attn_fwd_rows,
     layer_fwd,
+    layer_fwd_rows,
     layer_norm,
     pos_bucket,
     silu,

@@ -317,6 +317,46 @@ def layer_fwd(x, params: dict, seq_offsets, *, num_heads: int, dqk: int, dv: int
     return out, {"uvqk": g, "o": o, "y": y}
 
 
+def layer_fwd_rows(x, params: dict, seq_offsets, rows, *, num_heads: int, dqk: int, dv: int,
+                   timestamps=None, eps: float = 1e-6, alpha: float = 1.0, divisor: float = 0.0):
+    """Rows ``rows`` (global token indices) of ``layer_fwd``'s output, float64.
+
+    The projection G is formed for every token (later rows attend to all
+    earlier ones); the attention, post-pooling norm, gate and output projection
+    are then evaluated only for the requested rows, each from the same
+    definitions as ``layer_fwd``. Returns [len(rows), D].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T, D = x.shape
+    H = num_heads
+    off = np.asarray(seq_offsets, dtype=np.int64)
+    xn = layer_norm(x, params["ln_in_gamma"], params["ln_in_beta"], eps)
+    z = xn @ _f64(params["w_uvqk"]).T
+    if params.get("b_uvqk") is not None:
+        z = z + _f64(params["b_uvqk"])
+    g = silu(z)
+    u = g[:, 0:H * dv]
+    vv = g[:, H * dv:2 * H * dv].reshape(T, H, dv)
+    qq = g[:, 2 * H * dv:2 * H * dv + H * dqk].reshape(T, H, dqk)
+    kk = g[:, 2 * H * dv + H * dqk:2 * H * dv + 2 * H * dqk].reshape(T, H, dqk)
+    rows = np.asarray(rows, dtype=np.int64)
+    seq_of = np.searchsorted(off, rows, side="right") - 1
+    out = np.zeros((rows.size, D), dtype=np.float64)
+    for b in np.unique(seq_of):
+        sel = np.flatnonzero(seq_of == b)
+        pos = rows[sel] - off[b]
+        o = np.concatenate([attn_fwd_rows(qq, kk, vv, off, int(b), h, pos, alpha=alpha,
+                                          divisor=divisor, pos_table=params.get("pos_table"),
+                                          time_table=params.get("time_table"),
+                                          timestamps=timestamps) for h in range(H)], axis=1)
+        y = layer_norm(o, params["ln_out_gamma"], params["ln_out_beta"], eps) * u[rows[sel]]
+        r = x[rows[sel]] + y @ _f64(params["w_out"]).T
+        if params.get("b_out") is not None:
+            r = r + _f64(params["b_out"])
+        out[sel] = r
+    return out
+
+
 def stack_fwd(x, layers, seq_offsets, *, num_heads: int, dqk: int, dv: int,
               timestamps=None, eps: float = 1e-6):
     """A stack of HSTU layers applied in order (the neurarch model card lists

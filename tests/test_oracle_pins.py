@@ -366,6 +366,14 @@ def test_layer_matches_brute_force_loops():
     assert _rel(got, ref) < 1e-12
 
 
+def test_layer_rows_match_full_layer():
+    x, p, off, ts = _tiny_layer(17, [6, 0, 9])
+    full, _ = O.layer_fwd(x, p, off, num_heads=2, dqk=3, dv=3, timestamps=ts)
+    rows = [0, 5, 6, 14, 10]
+    got = O.layer_fwd_rows(x, p, off, rows, num_heads=2, dqk=3, dv=3, timestamps=ts)
+    assert _rel(got, full[rows]) < 1e-13
+
+
 def test_layer_zero_out_projection_is_identity():
     x, p, off, ts = _tiny_layer(14, [5, 4])
     p["w_out"] = np.zeros_like(p["w_out"])
