@@ -107,6 +107,34 @@ hstu::AttnArgs make_args(const hstu_attn_desc_t* d, const hstu_jagged_t* j, cons
   return a;
 }
 
+
+// Backward support beyond the forward's: bf16 only, and position tables that
+// fit the kernels' LDS copy.
+hstu_status_t check_bwd_support(const hstu_attn_desc_t* d, const hstu_bias_t* bias) {
+  if (d->dtype != HSTU_BF16) return fail(HSTU_E_UNSUPPORTED, "the backward is built for bf16 only");
+  if (bias && bias->pos_table && bias->pos_buckets > hstu::kBwdPosMax)
+    return fail(HSTU_E_UNSUPPORTED, "the backward supports at most %d position buckets", hstu::kBwdPosMax);
+  return ok();
+}
+
+// Workspace of the backward: the forward's work list and block metadata, then
+// one row of bias-gradient partial sums per (head, key tile).
+struct BwdLayout {
+  size_t partial_off = 0, bytes = 0;
+  int grad_stride = 0;
+  int64_t tile_rows = 0;
+};
+
+BwdLayout bwd_layout(const hstu::WorklistLayout& L, const hstu_attn_desc_t* d, const hstu_bias_t* bias) {
+  BwdLayout B;
+  B.grad_stride = (bias && bias->pos_table ? bias->pos_buckets : 0) + (bias && bias->time_table ? hstu::kBwdTimeSlots : 0);
+  B.tile_rows = d->num_heads > 0 ? L.capacity / d->num_heads : 0;
+  B.partial_off = (L.bytes + 255) & ~size_t(255);
+  B.bytes = B.partial_off + sizeof(float) * static_cast<size_t>(L.capacity) * static_cast<size_t>(B.grad_stride);
+  if (B.grad_stride == 0) B.bytes = L.bytes;
+  return B;
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,7 +148,8 @@ hstu_status_t hstu_attn_workspace_size(const hstu_attn_desc_t* desc, const hstu_
       hstu::worklist_layout(jag->num_seqs, jag->total_tokens, desc->num_heads, hstu::kAttnBM);
   size_t total = L.bytes;
   if (is_bwd) {
-    return fail(HSTU_E_UNSUPPORTED, "backward not built yet");
+    if ((st = check_bwd_support(desc, bias)) != HSTU_OK) return st;
+    total = bwd_layout(L, desc, bias).bytes;
   }
   *bytes = total;
   return ok();
@@ -169,10 +198,83 @@ hstu_status_t hstu_attn_fwd(const hstu_attn_desc_t* desc, const hstu_jagged_t* j
   return ok();
 }
 
-hstu_status_t hstu_attn_bwd(const hstu_attn_desc_t*, const hstu_jagged_t*, const hstu_bias_t*, const void*,
-                            int64_t, const void*, int64_t, const void*, int64_t, const void*, int64_t, void*,
-                            int64_t, void*, int64_t, void*, int64_t, float*, float*, void*, size_t, void*) {
-  return fail(HSTU_E_UNSUPPORTED, "backward not built yet");
+hstu_status_t hstu_attn_bwd(const hstu_attn_desc_t* desc, const hstu_jagged_t* jag, const hstu_bias_t* bias,
+                            const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v, int64_t ldv,
+                            const void* d_o, int64_t lddo, void* dq, int64_t lddq, void* dk, int64_t lddk, void* dv,
+                            int64_t lddv, float* d_pos_table, float* d_time_table, void* workspace,
+                            size_t workspace_bytes, void* hip_stream) {
+  hstu_status_t st = check_attn_common(desc, jag, bias);
+  if (st != HSTU_OK) return st;
+  if ((st = check_bwd_support(desc, bias)) != HSTU_OK) return st;
+  const int64_t T = jag->total_tokens, H = desc->num_heads;
+  const int64_t wq = H * desc->dqk, wv = H * desc->dv;
+  const hstu_dtype_t dt = desc->dtype;
+  if ((st = check_view("q", q, ldq, wq, T, dt)) != HSTU_OK) return st;
+  if ((st = check_view("k", k, ldk, wq, T, dt)) != HSTU_OK) return st;
+  if ((st = check_view("v", v, ldv, wv, T, dt)) != HSTU_OK) return st;
+  if ((st = check_view("d_o", d_o, lddo, wv, T, dt)) != HSTU_OK) return st;
+  if ((st = check_view("dq", dq, lddq, wq, T, dt)) != HSTU_OK) return st;
+  if ((st = check_view("dk", dk, lddk, wq, T, dt)) != HSTU_OK) return st;
+  if ((st = check_view("dv", dv, lddv, wv, T, dt)) != HSTU_OK) return st;
+  const bool has_pos = bias && bias->pos_table, has_time = bias && bias->time_table;
+  if (has_pos != (d_pos_table != nullptr))
+    return fail(HSTU_E_NULL, "d_pos_table must be given exactly when the position table is");
+  if (has_time != (d_time_table != nullptr))
+    return fail(HSTU_E_NULL, "d_time_table must be given exactly when the time table is");
+  const size_t es = elem_size(dt);
+  const Range rq = view_range(q, T, ldq, wq, es), rk = view_range(k, T, ldk, wq, es),
+              rv = view_range(v, T, ldv, wv, es), rdo = view_range(d_o, T, lddo, wv, es);
+  const Range outs[3] = {view_range(dq, T, lddq, wq, es), view_range(dk, T, lddk, wq, es),
+                         view_range(dv, T, lddv, wv, es)};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], rq) || overlaps(outs[i], rk) || overlaps(outs[i], rv) || overlaps(outs[i], rdo))
+      return fail(HSTU_E_ALIAS, "dq, dk and dv must not overlap q, k, v or d_o");
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(HSTU_E_ALIAS, "dq, dk and dv must not overlap each other");
+  }
+  hstu::WorklistLayout L = hstu::worklist_layout(jag->num_seqs, T, (int)H, hstu::kAttnBM);
+  const BwdLayout BL = bwd_layout(L, desc, bias);
+  if (workspace_bytes < BL.bytes || (BL.bytes > 0 && !workspace))
+    return fail(HSTU_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes,
+                BL.bytes);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (jag->num_seqs == 0 || T == 0) {
+    // no pairs: the table gradients are zero
+    hipError_t e = hipSuccess;
+    if (has_pos) e = hstu::launch_fill_f32(d_pos_table, H * bias->pos_buckets, 0.f, stream);
+    if (e == hipSuccess && has_time) e = hstu::launch_fill_f32(d_time_table, H * bias->time_buckets, 0.f, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "zeroing the bias gradients");
+  }
+  if (!aligned16(workspace)) return fail(HSTU_E_ALIGN, "workspace must be 16-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = hstu::launch_build_worklist(jag->seq_offsets, jag->num_seqs, (int)H, hstu::kAttnBM, L, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "work-list launch");
+  hstu::AttnBwdArgs g{};
+  g.f = make_args(desc, jag, bias, q, ldq, k, ldk, v, ldv);
+  g.f.items = ws + L.items_off;
+  g.f.item_count = reinterpret_cast<const int*>(ws + L.hdr_off);
+  g.f.capacity = L.capacity;
+  g.f.tile_base = reinterpret_cast<const int*>(ws + L.tile_base_off);
+  g.f.meta = ws + L.meta_off;
+  g.f.meta_blocks = L.meta_blocks;
+  g.d_o = d_o;
+  g.lddo = lddo;
+  g.dq = dq;
+  g.lddq = lddq;
+  g.dk = dk;
+  g.lddk = lddk;
+  g.dv = dv;
+  g.lddv = lddv;
+  g.d_pos = d_pos_table;
+  g.d_time = d_time_table;
+  g.partial = BL.grad_stride > 0 ? reinterpret_cast<float*>(ws + BL.partial_off) : nullptr;
+  g.grad_stride = BL.grad_stride;
+  g.tile_rows = BL.tile_rows;
+  g.num_seqs = jag->num_seqs;
+  e = hstu::launch_attn_bwd_bf16(g, desc->dqk, desc->dv, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+  return ok();
 }
 
 }  // extern "C"

@@ -23,6 +23,7 @@
 //
 // fp32 kernel (VALU): one thread per query row, fp32 throughout, for the
 // fp32 workload and as a precision reference path.
+#include "attn_common.h"
 #include "common.h"
 #include "launch.h"
 
@@ -105,7 +106,6 @@ constexpr int kPosLdsFast = 1024;
 constexpr float kPolyC0 = 1.731778037e-01f, kPolyC1 = -6.804446619e-03f, kPolyC2 = 2.799578346e-04f,
                 kPolyC3 = -6.863766511e-06f;
 constexpr float kPolyBound = 1.95f * kLog2e;   // in x' units; fit range is 2 log2(e)
-constexpr int kRsrcFlags = 0x00020000;
 
 __device__ __forceinline__ float silu2_exact(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x));
@@ -116,26 +116,6 @@ __device__ __forceinline__ float silu2_poly(float x) {
   p = fmaf(y, p, kPolyC1);
   p = fmaf(y, p, kPolyC0);
   return fmaf(x, 0.5f, y * p);
-}
-
-__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
-  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ lds_ptr_t to_lds(void* p) { return (lds_ptr_t)(p); }
-
-__device__ __forceinline__ bf16x4_t tr_read(const char* p) {
-  s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
-  return __builtin_bit_cast(bf16x4_t, r);
-}
-
-__device__ __forceinline__ uint32_t clamp_records(int64_t bytes) {
-  return bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes));
 }
 
 // Direct HBM -> LDS loads of one key tile (K, V and key timestamps). Kept out
@@ -174,20 +154,6 @@ __device__ __forceinline__ void issue_tile_loads(const char* kbase, const char* 
   }
 }
 
-// Workgroup barrier of the tile loop. __syncthreads() would add a release
-// fence, i.e. wait for every outstanding memory operation of the wave --
-// including the direct loads of tiles that are meant to stay in flight. Here
-// the caller waits for exactly the loads it needs (wait_vmcnt), this function
-// waits for the wave's own LDS reads (their buffer is refilled after the
-// barrier) and the empty asm statements keep the compiler from moving memory
-// accesses across the barrier.
-__device__ __forceinline__ void tile_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited on
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Direct loads this wave issues per tile (see issue_tile_loads).
 template <int KCH, int VCH>
 __device__ __forceinline__ int loads_per_tile(int w) {
@@ -195,27 +161,6 @@ __device__ __forceinline__ int loads_per_tile(int w) {
   for (int i = w; i < KCH; i += kWaves) ++c;
   for (int i = w; i < VCH; i += kWaves) ++c;
   return c + (w == 0 ? 1 : 0);
-}
-
-// s_waitcnt vmcnt(n) (no wait on the other counters) for a wave-uniform n.
-__device__ __forceinline__ void wait_vmcnt(int n) {
-#define HSTU_VMCNT(c) __builtin_amdgcn_s_waitcnt(((c) & 15) | 0x70 | 0xF00 | (((c) >> 4) << 14))
-  switch (n) {
-    case 0: HSTU_VMCNT(0); break;
-    case 1: HSTU_VMCNT(1); break;
-    case 2: HSTU_VMCNT(2); break;
-    case 3: HSTU_VMCNT(3); break;
-    case 4: HSTU_VMCNT(4); break;
-    case 5: HSTU_VMCNT(5); break;
-    case 6: HSTU_VMCNT(6); break;
-    case 7: HSTU_VMCNT(7); break;
-    case 8: HSTU_VMCNT(8); break;
-    case 9: HSTU_VMCNT(9); break;
-    case 10: HSTU_VMCNT(10); break;
-    case 11: HSTU_VMCNT(11); break;
-    default: HSTU_VMCNT(0); break;
-  }
-#undef HSTU_VMCNT
 }
 
 template <int DQK, int DV>

@@ -64,7 +64,37 @@ struct BlockMeta {
 };
 static_assert(sizeof(BlockMeta) == 32, "BlockMeta layout");
 
+hipError_t launch_attn_block_meta(const AttnArgs& a, int dqk, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int dqk, int dv, hipStream_t stream);
+
+// ---------------------------------------------------------------- backward
+// Position-table entries the backward keeps (values and gradients) in LDS;
+// larger tables are rejected by the C ABI.
+constexpr int kBwdPosMax = 1024;
+// Time buckets that int64 gaps can reach (0..62), rounded up.
+constexpr int kBwdTimeSlots = 64;
+
+struct AttnBwdArgs {
+  AttnArgs f;               // forward inputs, work list and block metadata
+  const void* d_o;
+  int64_t lddo;
+  void* dq;
+  int64_t lddq;
+  void* dk;
+  int64_t lddk;
+  void* dv;
+  int64_t lddv;
+  float* d_pos;             // [H][Bp] or NULL
+  float* d_time;            // [H][Bt] or NULL
+  float* partial;           // [H][tile_rows][grad_stride]: bias-gradient sums of one key tile
+  int grad_stride;          // (Bp if pos) + (kBwdTimeSlots if time)
+  int64_t tile_rows;        // rows per head of `partial` (>= total query tiles)
+  int num_seqs;
+};
+
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, int dqk, int dv, hipStream_t stream);
+// x[0 .. n) = value (a kernel, so that the call can be captured in a graph)
+hipError_t launch_fill_f32(float* x, int64_t n, float value, hipStream_t stream);
 
 }  // namespace hstu

@@ -98,3 +98,46 @@ def test_workspace_size_is_a_host_function(lib):
     # 4 sequences x 8192 tokens, 128-row tiles: at most 8 * (32768 + 4*127)/128 + 8 items
     assert 8 * 260 * 8 <= out.value < 1 << 20
     assert c.hstu_attn_workspace_size(ctypes.byref(d), ctypes.byref(j), None, 0, None) == 1
+
+
+FAKE_DO, FAKE_DQ, FAKE_DK, FAKE_DV = 0x700000, 0x800000, 0x900000, 0xA00000
+
+
+def _bwd(lib, desc, jag, bias=None, d_o=FAKE_DO, dq=FAKE_DQ, dk=FAKE_DK, dv=FAKE_DV, dpos=None, dtime=None,
+         wsb=0):
+    c = lib.load()
+    b = bias if bias is not None else lib.Bias()
+    return c.hstu_attn_bwd(ctypes.byref(desc), ctypes.byref(jag), ctypes.byref(b),
+                           FAKE_Q, 128, FAKE_K, 128, FAKE_V, 128, d_o, 128, dq, 128, dk, 128, dv, 128,
+                           dpos, dtime, FAKE_W, wsb, None)
+
+
+def test_backward_rejections(lib):
+    d, j = _desc(lib), _jag(lib)
+    assert _bwd(lib, _desc(lib, dtype=lib.HSTU_F32), j) == 5          # fp32 backward not built
+    assert _bwd(lib, d, j, d_o=None) == 1                            # NULL upstream gradient
+    assert _bwd(lib, d, j, dq=FAKE_Q) == 7                           # dq overlaps q
+    assert _bwd(lib, d, j, dk=FAKE_DQ + 64) == 7                     # dk overlaps dq
+    assert _bwd(lib, d, j) == 6                                      # workspace too small
+    b = lib.Bias()
+    b.pos_table, b.pos_buckets = 0x600000, 128
+    assert _bwd(lib, d, j, bias=b) == 1                              # table without its gradient
+    assert _bwd(lib, d, j, dpos=0xB00000) == 1                       # gradient without its table
+    b.pos_buckets = 1025
+    assert _bwd(lib, d, j, bias=b, dpos=0xB00000) == 5               # position table too large
+
+
+def test_backward_workspace_adds_bias_partials(lib):
+    c = lib.load()
+    d = _desc(lib, H=4, d=128)
+    j = _jag(lib, B=32, T=24321, ts=True)
+    fwd, bwd, nob = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    b = lib.Bias()
+    b.pos_table, b.pos_buckets, b.time_table, b.time_buckets = 0x600000, 128, 0x610000, 128
+    assert c.hstu_attn_workspace_size(ctypes.byref(d), ctypes.byref(j), ctypes.byref(b), 0, ctypes.byref(fwd)) == 0
+    assert c.hstu_attn_workspace_size(ctypes.byref(d), ctypes.byref(j), ctypes.byref(b), 1, ctypes.byref(bwd)) == 0
+    assert c.hstu_attn_workspace_size(ctypes.byref(d), ctypes.byref(j), None, 1, ctypes.byref(nob)) == 0
+    assert nob.value == fwd.value
+    # one row of 128 position + 64 time slots per (head, key tile)
+    tiles = (24321 + 32 * 127) // 128
+    assert bwd.value >= fwd.value + 4 * 4 * tiles * (128 + 64)

@@ -113,7 +113,7 @@ def test_four_layer_stack_full_size(hstu):
     wl = make_workload("c1")
     x_gpu = to_dev(wl.x, torch.bfloat16)
     off = to_dev(wl.seq_offsets)
-    ts = to_dev(wl.timestamps)
+    ts = None if wl.timestamps is None else to_dev(wl.timestamps)
     for li, p in enumerate(wl.layers):
         params, keep = _dev_layer(hstu, wl, p)
         x_in = x_gpu.float().cpu().numpy()
