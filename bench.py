@@ -1,15 +1,23 @@
 #!/usr/bin/env python3
-"""Benchmark of the HSTU causal pointwise attention forward on one MI355X.
+"""Benchmark of the HSTU hot path on one MI355X.
 
-One step = one hstu_attn_fwd call (work-list build + attention kernel) over the
-long-history workload: 4 sequences x 8192 tokens, 8 heads, dqk = dv = 128,
-relative position + time bias, divisor n, bf16 inputs with fp32 accumulation.
-Inputs are synthetic (seeded recipes in ``workloads``) and resident in HBM
-before the timed region.
+Headline (the JSON line's ``value``): causal-effective TFLOP/s of the attention
+forward on the long-history workload -- 4 sequences x 8192 tokens, 8 heads,
+dqk = dv = 128, relative position + time bias, divisor n, bf16 inputs with
+fp32 accumulation. One step = one hstu_attn_fwd call (work-list build, block
+metadata, attention kernel). Inputs are synthetic (seeded recipes in
+``workloads``) and resident in HBM before the timed region.
 
-Prints ONE JSON line with the causal-effective TFLOP/s (the metric), tokens/s,
-a roofline object for the attention kernel (bf16 MFMA bound) and the CPU
-oracle timed on a bounded sample of the same workload.
+Also on the line:
+  roofline      the attention kernel's own average launch time, taken with HIP
+                events that the library records around each launch on the
+                launch stream (hstu_timing_enable), against the bf16 MFMA peak;
+                HBM traffic from the committed rocprofv3 counter summary when
+                it was taken on the current kernel source, else null;
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload;
+  secondary     tokens/s per layer of the 4-layer stack (8 x 1024 tokens) and
+                of one layer over the 64-sequence jagged batch, and the
+                attention forward + backward of the 32-sequence jagged batch.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
     python bench.py --copy-calib      # plain copy of known size, for counter scaling
@@ -29,18 +37,22 @@ sys.path.insert(0, ROOT)
 
 METRIC = "HSTU attention causal-effective TFLOP/s + tokens/s/layer, jagged bf16, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
-PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_c3_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "hstu_pointwise_attention_causal_amd", "csrc", "attn_fwd.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "hstu_pointwise_attention_causal_amd", "csrc", f)
+               for f in ("attn_fwd.hip", "attn_common.h", "common.h", "launch.h")]
 COPY_BYTES = 1 << 30
 
 
-def _kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_hash() -> str:
+    """Hash of the sources the attention forward kernel is compiled from."""
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def _traffic(steps_note=None):
+def _traffic():
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when the attention kernel source changed since it was taken."""
     try:
@@ -48,7 +60,7 @@ def _traffic(steps_note=None):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256_16") != _kernel_hash():
+    if t.get("kernel_sha256_16") != kernel_hash():
         return None
     return t.get("bytes_per_launch")
 
@@ -94,19 +106,160 @@ def cpu_baseline(wl, target_s: float):
         if time.perf_counter() - t0 >= target_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{units} of {wl.num_seqs * wl.num_heads} (sequence, head) units of the "
                       f"workload, fp64 NumPy oracle, {dt:.1f} s wall; BLAS threads {threads}, "
                       f"elementwise steps single-threaded"}
 
 
+def time_steps(step, steps: int, warmup: int, stream):
+    """Warm up, then time exactly `steps` calls between two synchronizations;
+    returns (ms per step from HIP events on `stream`, ms per step of wall time)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - wall0) * 1e3 / steps
+    return ev0.elapsed_time(ev1) / steps, wall
+
+
+def kernel_ms(hstu, step, steps: int, kernels):
+    """Average launch time of each named kernel over `steps` further calls,
+    from the events the library records around each launch."""
+    import torch
+    for k in kernels:
+        hstu.timing_read(k)          # drop anything recorded before
+    hstu.timing_enable(True)
+    try:
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        out = {}
+        for k in kernels:
+            n, ms = hstu.timing_read(k)
+            out[k] = ms / n if n else None
+    finally:
+        hstu.timing_enable(False)
+    return out
+
+
+def _attn_tensors(wl, dev):
+    import torch
+    t = lambda a, dt: torch.from_numpy(a).to(dev).to(dt)  # noqa: E731
+    d = dict(q=t(wl.q, torch.bfloat16), k=t(wl.k, torch.bfloat16), v=t(wl.v, torch.bfloat16),
+             off=torch.from_numpy(wl.seq_offsets).to(dev),
+             ts=torch.from_numpy(wl.timestamps).to(dev) if wl.timestamps is not None else None,
+             pt=t(wl.pos_table, torch.float32) if wl.pos_table is not None else None,
+             tt=t(wl.time_table, torch.float32) if wl.time_table is not None else None)
+    if wl.d_o is not None:
+        d["d_o"] = t(wl.d_o, torch.bfloat16)
+    return d
+
+
+def secondary_layers(hstu, name: str, steps: int, warmup: int, dev):
+    """Tokens/s per layer of a layer workload (all its layers per step)."""
+    import torch
+    from workloads import make_workload
+    wl = make_workload(name)
+    x0 = torch.from_numpy(wl.x).to(dev).to(torch.bfloat16)
+    off = torch.from_numpy(wl.seq_offsets).to(dev)
+    ts = torch.from_numpy(wl.timestamps).to(dev) if wl.timestamps is not None else None
+    keep, params = [], []
+    for p in wl.layers:
+        dv = {}
+        for k in ("w_uvqk", "w_out"):
+            dv[k] = torch.from_numpy(p[k]).to(dev).to(torch.bfloat16)
+        for k in ("b_uvqk", "b_out", "ln_in_gamma", "ln_in_beta", "ln_out_gamma", "ln_out_beta",
+                  "pos_table", "time_table"):
+            dv[k] = None if p.get(k) is None else torch.from_numpy(p[k]).to(dev).to(torch.float32)
+        keep.append(dv)
+        params.append(hstu.make_layer_params(wl.embed_dim, wl.num_heads, wl.dqk, wl.dv, ln_eps=wl.ln_eps, **dv))
+    bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+    ws = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # >= hstu_layer_workspace_size
+
+    def step():
+        x = x0
+        for i, p in enumerate(params):
+            x = hstu.layer_fwd(x, off, p, timestamps=ts, out=bufs[i & 1], workspace=ws)
+
+    stream = torch.cuda.current_stream(dev)
+    ms_ev, ms_wall = time_steps(step, steps, warmup, stream)
+    ms = max(ms_ev, ms_wall)
+    L = len(params)
+    kern = kernel_ms(hstu, step, steps, ["attn_fwd", "layer_gemm_uvqk", "layer_gemm_out", "layer_norm"])
+    per_layer = {k: (None if v is None else round(v * (1 if k != "layer_norm" else 2), 5))
+                 for k, v in kern.items()}
+    gemm_ms = (kern["layer_gemm_uvqk"] or 0) + (kern["layer_gemm_out"] or 0)
+    return {
+        "workload": f"{name}: {wl.note}",
+        "tokens_per_s_per_layer": round(wl.total_tokens / (ms * 1e-3 / L), 1),
+        "ms_per_layer": round(ms / L, 5),
+        "layers": L,
+        "total_tokens": wl.total_tokens,
+        "kernel_ms_per_layer": per_layer,
+        "gemm_tflops": round(wl.layer_gemm_flops() / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms else None,
+        "attn_fwd_tflops": round(wl.attn_fwd_flops() / (kern["attn_fwd"] * 1e-3) / 1e12, 2)
+        if kern["attn_fwd"] else None,
+    }
+
+
+def secondary_fwd_bwd(hstu, name: str, steps: int, warmup: int, dev):
+    """Attention forward + backward of a training-step workload."""
+    import torch
+    from workloads import make_workload
+    wl = make_workload(name)
+    a = _attn_tensors(wl, dev)
+    o = torch.empty_like(a["v"])
+    grads = (torch.empty_like(a["q"]), torch.empty_like(a["k"]), torch.empty_like(a["v"]),
+             torch.empty_like(a["pt"]) if a["pt"] is not None else None,
+             torch.empty_like(a["tt"]) if a["tt"] is not None else None)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+
+    def fwd():
+        hstu.attn_fwd(a["q"], a["k"], a["v"], a["off"], timestamps=a["ts"], pos_table=a["pt"],
+                      time_table=a["tt"], alpha=wl.alpha, divisor=wl.divisor, out=o, workspace=ws)
+
+    def bwd():
+        hstu.attn_bwd(a["q"], a["k"], a["v"], a["d_o"], a["off"], timestamps=a["ts"], pos_table=a["pt"],
+                      time_table=a["tt"], alpha=wl.alpha, divisor=wl.divisor, workspace=ws, out=grads)
+
+    def step():
+        fwd()
+        bwd()
+
+    stream = torch.cuda.current_stream(dev)
+    ms_ev, ms_wall = time_steps(step, steps, warmup, stream)
+    ms = max(ms_ev, ms_wall)
+    kern = kernel_ms(hstu, step, steps, ["attn_fwd", "attn_bwd_kv", "attn_bwd_q"])
+    F_f, F_b = wl.attn_fwd_flops(), wl.attn_bwd_flops()
+    bwd_k = (kern["attn_bwd_kv"] or 0) + (kern["attn_bwd_q"] or 0)
+    return {
+        "workload": f"{name}: {wl.note}",
+        "fwd_bwd_tflops": round((F_f + F_b) / (ms * 1e-3) / 1e12, 2),
+        "ms_per_step": round(ms, 5),
+        "total_tokens": wl.total_tokens,
+        "kernel_ms": {k: (None if v is None else round(v, 5)) for k, v in kern.items()},
+        "bwd_kernels_tflops": round(F_b / (bwd_k * 1e-3) / 1e12, 2) if bwd_k else None,
+        "fwd_kernel_tflops": round(F_f / (kern["attn_fwd"] * 1e-3) / 1e12, 2) if kern["attn_fwd"] else None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="c3", help="attention-forward workload of the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true")
     args = ap.parse_args()
@@ -126,42 +279,24 @@ def main():
     hstu.load()
     dev = torch.device("cuda:0")
     wl = make_workload(args.workload)
-    t = lambda a, dt: torch.from_numpy(a).to(dev).to(dt)  # noqa: E731
-    q, k, v = t(wl.q, torch.bfloat16), t(wl.k, torch.bfloat16), t(wl.v, torch.bfloat16)
-    off = torch.from_numpy(wl.seq_offsets).to(dev)
-    ts = torch.from_numpy(wl.timestamps).to(dev) if wl.timestamps is not None else None
-    pt = t(wl.pos_table, torch.float32) if wl.pos_table is not None else None
-    tt = t(wl.time_table, torch.float32) if wl.time_table is not None else None
-    out = torch.empty_like(v)
+    a = _attn_tensors(wl, dev)
+    out = torch.empty_like(a["v"])
     ws = torch.empty(hstu.attn_workspace_size(wl.num_heads, wl.dqk, wl.dv, torch.bfloat16,
                                               wl.num_seqs, wl.total_tokens), dtype=torch.uint8,
                      device=dev)
 
     def step():
-        hstu.attn_fwd(q, k, v, off, timestamps=ts, pos_table=pt, time_table=tt,
-                      alpha=wl.alpha, divisor=wl.divisor, out=out, workspace=ws)
+        hstu.attn_fwd(a["q"], a["k"], a["v"], a["off"], timestamps=a["ts"], pos_table=a["pt"],
+                      time_table=a["tt"], alpha=wl.alpha, divisor=wl.divisor, out=out, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)   # the stream every kernel is launched on
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_events = ev0.elapsed_time(ev1) / args.steps
-    ms_step = max(ms_events, wall * 1e3 / args.steps)
+    ms_events, ms_wall = time_steps(step, args.steps, args.warmup, stream)
+    ms_step = max(ms_events, ms_wall)
+    kern = kernel_ms(hstu, step, args.steps, ["attn_fwd"])["attn_fwd"]
 
     flops = wl.attn_fwd_flops()
     value = flops / (ms_step * 1e-3) / 1e12
-    achieved = flops / (ms_events * 1e-3) / 1e12
-    tokens_s = wl.total_tokens / (ms_step * 1e-3)
+    achieved = flops / (kern * 1e-3) / 1e12
 
     res = {
         "metric": METRIC,
@@ -186,7 +321,7 @@ def main():
             "dv": wl.dv,
             "parallelism": "none (1 GPU)",
         },
-        "tokens_per_s": round(tokens_s, 1),
+        "tokens_per_s": round(wl.total_tokens / (ms_step * 1e-3), 1),
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 3),
@@ -194,11 +329,18 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": _traffic(),
-            "kernel": "attn_fwd_bf16_kernel<128,128> (+ work-list builder inside the timed call)",
+            "kernel": f"attn_fwd_bf16_kernel<{wl.dqk},{wl.dv}>",
             "algorithmic_flops_per_launch": flops,
-            "avg_launch_ms": round(ms_events, 5),
+            "avg_launch_ms": round(kern, 5),
+            "kernel_sha256_16": kernel_hash(),
         },
     }
+    if not args.no_secondary:
+        res["secondary"] = {
+            "layer_stack": secondary_layers(hstu, "c1", args.steps, args.warmup, dev),
+            "layer_jagged": secondary_layers(hstu, "c2", max(5, args.steps // 5), max(2, args.warmup // 10), dev),
+            "attn_fwd_bwd": secondary_fwd_bwd(hstu, "c4", args.steps, args.warmup, dev),
+        }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)

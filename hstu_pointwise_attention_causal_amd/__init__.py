@@ -14,7 +14,9 @@ from .ops import (  # noqa: F401
     attn_workspace_size,
     layer_fwd,
     make_layer_params,
+    timing_enable,
+    timing_read,
 )
 
 __all__ = ["HstuError", "load", "attn_fwd", "attn_bwd", "attn_workspace_size", "layer_fwd",
-           "make_layer_params"]
+           "make_layer_params", "timing_enable", "timing_read"]

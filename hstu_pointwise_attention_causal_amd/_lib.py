@@ -24,6 +24,7 @@ STATUS_NAMES = {
 EXPORTED = (
     "hstu_attn_workspace_size", "hstu_attn_fwd", "hstu_attn_bwd",
     "hstu_layer_workspace_size", "hstu_layer_fwd",
+    "hstu_timing_enable", "hstu_timing_read",
     "hstu_status_string", "hstu_last_error", "hstu_version",
 )
 
@@ -103,6 +104,10 @@ def load() -> ctypes.CDLL:
     lib.hstu_layer_workspace_size.restype = c
     lib.hstu_layer_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.hstu_layer_fwd.restype = c
+    lib.hstu_timing_enable.argtypes = [c]
+    lib.hstu_timing_enable.restype = c
+    lib.hstu_timing_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]
+    lib.hstu_timing_read.restype = c
     lib.hstu_status_string.argtypes = [c]
     lib.hstu_status_string.restype = ctypes.c_char_p
     lib.hstu_last_error.argtypes = []

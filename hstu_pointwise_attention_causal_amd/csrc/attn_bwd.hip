@@ -43,6 +43,7 @@
 #include "attn_common.h"
 #include "common.h"
 #include "launch.h"
+#include "timing.h"
 
 namespace hstu {
 
@@ -646,29 +647,50 @@ __global__ __launch_bounds__(kBThreads, 2) void attn_bwd_q_kernel(AttnBwdArgs g)
 }
 
 // ============================================================================
-// bias-table gradients: per-head sums of the key tiles' partial rows, in tile
-// order (one workgroup per head)
+// bias-table gradients: per-head sums of the key tiles' partial rows. One
+// workgroup per (64 consecutive partial-row slots, head): lane l of wave g
+// sums slot l over tiles g, g + 16, g + 32, ... (four independent chains),
+// then wave 0 adds the 16 group sums in order -- a fixed summation order.
 // ============================================================================
-__global__ __launch_bounds__(256) void attn_bwd_bias_reduce_kernel(AttnBwdArgs g) {
+constexpr int kReduceGroups = 16;
+
+__global__ __launch_bounds__(kReduceGroups * 64) void attn_bwd_bias_reduce_kernel(AttnBwdArgs g) {
   const AttnArgs& a = g.f;
-  const int h = blockIdx.x;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int slot = blockIdx.x * 64 + lane;
   const int tiles = a.tile_base[g.num_seqs];
-  const float* base = g.partial + static_cast<int64_t>(h) * g.tile_rows * g.grad_stride;
+  const int stride = g.grad_stride;
+  // time buckets past the reachable ones (>= kBwdTimeSlots) receive no pair
+  if (blockIdx.x == 0 && g.d_time)
+    for (int j = kBwdTimeSlots + threadIdx.x; j < a.time_buckets; j += blockDim.x)
+      g.d_time[h * a.time_buckets + j] = 0.f;
+  const float* col = g.partial + static_cast<int64_t>(h) * g.tile_rows * stride + slot;
+  __shared__ float part[kReduceGroups][64];
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  if (slot < stride) {
+    int t = grp;
+    for (; t + 3 * kReduceGroups < tiles; t += 4 * kReduceGroups) {
+      s0 += col[static_cast<int64_t>(t) * stride];
+      s1 += col[static_cast<int64_t>(t + kReduceGroups) * stride];
+      s2 += col[static_cast<int64_t>(t + 2 * kReduceGroups) * stride];
+      s3 += col[static_cast<int64_t>(t + 3 * kReduceGroups) * stride];
+    }
+    for (; t < tiles; t += kReduceGroups) s0 += col[static_cast<int64_t>(t) * stride];
+  }
+  part[grp][lane] = (s0 + s1) + (s2 + s3);
+  __syncthreads();
+  if (grp != 0 || slot >= stride) return;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kReduceGroups; ++i) s += part[i][lane];
   const int Bp = a.pos_buckets, Bt = a.time_buckets;
-  if (g.d_pos)
-    for (int i = threadIdx.x; i < Bp; i += blockDim.x) {
-      float s = 0.f;
-      for (int t = 0; t < tiles; ++t) s += base[static_cast<int64_t>(t) * g.grad_stride + i];
-      g.d_pos[h * Bp + i] = s;
-    }
-  if (g.d_time) {
-    const int o = g.d_pos ? Bp : 0;
-    for (int i = threadIdx.x; i < Bt; i += blockDim.x) {
-      float s = 0.f;
-      if (i < kBwdTimeSlots)
-        for (int t = 0; t < tiles; ++t) s += base[static_cast<int64_t>(t) * g.grad_stride + o + i];
-      g.d_time[h * Bt + i] = s;
-    }
+  const int pos_slots = g.d_pos ? Bp : 0;
+  if (slot < pos_slots) {
+    g.d_pos[h * Bp + slot] = s;
+  } else if (g.d_time) {
+    const int tb = slot - pos_slots;   // < kBwdTimeSlots
+    if (tb < Bt) g.d_time[h * Bt + tb] = s;
   }
 }
 
@@ -681,13 +703,21 @@ hipError_t launch_bwd_items(K kernel, const AttnBwdArgs& g, hipStream_t stream) 
 
 template <int D>
 hipError_t launch_bwd_dims(const AttnBwdArgs& g, hipStream_t stream) {
-  hipError_t e = launch_bwd_items(attn_bwd_kv_kernel<D, D>, g, stream);
+  hipError_t e;
+  {
+    TimedScope timed(kTimedAttnBwdKv, stream);
+    e = launch_bwd_items(attn_bwd_kv_kernel<D, D>, g, stream);
+  }
   if (e != hipSuccess) return e;
-  e = launch_bwd_items(attn_bwd_q_kernel<D, D>, g, stream);
+  {
+    TimedScope timed(kTimedAttnBwdQ, stream);
+    e = launch_bwd_items(attn_bwd_q_kernel<D, D>, g, stream);
+  }
   if (e != hipSuccess) return e;
   if (g.grad_stride > 0) {
-    hipLaunchKernelGGL(attn_bwd_bias_reduce_kernel, dim3(static_cast<unsigned>(g.f.num_heads)), dim3(256), 0, stream,
-                       g);
+    hipLaunchKernelGGL(attn_bwd_bias_reduce_kernel,
+                       dim3(static_cast<unsigned>((g.grad_stride + 63) / 64), static_cast<unsigned>(g.f.num_heads)),
+                       dim3(kReduceGroups * 64), 0, stream, g);
     e = hipGetLastError();
   }
   return e;

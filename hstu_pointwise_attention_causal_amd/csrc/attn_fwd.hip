@@ -26,6 +26,7 @@
 #include "attn_common.h"
 #include "common.h"
 #include "launch.h"
+#include "timing.h"
 
 namespace hstu {
 
@@ -669,6 +670,7 @@ hipError_t launch_attn_block_meta(const AttnArgs& a, int dqk, hipStream_t stream
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, hipStream_t stream) {
   hipError_t e = launch_attn_block_meta(a, dqk, stream);
   if (e != hipSuccess) return e;
+  TimedScope timed(kTimedAttnFwd, stream);
   if (dqk == 128 && dv == 128) return launch_items(attn_fwd_bf16_kernel<128, 128>, a, kThreads, stream);
   if (dqk == 64 && dv == 64) return launch_items(attn_fwd_bf16_kernel<64, 64>, a, kThreads, stream);
   if (dqk == 32 && dv == 32) return launch_items(attn_fwd_bf16_kernel<32, 32>, a, kThreads, stream);

@@ -18,6 +18,7 @@
 // output rounded to bf16.
 #include "common.h"
 #include "layer.h"
+#include "timing.h"
 
 namespace hstu {
 
@@ -214,6 +215,7 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(LnArgs a) {
 hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const int tiles = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
+  TimedScope timed(epi == kEpiResidual ? kTimedGemmOut : kTimedGemmUvqk, stream);
   if (epi == kEpiSilu)
     hipLaunchKernelGGL(gemm_nt_kernel<kEpiSilu>, dim3(tiles), dim3(kGemmThreads), 0, stream, g);
   else if (epi == kEpiResidual)
@@ -226,6 +228,7 @@ hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream) {
 hipError_t launch_ln_rows(const LnArgs& a, int width, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((a.rows + 3) / 4));
+  TimedScope timed(kTimedLayerNorm, stream);
   switch (width) {
     case 512: hipLaunchKernelGGL(ln_rows_kernel<512>, grid, dim3(256), 0, stream, a); break;
     case 1024: hipLaunchKernelGGL(ln_rows_kernel<1024>, grid, dim3(256), 0, stream, a); break;

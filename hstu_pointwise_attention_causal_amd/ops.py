@@ -124,19 +124,24 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets: tor
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tensor,
              seq_offsets: torch.Tensor, *, timestamps: Optional[torch.Tensor] = None,
              pos_table: Optional[torch.Tensor] = None, time_table: Optional[torch.Tensor] = None,
-             alpha: float = 1.0, divisor: float = 0.0, workspace: Optional[torch.Tensor] = None):
-    """hstu_attn_bwd: returns (dq, dk, dv, d_pos_table or None, d_time_table or None)."""
+             alpha: float = 1.0, divisor: float = 0.0, workspace: Optional[torch.Tensor] = None,
+             out: Optional[tuple] = None):
+    """hstu_attn_bwd: returns (dq, dk, dv, d_pos_table or None, d_time_table or None).
+    ``out`` may pass preallocated tensors in that order (the same shapes)."""
     lib = _lib.load()
     T, H = q.shape[0], q.shape[1]
     dqk, ldq = _token_view("q", q, H)
     _, ldk = _token_view("k", k, H)
     dv_, ldv = _token_view("v", v, H)
     _, lddo = _token_view("d_o", d_o, H)
-    dq = torch.empty((T, H, dqk), dtype=q.dtype, device=q.device)
-    dk = torch.empty((T, H, dqk), dtype=q.dtype, device=q.device)
-    dvv = torch.empty((T, H, dv_), dtype=q.dtype, device=q.device)
-    dP = torch.empty_like(pos_table) if pos_table is not None else None
-    dTt = torch.empty_like(time_table) if time_table is not None else None
+    if out is not None:
+        dq, dk, dvv, dP, dTt = out
+    else:
+        dq = torch.empty((T, H, dqk), dtype=q.dtype, device=q.device)
+        dk = torch.empty((T, H, dqk), dtype=q.dtype, device=q.device)
+        dvv = torch.empty((T, H, dv_), dtype=q.dtype, device=q.device)
+        dP = torch.empty_like(pos_table) if pos_table is not None else None
+        dTt = torch.empty_like(time_table) if time_table is not None else None
     d = _desc(H, dqk, dv_, q.dtype, alpha, divisor)
     j = _jagged(seq_offsets, T, timestamps)
     b = _bias(pos_table, time_table)
@@ -147,7 +152,8 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tenso
         workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
     _lib.check(lib.hstu_attn_bwd(ctypes.byref(d), ctypes.byref(j), ctypes.byref(b),
                                  _ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv, _ptr(d_o), lddo,
-                                 _ptr(dq), dqk * H, _ptr(dk), dqk * H, _ptr(dvv), dv_ * H,
+                                 _ptr(dq), _token_view("dq", dq, H)[1], _ptr(dk), _token_view("dk", dk, H)[1],
+                                 _ptr(dvv), _token_view("dv", dvv, H)[1],
                                  _ptr(dP), _ptr(dTt), _ptr(workspace), workspace.numel(),
                                  _stream_handle(q.device)))
     return dq, dk, dvv, dP, dTt
@@ -192,3 +198,17 @@ def layer_fwd(x: torch.Tensor, seq_offsets: torch.Tensor, params: "_lib.LayerPar
                                   _ptr(uvqk_out), _ptr(o_out), _ptr(workspace), workspace.numel(),
                                   _stream_handle(x.device)))
     return out
+
+
+def timing_enable(enable: bool = True) -> None:
+    """hstu_timing_enable: bracket every timed kernel launch with HIP events."""
+    _lib.check(_lib.load().hstu_timing_enable(int(bool(enable))))
+
+
+def timing_read(kernel: str):
+    """hstu_timing_read: (launches, total milliseconds) of `kernel` since its
+    last read; waits for the recorded events."""
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0.0)
+    _lib.check(_lib.load().hstu_timing_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)

@@ -187,6 +187,20 @@ hstu_status_t hstu_layer_fwd(const hstu_layer_params_t* params, const hstu_jagge
                              const void* x, void* y, void* uvqk_out, void* o_out,
                              void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * Kernel timing for measurement tools. While enabled (process-wide), every
+ * launch of a timed kernel is bracketed by two HIP events recorded on the
+ * caller's stream, which adds a small gap between launches; off by default.
+ * hstu_timing_read waits for the recorded events of all kernels, returns the
+ * number of launches of `kernel` and their summed duration in milliseconds
+ * since the last read of that kernel, and resets that kernel's totals.
+ * Kernel names: "attn_fwd", "attn_bwd_kv", "attn_bwd_q", "layer_gemm_uvqk",
+ * "layer_gemm_out", "layer_norm". Host pointers. Errors: HSTU_E_NULL,
+ * HSTU_E_SHAPE (unknown name), HSTU_E_HIP (an event failed).
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_timing_enable(int enable);
+hstu_status_t hstu_timing_read(const char* kernel, int64_t* launches, double* total_ms);
+
 /* Static English text of a status code. */
 const char* hstu_status_string(hstu_status_t status);
 
