@@ -23,6 +23,8 @@
 //
 // fp32 kernel (VALU): one thread per query row, fp32 throughout, for the
 // fp32 workload and as a precision reference path.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "common.h"
 #include "launch.h"
@@ -129,23 +131,33 @@ __device__ __forceinline__ float silu2_poly(float x) {
 template <int KCH, int VCH>
 __device__ __forceinline__ void issue_tile_loads(const char* kbase, const char* vbase, const int64_t* tsbase,
                                                  int64_t ldk, int64_t ldv, int n, int k0, int w, int lane,
-                                                 const uint32_t* koff, const uint32_t* voff, char* sk, char* sv,
-                                                 int64_t* st) {
+                                                 char* sk, char* sv, int64_t* st) {
   __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(kbase + static_cast<int64_t>(k0) * ldk * 2), 0,
       static_cast<int>(clamp_records(static_cast<int64_t>(n - k0) * ldk * 2)), kRsrcFlags);
   __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(vbase + static_cast<int64_t>(k0) * ldv * 2), 0,
       static_cast<int>(clamp_records(static_cast<int64_t>(n - k0) * ldv * 2)), kRsrcFlags);
+  // Per-lane source offsets are recomputed here rather than kept live across
+  // the tile loop: instruction i fills LDS slots [64 i, 64 i + 64) of the tile,
+  // slot s holding chunk (s % CH) ^ swizzle(row) of row s / CH.
 #pragma unroll
   for (int j = 0; j < (KCH + kWaves - 1) / kWaves; ++j) {
     const int i = w + j * kWaves;
-    if (i < KCH) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(sk + i * 1024), 16, koff[j], 0, 0, 0);
+    if (KCH % kWaves == 0 || i < KCH) {
+      const int sl = i * 64 + lane, r = sl / KCH, c = (sl % KCH) ^ (r & (KCH - 1));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(sk + i * 1024), 16,
+                                               static_cast<uint32_t>(r * ldk * 2 + c * 16), 0, 0, 0);
+    }
   }
 #pragma unroll
   for (int j = 0; j < (VCH + kWaves - 1) / kWaves; ++j) {
     const int i = w + j * kWaves;
-    if (i < VCH) __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(sv + i * 1024), 16, voff[j], 0, 0, 0);
+    if (VCH % kWaves == 0 || i < VCH) {
+      const int sl = i * 64 + lane, r = sl / VCH, c = (sl % VCH) ^ ((4 * r) & (VCH - 1));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(sv + i * 1024), 16,
+                                               static_cast<uint32_t>(r * ldv * 2 + c * 16), 0, 0, 0);
+    }
   }
   if (w == 0 && lane < kBN / 2) {
     __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
@@ -180,6 +192,7 @@ struct FwdSmem {
 // valid for every row of the wave, [8:3] lower time bucket of a kTwoTime block.
 constexpr int kInfoPolyAll = 4;
 constexpr int kInfoMasked = 1 << 9;
+constexpr int kInfoExactAll = 1 << 10;   // no row of the wave qualifies for the polynomial
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_kernel(AttnArgs a) {
@@ -221,7 +234,8 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
   if (has_time) {
     for (int i = tid; i < min(Bt, kTimeLds); i += kThreads) sm.time[i] = kLog2e * a.time_table[h * Bt + i];
   }
-  const float pos_last = has_pos ? kLog2e * a.pos_table[h * Bp + Bp - 1] : 0.f;   // bias of far pairs
+  const float pos_last = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(
+      has_pos ? kLog2e * a.pos_table[h * Bp + Bp - 1] : 0.f)));   // bias of far pairs
   // |bias| <= cmax for every pair: max |L P[h][.]| + max |L Tt[h][.]| (NaN propagates)
   float pmax = 0.f, tmax_ = 0.f;
   bool bad = false;
@@ -241,7 +255,10 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
     pmax = fmaxf(pmax, __shfl_xor(pmax, o, 64));
     tmax_ = fmaxf(tmax_, __shfl_xor(tmax_, o, 64));
   }
-  const float cmax = __builtin_amdgcn_ballot_w64(bad) ? __builtin_nanf("") : pmax + tmax_;
+  // wave-uniform values are moved to scalar registers
+  const float cmax = __builtin_amdgcn_ballot_w64(bad) ? __builtin_nanf("")
+                                                      : __int_as_float(__builtin_amdgcn_readfirstlane(
+                                                            __float_as_int(pmax + tmax_)));
 
   const __bf16* qp = static_cast<const __bf16*>(a.q);
   bf16x8_t qf[KB];
@@ -259,6 +276,10 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
   float qbound_max = qbound;
   for (int o = 1; o < 64; o <<= 1) qbound_max = fmaxf(qbound_max, __shfl_xor(qbound_max, o, 64));
   if (__builtin_amdgcn_ballot_w64(qbound != qbound)) qbound_max = __builtin_nanf("");
+  qbound_max = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(qbound_max)));
+  float qbound_min = qrow < n ? qbound : __builtin_inff();   // smallest row bound of the wave
+  for (int o = 1; o < 64; o <<= 1) qbound_min = fminf(qbound_min, __shfl_xor(qbound_min, o, 64));
+  qbound_min = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(qbound_min)));
   const int64_t tq = (has_time && qrow < n) ? a.ts[seq0 + qrow] : 0;
   int64_t wq_min = 0, wq_max = 0;   // timestamps of this wave's query rows (metadata of its block)
   if (has_time && qa < n) {
@@ -273,26 +294,12 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
   const int kv_end = min(n, q0 + kAttnBM);
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
-  // ---- per-lane offsets of the direct loads (constant over tiles)
-  uint32_t koff[KINST], voff[VINST];
-#pragma unroll
-  for (int j = 0; j < KINST; ++j) {   // instruction w + j*kWaves fills LDS slots [64 i, 64 i + 64)
-    const int s = (w + j * kWaves) * 64 + lane;
-    const int r = s / KCH, c = (s % KCH) ^ (r & (KCH - 1));
-    koff[j] = static_cast<uint32_t>(r * a.ldk * 2 + c * 16);
-  }
-#pragma unroll
-  for (int j = 0; j < VINST; ++j) {
-    const int s = (w + j * kWaves) * 64 + lane;
-    const int r = s / VCH, c = (s % VCH) ^ ((4 * r) & (VCH - 1));
-    voff[j] = static_cast<uint32_t>(r * a.ldv * 2 + c * 16);
-  }
   const char* kbase = static_cast<const char*>(a.k) + (seq0 * a.ldk + h * DQK) * 2;
   const char* vbase = static_cast<const char*>(a.v) + (seq0 * a.ldv + h * DV) * 2;
 
   auto issue_tile = [&] __device__(int kt, char* dk, char* dv, int64_t* dt) {
     issue_tile_loads<KCH, VCH>(kbase, vbase, has_time ? a.ts + seq0 : nullptr, a.ldk, a.ldv, n, kt * kBN, w, lane,
-                               koff, voff, dk, dv, dt);
+                               dk, dv, dt);
   };
   const int per_tile = loads_per_tile<KCH, VCH>(w);
 
@@ -323,12 +330,16 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[kb], s1, 0, 0, 0);
     }
   };
-  auto pv_block = [&] __device__(const char* vbuf, int kvb, const float* p) {
+  auto pack_p = [&] __device__(const float* p, bf16x8_t* pa) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pa[kk][i] = static_cast<__bf16>(p[kk * 8 + i]);
+  };
+  auto pv_block = [&] __device__(const char* vbuf, int kvb, const bf16x8_t* pp) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_t pa;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pa[i] = static_cast<__bf16>(p[kk * 8 + i]);
+      const bf16x8_t pa = pp[kk];
       const char* vb0 = vbuf + (kvb * 32 + kk * 16) * VCH * 16;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -345,7 +356,7 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
   float rec_clo = 0.f, rec_chi = 0.f, rec_kmax = 0.f;
   auto classify_window = [&] __device__(int win, const float* stime) {
     const int ka = (win * 64 + lane) * 32;
-    int info = kGeneral;
+    int info = kGeneral | kInfoMasked;   // a block with no pair for this wave: everything masked
     float clo = 0.f, chi = 0.f, km = 0.f;
     if (ka < n && ka <= qa + 31) {
       const BlockMeta m = meta_row[win * 64 + lane];
@@ -371,7 +382,10 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
         }
       }
       const bool polyall = !need_mask && fmaf(qbound_max, km, cmax) <= kPolyBound;
-      info = path | (polyall ? kInfoPolyAll : 0) | (blo << 3) | (need_mask ? kInfoMasked : 0);
+      // every row fails the bound when the smallest one does (fma is monotone in it)
+      const bool exactall = !need_mask && fmaf(qbound_min, km, cmax) > kPolyBound;
+      info = path | (polyall ? kInfoPolyAll : 0) | (exactall ? kInfoExactAll : 0) | (blo << 3) |
+             (need_mask ? kInfoMasked : 0);
     }
     rec_info = info;
     rec_clo = clo;
@@ -379,88 +393,76 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
     rec_kmax = km;
   };
 
-  // ---- scores -> P for one block (paths other than the fast tile)
-  auto eval_block = [&] __device__(const f32x16_t& s, int info, float c_lo, float c_hi, float kmax, int kt, int kvb,
-                                   const int64_t* tbuf, const float* spos, const float* stime, float* p) {
-    // Polynomial or exact SiLU, decided per row from that row's norm, the
-    // block's largest key norm and the bias bound of the whole table -- never
-    // from the bias path, so a block's path (which may depend on later rows'
-    // timestamps) cannot change a row's result. Masked blocks (which hold
-    // keys after some rows) always take the exact form.
+  // P of one block from its scores, for every block the common case does not
+  // cover: diagonal and sequence-end blocks, blocks with two time buckets or
+  // per-pair buckets, and blocks whose rows differ in SiLU form. The bias of
+  // each pair is computed one of three ways (constant, compare-and-select
+  // between two time buckets, per-pair lookups: always the same fp32 sum of
+  // the same table values), then SiLU is evaluated in the form each row's own
+  // bound allows, and the causal / sequence mask zeroes pairs past the row or
+  // the sequence (which also covers a block with no work for this wave).
+  auto general_block = [&] __device__(const f32x16_t& sc, int l, int k0, int kvb, const int64_t* rt,
+                                      const float* spos, const float* stime, bf16x8_t* pa) {
+    const int info = __builtin_amdgcn_readlane(rec_info, l);
     const int path = info & 3;
-    int mode = kPolyNone;
-    bool mine = false;
+    float x[16];
+    if (path == kUniform) {
+      const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_clo), l));
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = fmaf(sc[j], alpha_l, c);
+    } else if (path == kTwoTime) {
+      const float clo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_clo), l));
+      const float chi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_chi), l));
+      const int64_t lim = tq - ((int64_t(1) << (((info >> 3) & 63) + 1)) - 1);
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        x[j] = fmaf(sc[j], alpha_l, rt[kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)] <= lim ? chi : clo);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kvl = kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
+        float c = 0.f;
+        if (has_pos) {
+          const int pb = min(max(qrow - (k0 + kvl), 0), Bp - 1);
+          c = pb < kPosLdsFast ? spos[pb] : kLog2e * a.pos_table[h * Bp + pb];
+        }
+        if (has_time) c += stime[time_bucket64(tq - rt[kvl], Bt)];
+        x[j] = fmaf(sc[j], alpha_l, c);
+      }
+    }
+    float p[16];
     if (info & kInfoPolyAll) {
-      mode = kPolyAll;
-    } else if (!(info & kInfoMasked)) {
-      mine = fmaf(qbound, kmax, cmax) <= kPolyBound;
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(mine);
-      mode = bal == 0 ? kPolyNone : kPolyMixed;
-    }
-    if (path != kGeneral) {
-      int64_t lim = 0;
-      if (path == kTwoTime) lim = tq - ((int64_t(1) << (((info >> 3) & 63) + 1)) - 1);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int j = 0; j < 16; ++j) p[j] = silu2_poly(x[j]);
+    } else if (info & (kInfoExactAll | kInfoMasked)) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float c = c_lo;
-          if (path == kTwoTime) c = tbuf[kvb * 32 + 8 * g + 4 * lh + e] <= lim ? c_hi : c_lo;
-          const float x = fmaf(s[4 * g + e], alpha_l, c);
-          float r;
-          if (mode == kPolyAll) r = silu2_poly(x);
-          else if (mode == kPolyNone) r = silu2_exact(x);
-          else r = mine ? silu2_poly(x) : silu2_exact(x);
-          p[4 * g + e] = r;
-        }
-      }
+      for (int j = 0; j < 16; ++j) p[j] = silu2_exact(x[j]);
     } else {
-      const int k0 = kt * kBN;
+      // rows differ: each takes the form its own bound allows
+      const float km = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_kmax), l));
+      const bool poly_row = fmaf(qbound, km, cmax) <= kPolyBound;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int j = 0; j < 16; ++j) p[j] = poly_row ? silu2_poly(x[j]) : silu2_exact(x[j]);
+    }
+    if (info & kInfoMasked) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kvl = kvb * 32 + 8 * g + 4 * lh + e;
-          const int kv = k0 + kvl;
-          float c = 0.f;
-          if (has_pos) {
-            const int pb = min(max(qrow - kv, 0), Bp - 1);
-            c = pos_in_lds ? spos[pb] : (pb < kPosLdsFast ? spos[pb] : kLog2e * a.pos_table[h * Bp + pb]);
-          }
-          if (has_time) c += stime[time_bucket64(tq - tbuf[kvl], Bt)];
-          const float x = fmaf(s[4 * g + e], alpha_l, c);
-          float r;
-          if (mode == kPolyAll) r = silu2_poly(x);
-          else if (mode == kPolyNone) r = silu2_exact(x);
-          else r = mine ? silu2_poly(x) : silu2_exact(x);
-          p[4 * g + e] = (kv <= qrow && kv < n) ? r : 0.0f;
-        }
+      for (int j = 0; j < 16; ++j) {
+        const int kv = k0 + kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
+        p[j] = (kv <= qrow && kv < n) ? p[j] : 0.0f;
       }
     }
-  };
-
-  // scores -> P for block kvb of tile kt, record in lane `rl` of the window
-  auto eval_tile_block = [&] __device__(const f32x16_t& s, bool active, int rl, int kt, int kvb,
-                                        const int64_t* tbuf, const float* spos, const float* stime, float* p) {
-    const int info = __builtin_amdgcn_readlane(rec_info, rl);
-    const float clo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_clo), rl));
-    if (!active) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) p[j] = 0.f;
-    } else if ((info & 7) == (kUniform | kInfoPolyAll)) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) p[j] = silu2_poly(fmaf(s[j], alpha_l, clo));
-    } else {
-      const float chi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_chi), rl));
-      const float km = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_kmax), rl));
-      eval_block(s, info, clo, chi, km, kt, kvb, tbuf, spos, stime, p);
-    }
+    pack_p(p, pa);
   };
 
   // One tile step. Every LDS buffer it touches comes in through a __restrict__
   // parameter: the buffers being read (tile kt) and the ones the direct loads
   // are filling (tile kt + kBufs - 1) are then known to be disjoint, so the
   // compiler does not wait for the in-flight loads before reading LDS.
+  //
+  // Both products are straight-line code; one branch per tile chooses how P
+  // is computed, so only the packed P values cross a branch merge. The common
+  // case -- both blocks unmasked, each with one constant bias, every row on
+  // the polynomial -- is a few FMA-class operations per pair.
   auto tile_step = [&] __device__(const char* __restrict__ rk, const char* __restrict__ rv,
                                   const int64_t* __restrict__ rt, char* __restrict__ dk, char* __restrict__ dv,
                                   int64_t* __restrict__ dt, const float* __restrict__ spos,
@@ -470,19 +472,28 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
     // tile kt + kBufs - 1 reuses the buffer of tile kt - 1, released by the last barrier
     issue_tile(kt + kBufs - 1, dk, dv, dt);
     if (qa < n && k0 <= qa + 31) {
-      // Only the score -> P evaluation branches; both QK^T and P.V products are
-      // straight-line code, so O's accumulators never cross a branch merge.
-      // A block with no work for this wave (past its rows or past the
-      // sequence) takes P = 0.
       const int l0 = (2 * kt) & 63;
-      const bool act0 = k0 < n;                               // k0 <= qa + 31 already holds
-      const bool act1 = (k0 + 32 <= qa + 31) && (k0 + 32 < n);
       f32x16_t s0, s1;
       qk_tile(rk, s0, s1);
-      float p0[16], p1[16];
-      eval_tile_block(s0, act0, l0, kt, 0, rt, spos, stime, p0);
+      const int i0 = __builtin_amdgcn_readlane(rec_info, l0), i1 = __builtin_amdgcn_readlane(rec_info, l0 + 1);
+      constexpr int kFast = kUniform | kInfoPolyAll;
+      bf16x8_t p0[2], p1[2];
+      if ((i0 & (7 | kInfoMasked)) == kFast && (i1 & (7 | kInfoMasked)) == kFast && k0 + 32 <= qa) {
+        const float c0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_clo), l0));
+        const float c1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_clo), l0 + 1));
+        float q0[16], q1[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          q0[j] = silu2_poly(fmaf(s0[j], alpha_l, c0));
+          q1[j] = silu2_poly(fmaf(s1[j], alpha_l, c1));
+        }
+        pack_p(q0, p0);
+        pack_p(q1, p1);
+      } else {
+        general_block(s0, l0, k0, 0, rt, spos, stime, p0);
+        general_block(s1, l0 + 1, k0, 1, rt, spos, stime, p1);
+      }
       pv_block(rv, 0, p0);
-      eval_tile_block(s1, act1, l0 + 1, kt, 1, rt, spos, stime, p1);
       pv_block(rv, 1, p1);
     }
   };
