@@ -110,15 +110,18 @@ constexpr float kPolyC0 = 1.731778037e-01f, kPolyC1 = -6.804446619e-03f, kPolyC2
                 kPolyC3 = -6.863766511e-06f;
 constexpr float kPolyBound = 1.95f * kLog2e;   // in x' units; fit range is 2 log2(e)
 
+// Both forms return 2 g(x') (the factor 2 is exact and removed in the output
+// scale): exactly x' / (1/2 + 2^-x' / 2), or x' + y 2P(y) with y = x'^2 -- five
+// FMA-class operations.
 __device__ __forceinline__ float silu2_exact(float x) {
-  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x));
+  return x * __builtin_amdgcn_rcpf(fmaf(__builtin_amdgcn_exp2f(-x), 0.5f, 0.5f));
 }
 __device__ __forceinline__ float silu2_poly(float x) {
   const float y = x * x;
-  float p = fmaf(y, kPolyC3, kPolyC2);
-  p = fmaf(y, p, kPolyC1);
-  p = fmaf(y, p, kPolyC0);
-  return fmaf(x, 0.5f, y * p);
+  float p = fmaf(y, 2.0f * kPolyC3, 2.0f * kPolyC2);
+  p = fmaf(y, p, 2.0f * kPolyC1);
+  p = fmaf(y, p, 2.0f * kPolyC0);
+  return fmaf(y, p, x);
 }
 
 // Direct HBM -> LDS loads of one key tile (K, V and key timestamps). Kept out
@@ -336,19 +339,34 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
 #pragma unroll
       for (int i = 0; i < 8; ++i) pa[kk][i] = static_cast<__bf16>(p[kk * 8 + i]);
   };
-  auto pv_block = [&] __device__(const char* vbuf, int kvb, const bf16x8_t* pp) {
+  // V^T fragments of block kvb (B operands of P.V, keys in the permuted order):
+  // vf[kk * NB + nb] for the 16-key step kk and output column group nb.
+  auto read_v = [&] __device__(const char* vbuf, int kvb, bf16x8_t* vf) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8_t pa = pp[kk];
       const char* vb0 = vbuf + (kvb * 32 + kk * 16) * VCH * 16;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const bf16x4_t v0 = tr_read(vb0 + v_lds[nb]);
         const bf16x4_t v1 = tr_read(vb0 + v_lds[nb] + 8 * VCH * 16);
-        const bf16x8_t vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, oacc[nb], 0, 0, 0);
+        vf[kk * NB + nb] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     }
+  };
+  auto pv_mfma = [&] __device__(const bf16x8_t* vf, const bf16x8_t* pp) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pp[kk], vf[kk * NB + nb], oacc[nb], 0, 0, 0);
+  };
+  // K fragments (A operands of S^T) of both blocks of a tile: kf[2 kb + kvb].
+  auto read_k = [&] __device__(const char* kbuf, bf16x8_t* kf) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int kvb = 0; kvb < 2; ++kvb)
+        kf[2 * kb + kvb] = *reinterpret_cast<const bf16x8_t*>(kbuf + kvb * 32 * KCH * 16 + k_lds[kb]);
   };
 
   // ---- classification of 64 key blocks (one per lane) for this wave's rows
@@ -454,10 +472,20 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
     pack_p(p, pa);
   };
 
-  // One tile step. Every LDS buffer it touches comes in through a __restrict__
-  // parameter: the buffers being read (tile kt) and the ones the direct loads
-  // are filling (tile kt + kBufs - 1) are then known to be disjoint, so the
-  // compiler does not wait for the in-flight loads before reading LDS.
+  constexpr int kFast = kUniform | kInfoPolyAll;
+  // Block 1 of the previous tile: its V fragments and P, whose products run
+  // at the start of the next step, while that step's K reads are in flight.
+  bf16x8_t vf1[2 * NB], p1[2];
+  bool prev_active = false;
+
+  // One step, entered right after the barrier that publishes tile kt:
+  //   loads of tile kt + 1 into the buffer tile kt - 1 has released; K
+  //   fragments of tile kt (their latency hidden by block 1's products of tile
+  //   kt - 1); S^T of both blocks; V of block 0 read while P is computed;
+  //   block 0's products; V of block 1 read; barrier.
+  // Every LDS buffer comes in through a __restrict__ parameter: the step only
+  // reads tile kt's buffers and only fills tile kt + 1's, so the compiler does
+  // not wait for the in-flight loads before reading LDS.
   //
   // Both products are straight-line code; one branch per tile chooses how P
   // is computed, so only the packed P values cross a branch merge. The common
@@ -468,16 +496,25 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
                                   int64_t* __restrict__ dt, const float* __restrict__ spos,
                                   const float* __restrict__ stime, int kt) {
     const int k0 = kt * kBN;
+    // tile kt + 1 reuses the buffer of tile kt - 1, released by the last barrier
+    issue_tile(kt + 1, dk, dv, dt);
     if ((kt & 31) == 0) classify_window(kt >> 5, stime);
-    // tile kt + kBufs - 1 reuses the buffer of tile kt - 1, released by the last barrier
-    issue_tile(kt + kBufs - 1, dk, dv, dt);
-    if (qa < n && k0 <= qa + 31) {
+    const bool active = qa < n && k0 <= qa + 31;
+    bf16x8_t kf[2 * KB];
+    if (active) read_k(rk, kf);
+    if (prev_active) pv_mfma(vf1, p1);
+    if (active) {
       const int l0 = (2 * kt) & 63;
-      f32x16_t s0, s1;
-      qk_tile(rk, s0, s1);
+      f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * kb], qf[kb], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * kb + 1], qf[kb], s1, 0, 0, 0);
+      }
+      bf16x8_t vf0[2 * NB];
+      read_v(rv, 0, vf0);
       const int i0 = __builtin_amdgcn_readlane(rec_info, l0), i1 = __builtin_amdgcn_readlane(rec_info, l0 + 1);
-      constexpr int kFast = kUniform | kInfoPolyAll;
-      bf16x8_t p0[2], p1[2];
+      bf16x8_t p0[2];
       if ((i0 & (7 | kInfoMasked)) == kFast && (i1 & (7 | kInfoMasked)) == kFast && k0 + 32 <= qa) {
         const float c0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_clo), l0));
         const float c1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec_clo), l0 + 1));
@@ -493,29 +530,28 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
         general_block(s0, l0, k0, 0, rt, spos, stime, p0);
         general_block(s1, l0 + 1, k0, 1, rt, spos, stime, p1);
       }
-      pv_block(rv, 0, p0);
-      pv_block(rv, 1, p1);
+      pv_mfma(vf0, p0);
+      read_v(rv, 1, vf1);
     }
+    prev_active = active;
+    wait_vmcnt(0);    // this wave's loads of tile kt + 1 have landed
+    tile_barrier();   // ... and every other wave's; tile kt's buffers are free
   };
 
-  // tiles 0..kBufs-2 in flight, then wait for tile 0
-  if (ntiles > 0) {
-#pragma unroll
-    for (int t = 0; t < kBufs - 1; ++t) issue_tile(t, sm.k[t], sm.v[t], sm.t[t]);
-  }
-  wait_vmcnt((kBufs - 2) * per_tile);
+  // tile 0 in flight, then wait for it
+  if (ntiles > 0) issue_tile(0, sm.k[0], sm.v[0], sm.t[0]);
+  wait_vmcnt(0);
   __syncthreads();   // also publishes the bias tables staged with ordinary LDS stores
 
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt % kBufs, nxt = (kt + kBufs - 1) % kBufs;
+    const int buf = kt % kBufs, nxt = (kt + 1) % kBufs;
     tile_step(sm.k[buf], sm.v[buf], sm.t[buf], sm.k[nxt], sm.v[nxt], sm.t[nxt], sm.pos, sm.time, kt);
-    wait_vmcnt((kBufs - 2) * per_tile);   // this wave's loads of tile kt + 1 have landed
-    tile_barrier();                        // ... and every other wave's
   }
+  if (prev_active) pv_mfma(vf1, p1);
   wait_vmcnt(0);
 
-  // ---- epilogue: oacc[nb][j] = log2(e) * N * O[qa + 8(j/4) + 4 lh + j%4][nb*32 + lr]
-  const float scale = (a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n)) / kLog2e;
+  // ---- epilogue: oacc[nb][j] = 2 log2(e) * N * O[qa + 8(j/4) + 4 lh + j%4][nb*32 + lr]
+  const float scale = (a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n)) / (2.0f * kLog2e);
   __bf16* op = static_cast<__bf16*>(a.o) + (seq0 + qa) * a.ldo + h * DV + lr;
   if (qa + 31 < n) {
 #pragma unroll
