@@ -9,7 +9,9 @@ namespace hstu {
 enum GemmEpilogue { kEpiSilu = 0, kEpiResidual = 1, kEpiNone = 2 };
 
 // C[M,N] (bf16, ldc) = epi(A[M,K] B[N,K]^T + bias[N]); A, B bf16 row-major.
-// kEpiSilu: SiLU; kEpiResidual: + R[M,N] (bf16, ldr). K must be a multiple of 64.
+// kEpiSilu: SiLU; kEpiResidual: + R[M,N] (bf16, ldr). K must be a multiple of
+// 64, N, ldc and ldr multiples of 8, C and R 16-byte aligned (else
+// hipErrorInvalidValue).
 struct GemmArgs {
   const void* a;
   int64_t lda;

@@ -6,12 +6,15 @@
 //
 // GEMM. C[M,N] = A[M,K] B[N,K]^T: A holds tokens, B is a weight matrix in the
 // nn.Linear [out, in] layout of the neurarch exported block, so both MFMA
-// operands are contiguous along K and no transpose is ever needed. A 128x128
-// output tile per workgroup, 4 waves of 64x64 (2x2 blocks of
+// operands are contiguous along K and no transpose is ever needed. Wide
+// outputs (N >= 1024) take 256x256 tiles of 8 waves with 128x64 each, narrow
+// ones 128x128 tiles of 4 waves with 64x64 each (blocks of
 // v_mfma_f32_32x32x16_bf16), K in steps of 64. A and B tiles go HBM -> LDS with
 // buffer_load ... lds (rows past M / N arrive as zeros), 16-byte chunks of each
 // row XOR-swizzled by the row index so the ds_read_b128 of 32 consecutive rows
-// hits distinct banks; two stages in flight.
+// hits distinct banks; the next stage loads while the current one multiplies.
+// The epilogue (bias, SiLU or residual) stages each wave's results through LDS
+// so that every global access is a row-contiguous 16-byte one.
 //
 // LayerNorm. One wave per token row; the row lives in registers (8 features
 // per lane per 512), mean and variance by wave butterflies (two passes, fp32),
@@ -27,137 +30,227 @@ namespace {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int kRsrcFlags = 0x00020000;
 
-constexpr int GBM = 128, GBN = 128, GBK = 64;
-constexpr int kGemmThreads = 256;
+constexpr int GBK = 64;            // K per stage
 constexpr int kChunks = GBK / 8;   // 16-byte chunks per tile row
 
 __device__ __forceinline__ uint32_t clamp_u32(int64_t bytes) {
   return bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes));
 }
 
-// One K-step of A and B tiles, direct to LDS. Instruction i (of 16 per operand)
-// fills LDS slots [64 i, 64 i + 64): wave w issues i = w, w + 4, w + 8, w + 12.
+// s_waitcnt vmcnt(n) lgkmcnt(0) for a small compile-time n.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);   // lgkmcnt(0), expcnt not waited
+}
+
+// GEMM tile shape: BM x BN outputs per workgroup, WM x WN per wave
+// ((WM/32) x (WN/32) blocks of v_mfma_f32_32x32x16_bf16), `ST` K stages of 64
+// in LDS.
+template <int BM, int BN, int WM, int WN, int ST>
+struct GemmShape {
+  static constexpr int kWavesM = BM / WM, kWavesN = BN / WN, kWaves = kWavesM * kWavesN;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int MB = WM / 32, NB = WN / 32;
+  static constexpr int kAInst = BM * kChunks / 64;   // 1 KB direct loads per stage
+  static constexpr int kBInst = BN * kChunks / 64;
+  static constexpr int kAPer = kAInst / kWaves, kBPer = kBInst / kWaves;
+  static constexpr int kLoadsPerStage = kAPer + kBPer;   // per wave
+  static constexpr int kStagesAhead = ST - 1;
+  static_assert(kAInst % kWaves == 0 && kBInst % kWaves == 0, "loads spread evenly over the waves");
+  static_assert(ST >= 2 && ST <= 4, "stages");
+};
+
+// One K stage of A and B tiles, direct to LDS. Instruction i fills LDS slots
+// [64 i, 64 i + 64) of its operand: slot s holds chunk (s % 8) ^ (row & 7) of
+// row s / 8 (rows past M / N arrive as zeros).
+template <class S>
 __device__ __forceinline__ void gemm_issue(const char* abase, int64_t lda, uint32_t arecs, const char* bbase,
-                                           int64_t ldb, uint32_t brecs, int k0, int w, const uint32_t* aoff,
-                                           const uint32_t* boff, char* __restrict__ sa, char* __restrict__ sb) {
+                                           int64_t ldb, uint32_t brecs, int k0, int w, int lane,
+                                           char* __restrict__ sa, char* __restrict__ sb) {
   __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase + k0 * 2), 0,
                                                                  static_cast<int>(arecs), kRsrcFlags);
   __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(bbase + k0 * 2), 0,
                                                                  static_cast<int>(brecs), kRsrcFlags);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = w + 4 * j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sa + i * 1024), 16, aoff[j], 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sb + i * 1024), 16, boff[j], 0, 0, 0);
+  for (int j = 0; j < S::kAPer; ++j) {
+    const int i = w + S::kWaves * j, sl = i * 64 + lane, r = sl / kChunks, c = (sl % kChunks) ^ (r & 7);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sa + i * 1024), 16,
+                                             static_cast<uint32_t>(r * lda * 2 + c * 16), 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < S::kBPer; ++j) {
+    const int i = w + S::kWaves * j, sl = i * 64 + lane, r = sl / kChunks, c = (sl % kChunks) ^ (r & 7);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sb + i * 1024), 16,
+                                             static_cast<uint32_t>(r * ldb * 2 + c * 16), 0, 0, 0);
   }
 }
 
-// One K-step: MFMAs on stage (rs_a, rs_b) while the next step's tiles stream
-// into (ds_a, ds_b). All four buffers arrive as __restrict__ pointers, so the
-// compiler knows the reads never touch the stage being filled and does not
-// wait for the in-flight loads before reading LDS.
+// One K step: MFMAs on stage (rs_a, rs_b) while the stage ST - 1 steps ahead
+// streams into (ds_a, ds_b), then wait for the next stage and synchronize.
+// All buffers arrive as __restrict__ pointers, so the compiler knows the reads
+// never touch the stage being filled and does not wait for the in-flight
+// loads before reading LDS.
+template <class S>
 __device__ __forceinline__ void gemm_step(const GemmArgs& g, const char* __restrict__ rs_a,
                                           const char* __restrict__ rs_b, char* __restrict__ ds_a,
-                                          char* __restrict__ ds_b, bool issue_next, int k_next,
-                                          const char* abase, uint32_t arecs, const char* bbase, uint32_t brecs,
-                                          int w, const uint32_t* aoff, const uint32_t* boff,
-                                          const uint32_t (&a_lds)[2][4], const uint32_t (&b_lds)[2][4],
-                                          f32x16_t (&acc)[2][2]) {
-  if (issue_next) gemm_issue(abase, g.lda, arecs, bbase, g.ldb, brecs, k_next, w, aoff, boff, ds_a, ds_b);
+                                          char* __restrict__ ds_b, int kt, int nsteps, const char* abase,
+                                          uint32_t arecs, const char* bbase, uint32_t brecs, int w, int lane,
+                                          const uint32_t (&a_lds)[S::MB], const uint32_t (&b_lds)[S::NB],
+                                          f32x16_t (&acc)[S::MB][S::NB]) {
+  const bool issue = kt + S::kStagesAhead < nsteps;
+  if (issue) gemm_issue<S>(abase, g.lda, arecs, bbase, g.ldb, brecs, (kt + S::kStagesAhead) * GBK, w, lane, ds_a, ds_b);
+  const int lh = lane >> 5;
 #pragma unroll
   for (int k16 = 0; k16 < 4; ++k16) {
-    bf16x8_t af[2], bfr[2];
+    // logical chunk 2 k16 + lh of each row; the row's swizzle is folded into the offsets
+    const uint32_t cx = static_cast<uint32_t>((2 * k16 + lh) * 16);
+    bf16x8_t af[S::MB], bfr[S::NB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      af[mb] = *reinterpret_cast<const bf16x8_t*>(rs_a + a_lds[mb][k16]);
-      bfr[mb] = *reinterpret_cast<const bf16x8_t*>(rs_b + b_lds[mb][k16]);
-    }
+    for (int mb = 0; mb < S::MB; ++mb) af[mb] = *reinterpret_cast<const bf16x8_t*>(rs_a + (a_lds[mb] ^ cx));
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int nb = 0; nb < S::NB; ++nb) bfr[nb] = *reinterpret_cast<const bf16x8_t*>(rs_b + (b_lds[nb] ^ cx));
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+    for (int mb = 0; mb < S::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < S::NB; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[mb][nb], 0, 0, 0);
   }
+  // The next stage must have landed; the ones issued since may stay in flight.
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0);   // next stage landed, this stage's reads done
+  const int ahead = nsteps - 1 - (kt + 1);   // stages issued beyond the next one, capped below
+  if (ahead >= S::kStagesAhead - 1) {
+    if constexpr (S::kStagesAhead == 3) wait_vm_lgkm0<2 * S::kLoadsPerStage>();
+    else if constexpr (S::kStagesAhead == 2) wait_vm_lgkm0<S::kLoadsPerStage>();
+    else wait_vm_lgkm0<0>();
+  } else if (S::kStagesAhead == 3 && ahead == 1) {
+    wait_vm_lgkm0<S::kLoadsPerStage>();
+  } else {
+    wait_vm_lgkm0<0>();
+  }
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-template <int EPI>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) char sa[2][GBM * GBK * 2];
-  __shared__ __attribute__((aligned(16))) char sb[2][GBN * GBK * 2];
+template <int EPI, int BM, int BN, int WM, int WN, int ST>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_nt_kernel(GemmArgs g) {
+  using S = GemmShape<BM, BN, WM, WN, ST>;
+  __shared__ __attribute__((aligned(16))) char sa[ST][BM * GBK * 2];
+  __shared__ __attribute__((aligned(16))) char sb[ST][BN * GBK * 2];
 
-  const int tiles_n = (g.N + GBN - 1) / GBN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-  const int m0 = tm * GBM, n0 = tn * GBN;
+  // Workgroups are dealt to the 8 XCDs in turn (block b to XCD b % 8). Tile t
+  // of the row-major tile order goes to a block on XCD t / ceil-share, so each
+  // XCD's L2 serves a contiguous band of A rows against all of B.
+  const int tiles_n = (g.N + BN - 1) / BN;
+  const int tiles = gridDim.x, xcd = blockIdx.x % 8, q = tiles / 8, r = tiles % 8;
+  const int t = xcd * q + min(xcd, r) + blockIdx.x / 8;
+  const int tm = t / tiles_n, tn = t % tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / S::kWavesN, wn = w % S::kWavesN;
 
-  uint32_t aoff[4], boff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int s = (w + 4 * j) * 64 + lane;
-    const int r = s / kChunks, c = (s % kChunks) ^ (r & 7);
-    aoff[j] = static_cast<uint32_t>(r * g.lda * 2 + c * 16);
-    boff[j] = static_cast<uint32_t>(r * g.ldb * 2 + c * 16);
-  }
   const char* abase = static_cast<const char*>(g.a) + static_cast<int64_t>(m0) * g.lda * 2;
   const char* bbase = static_cast<const char*>(g.b) + static_cast<int64_t>(n0) * g.ldb * 2;
   // rows past M (N) are out of range: records end right after the last valid row's K range
   const uint32_t arecs = g.M > m0 ? clamp_u32(static_cast<int64_t>(g.M - m0 - 1) * g.lda * 2 + g.K * 2) : 0u;
   const uint32_t brecs = g.N > n0 ? clamp_u32(static_cast<int64_t>(g.N - n0 - 1) * g.ldb * 2 + g.K * 2) : 0u;
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[S::MB][S::NB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < S::MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16_t{};
+    for (int nb = 0; nb < S::NB; ++nb) acc[mb][nb] = f32x16_t{};
 
-  uint32_t a_lds[2][4], b_lds[2][4];   // byte offsets of this lane's fragments in a stage
+  // byte offset of this lane's row in a stage, with the row's chunk swizzle
+  // (r & 7) << 4 folded in: fragment offset = row offset ^ (chunk << 4)
+  uint32_t a_lds[S::MB], b_lds[S::NB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < S::MB; ++mb) {
+    const int r = wm * WM + mb * 32 + lr;
+    a_lds[mb] = static_cast<uint32_t>(r * kChunks * 16 + ((r & 7) << 4));
+  }
 #pragma unroll
-    for (int k16 = 0; k16 < 4; ++k16) {
-      const int ra = wm * 64 + mb * 32 + lr, rb = wn * 64 + mb * 32 + lr, c = 2 * k16 + lh;
-      a_lds[mb][k16] = (ra * kChunks + (c ^ (ra & 7))) * 16;
-      b_lds[mb][k16] = (rb * kChunks + (c ^ (rb & 7))) * 16;
-    }
-
-  gemm_issue(abase, g.lda, arecs, bbase, g.ldb, brecs, 0, w, aoff, boff, sa[0], sb[0]);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  const int nsteps = g.K / GBK;
-  for (int kt = 0; kt < nsteps; kt += 2) {   // stages alternate statically: 0 -> 1 -> 0 ...
-    gemm_step(g, sa[0], sb[0], sa[1], sb[1], kt + 1 < nsteps, (kt + 1) * GBK, abase, arecs, bbase, brecs, w,
-              aoff, boff, a_lds, b_lds, acc);
-    if (kt + 1 < nsteps)
-      gemm_step(g, sa[1], sb[1], sa[0], sb[0], kt + 2 < nsteps, (kt + 2) * GBK, abase, arecs, bbase, brecs, w,
-                aoff, boff, a_lds, b_lds, acc);
+  for (int nb = 0; nb < S::NB; ++nb) {
+    const int r = wn * WN + nb * 32 + lr;
+    b_lds[nb] = static_cast<uint32_t>(r * kChunks * 16 + ((r & 7) << 4));
   }
 
-  // epilogue: acc[mb][nb][j] = C[m0 + 64 wm + 32 mb + 8(j/4) + 4 lh + j%4][n0 + 64 wn + 32 nb + lr]
-  __bf16* cp = static_cast<__bf16*>(g.c);
-  const __bf16* rp = static_cast<const __bf16*>(g.r);
+  const int nsteps = g.K / GBK;
+  // stages 0 .. ST-2 in flight, wait for stage 0
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int n = n0 + wn * 64 + nb * 32 + lr;
-    if (n >= g.N) continue;
-    const float bias = g.bias ? g.bias[n] : 0.f;
+  for (int s_ = 0; s_ < ST - 1; ++s_)
+    if (s_ < nsteps) gemm_issue<S>(abase, g.lda, arecs, bbase, g.ldb, brecs, s_ * GBK, w, lane, sa[s_], sb[s_]);
+  wait_vm_lgkm0<0>();
+  __syncthreads();
+  // stages rotate statically; step t reads stage t % ST and fills (t + ST - 1) % ST
+  for (int kt = 0; kt < nsteps; kt += ST) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int u = 0; u < ST; ++u) {
+      if (kt + u >= nsteps) break;
+      gemm_step<S>(g, sa[u], sb[u], sa[(u + ST - 1) % ST], sb[(u + ST - 1) % ST], kt + u, nsteps, abase, arecs,
+                   bbase, brecs, w, lane, a_lds, b_lds, acc);
+    }
+  }
+
+  // Epilogue. The products ran as B A^T, so acc[mb][nb][4 jq + i] holds
+  // C[m][n + i] for m = 32 mb + lr, n = 32 nb + 8 jq + 4 lh (wave-tile
+  // coordinates). Each 32-row slice (one mb) goes through a wave-private fp32
+  // staging area of 32 rows x WN columns in the (now idle) A stage buffers,
+  // 16-byte chunks XOR-swizzled by row, and leaves as row-contiguous 16-byte
+  // stores of 8 bf16: one instruction covers 8 rows x 128 bytes. Bias and SiLU
+  // apply before staging, the residual after it; bf16 rounding happens once.
+  constexpr int kRowChunks = WN / 4;             // 16-byte fp32 chunks per staged row
+  static_assert(kRowChunks == 16, "staging swizzle assumes 64-column wave tiles");
+  static_assert(S::kWaves * 32 * WN * 4 <= sizeof(sa), "staging fits in the A stage buffers");
+  char* stage = &sa[0][0] + w * (32 * WN * 4);
+  float bias[S::NB][4][4];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = m0 + wm * 64 + mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
-        if (m >= g.M) continue;
-        float x = acc[mb][nb][j] + bias;
-        if (EPI == kEpiSilu) x = x / (1.0f + __expf(-x));
-        if (EPI == kEpiResidual) x += static_cast<float>(rp[static_cast<int64_t>(m) * g.ldr + n]);
-        cp[static_cast<int64_t>(m) * g.ldc + n] = static_cast<__bf16>(x);
+  for (int nb = 0; nb < S::NB; ++nb)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      const int n = n0 + wn * WN + nb * 32 + 8 * jq + 4 * lh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bias[nb][jq][i] = (g.bias && n + i < g.N) ? g.bias[n + i] : 0.f;
+    }
+  char* cp = static_cast<char*>(g.c);
+  const char* rp = static_cast<const char*>(g.r);
+  const int rr = lane >> 3, rc = lane & 7;   // read-back: row rr (+ 8 it), chunk pair rc
+#pragma unroll
+  for (int mb = 0; mb < S::MB; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        f32x4_t x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = acc[mb][nb][4 * jq + i] + bias[nb][jq][i];
+          if (EPI == kEpiSilu) v = silu_f32(v);
+          x[i] = v;
+        }
+        const int chunk = nb * 8 + 2 * jq + lh;
+        *reinterpret_cast<f32x4_t*>(stage + lr * (WN * 4) + ((chunk ^ (lr & 15)) << 4)) = x;
       }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int row = rr + 8 * it;
+      const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stage + row * (WN * 4) + (((2 * rc) ^ (row & 15)) << 4));
+      const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stage + row * (WN * 4) + (((2 * rc + 1) ^ (row & 15)) << 4));
+      const int m = m0 + wm * WM + mb * 32 + row, n = n0 + wn * WN + 8 * rc;
+      if (m >= g.M || n >= g.N) continue;
+      float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if (EPI == kEpiResidual) {
+        const bf16x8_t rv = *reinterpret_cast<const bf16x8_t*>(rp + (static_cast<int64_t>(m) * g.ldr + n) * 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] += static_cast<float>(rv[i]);
+      }
+      bf16x8_t out;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = static_cast<__bf16>(x[i]);
+      *reinterpret_cast<bf16x8_t*>(cp + (static_cast<int64_t>(m) * g.ldc + n) * 2) = out;
+    }
   }
 }
 
@@ -212,17 +305,33 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(LnArgs a) {
 
 }  // namespace
 
+namespace {
+template <int EPI, int BM, int BN, int WM, int WN, int ST>
+hipError_t launch_gemm_shape(const GemmArgs& g, hipStream_t stream) {
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_nt_kernel<EPI, BM, BN, WM, WN, ST>), dim3(tiles), dim3((BM / WM) * (BN / WN) * 64), 0,
+                     stream, g);
+  return hipGetLastError();
+}
+template <int EPI>
+hipError_t launch_gemm_epi(const GemmArgs& g, hipStream_t stream) {
+  // wide outputs: 256 x 256 tiles, 8 waves of 128 x 64; narrow ones: 128 x 128, 4 waves of 64 x 64
+  if (g.N >= 1024) return launch_gemm_shape<EPI, 256, 256, 128, 64, 2>(g, stream);
+  return launch_gemm_shape<EPI, 128, 128, 64, 64, 2>(g, stream);
+}
+}  // namespace
+
 hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  const int tiles = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
+  // 16-byte epilogue accesses: eight-column groups, 16-byte aligned rows
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (g.K % GBK != 0 || g.N % 8 != 0 || g.ldc % 8 != 0 || !a16(g.c) ||
+      (epi == kEpiResidual && (g.ldr % 8 != 0 || !a16(g.r))))
+    return hipErrorInvalidValue;
   TimedScope timed(epi == kEpiResidual ? kTimedGemmOut : kTimedGemmUvqk, stream);
-  if (epi == kEpiSilu)
-    hipLaunchKernelGGL(gemm_nt_kernel<kEpiSilu>, dim3(tiles), dim3(kGemmThreads), 0, stream, g);
-  else if (epi == kEpiResidual)
-    hipLaunchKernelGGL(gemm_nt_kernel<kEpiResidual>, dim3(tiles), dim3(kGemmThreads), 0, stream, g);
-  else
-    hipLaunchKernelGGL(gemm_nt_kernel<kEpiNone>, dim3(tiles), dim3(kGemmThreads), 0, stream, g);
-  return hipGetLastError();
+  if (epi == kEpiSilu) return launch_gemm_epi<kEpiSilu>(g, stream);
+  if (epi == kEpiResidual) return launch_gemm_epi<kEpiResidual>(g, stream);
+  return launch_gemm_epi<kEpiNone>(g, stream);
 }
 
 hipError_t launch_ln_rows(const LnArgs& a, int width, hipStream_t stream) {
