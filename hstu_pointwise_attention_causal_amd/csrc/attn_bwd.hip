@@ -184,9 +184,15 @@ struct BwdSmem {
   float time[kBwdTimeSlots];    // log2(e) Tt[h][.]
 };
 
+// Bias-table gradients of one key tile, summed in LDS. Position buckets: one
+// table per wave (its lanes' pairs rarely share a bucket within one add).
+// Time buckets: one column per lane of each wave ([wave][bucket][lane]) --
+// near the diagonal most pairs of a block share a bucket, and lane-private
+// columns keep those adds free of same-address serialization (and of atomics:
+// plain read-modify-write measured faster than conflict-free LDS atomics).
 struct BwdGradSmem {
   float gpos[kBW][kBwdPosMax];
-  float gtime[kBW][kBwdTimeSlots];
+  float gtime[kBW][kBwdTimeSlots][64];
 };
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
   if (has_time)
     for (int i = tid; i < min(Bt, kBwdTimeSlots); i += kBThreads) sm.time[i] = kLog2e * a.time_table[h * Bt + i];
   for (int i = tid; i < kBW * kBwdPosMax; i += kBThreads) (&gs.gpos[0][0])[i] = 0.f;
-  for (int i = tid; i < kBW * kBwdTimeSlots; i += kBThreads) (&gs.gtime[0][0])[i] = 0.f;
+  for (int i = tid; i < kBW * kBwdTimeSlots * 64; i += kBThreads) (&gs.gtime[0][0][0])[i] = 0.f;
   const float pos_last = has_pos ? kLog2e * a.pos_table[h * Bp + Bp - 1] : 0.f;
 
   // K and V rows of this lane's key: B operands of S = Q K^T and dA = dO V^T
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
   const int tq0 = k0 / kBBN;                       // first query tile: holds the diagonal
   const int ntq = (n + kBBN - 1) / kBBN - tq0;     // >= 1
   float* gpos = gs.gpos[w];
-  float* gtime = gs.gtime[w];
+  float* gtime = &gs.gtime[w][0][lane];   // bucket b of this lane: gtime[64 b]
 
   auto step = [&] __device__(const char* __restrict__ rq, const char* __restrict__ rd,
                              const int64_t* __restrict__ rt, const BlockMeta* __restrict__ rm,
@@ -344,12 +350,8 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
           }
           if (has_pos) far_acc += slo + shi;
           if (has_time) {
-            slo = row16_sum(slo);
-            if ((lane & 15) == 0) atomicAdd(&gtime[c.tlo], slo);
-            if (c.path == kBTwoTime) {
-              shi = row16_sum(shi);
-              if ((lane & 15) == 0) atomicAdd(&gtime[c.tlo + 1], shi);
-            }
+            gtime[64 * c.tlo] += slo;
+            if (c.path == kBTwoTime) gtime[64 * (c.tlo + 1)] += shi;
           }
         } else {
 #pragma unroll
@@ -370,8 +372,13 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
             silu_and_grad(x, pl, dsl);
             p[r] = valid ? pl : 0.f;
             ds[r] = valid ? da[r] * dsl : 0.f;
-            if (has_pos) atomicAdd(&gpos[pb], ds[r]);
-            if (has_time) atomicAdd(&gtime[tb], ds[r]);
+            // masked pairs add nothing; pairs in the last position bucket go
+            // to the register sum of the far pairs
+            if (has_pos && valid) {
+              if (pb < Bp - 1) atomicAdd(&gpos[pb], ds[r]);
+              else far_acc += ds[r];
+            }
+            if (has_time) gtime[64 * tb] += ds[r];
           }
         }
       }
@@ -446,13 +453,21 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
         prow[i] = s * inv_n;
       }
     if (has_time) {
+      // bucket tid / 4: thread (tid & 3) sums wave (tid & 3)'s 64 lane columns,
+      // then the 4 threads (adjacent lanes) combine, in a fixed order
+      static_assert(kBThreads == 4 * kBwdTimeSlots && kBW == 4, "one bucket per 4 threads");
       float* trow = prow + (has_pos ? Bp : 0);
-      for (int i = tid; i < kBwdTimeSlots; i += kBThreads) {
-        float s = 0.f;
+      const int tb = tid >> 2, ww = tid & 3;
+      const f32x4_t* col = reinterpret_cast<const f32x4_t*>(&gs.gtime[ww][tb][0]);
+      float s = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < kBW; ++ww) s += gs.gtime[ww][i];
-        trow[i] = s * inv_n;
+      for (int c4 = 0; c4 < 16; ++c4) {
+        const f32x4_t v4 = col[c4];
+        s += (v4[0] + v4[1]) + (v4[2] + v4[3]);
       }
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      if (ww == 0) trow[tb] = s * inv_n;
     }
   }
 }
