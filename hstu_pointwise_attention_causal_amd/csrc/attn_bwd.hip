@@ -296,11 +296,36 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
   float* gpos = gs.gpos[w];
   float* gtime = &gs.gtime[w][0][lane];   // bucket b of this lane: gtime[64 b]
 
+  // dV += P^T dO and dK += dS^T Q of a block run one block late: they are
+  // issued right after the next block's S and dA products, so they execute
+  // while that block's P and dS are computed. Carried between blocks: the
+  // packed P and dS and the block's transposed dO and Q fragments (read before
+  // the barrier that may recycle their tile). Zero-initialized, the first
+  // block's late products add nothing.
+  bf16x8_t pa_prev[2], sa_prev[2], ob_prev[2 * NV], qt_prev[2 * NQ];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) pa_prev[kk] = sa_prev[kk] = bf16x8_t{};
+#pragma unroll
+  for (int i = 0; i < 2 * NV; ++i) ob_prev[i] = bf16x8_t{};
+#pragma unroll
+  for (int i = 0; i < 2 * NQ; ++i) qt_prev[i] = bf16x8_t{};
+  auto late_products = [&] __device__() __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int nb = 0; nb < NV; ++nb)
+        dva[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_prev[kk], ob_prev[kk * NV + nb], dva[nb], 0, 0, 0);
+#pragma unroll
+      for (int nb = 0; nb < NQ; ++nb)
+        dka[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa_prev[kk], qt_prev[kk * NQ + nb], dka[nb], 0, 0, 0);
+    }
+  };
+
   auto step = [&] __device__(const char* __restrict__ rq, const char* __restrict__ rd,
                              const int64_t* __restrict__ rt, const BlockMeta* __restrict__ rm,
                              char* __restrict__ nq, char* __restrict__ nd, int64_t* __restrict__ nt,
                              BlockMeta* __restrict__ nm, const float* __restrict__ spos,
-                             const float* __restrict__ stime, int t) {
+                             const float* __restrict__ stime, int t) __attribute__((always_inline)) {
     const int i0 = (tq0 + t) * kBBN;
     if (t + 1 < ntq)
       issue_rows_tile<QCH, DCH>(qbase, dbase, a.ldq, g.lddo, tsbase, meta_row, n, i0 + kBBN, w, lane, qoff, doff, nq,
@@ -312,15 +337,34 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
       f32x16_t s = f32x16_t{}, da = f32x16_t{};
       const char* qblk = rq + qb * 32 * QCH * 16;
       const char* dblk = rd + qb * 32 * DCH * 16;
+      // all A fragments first (their reads overlap), then the two chains
+      bf16x8_t qfr[KB], dfr[VB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) qfr[kb] = *reinterpret_cast<const bf16x8_t*>(qblk + q_row[kb]);
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) dfr[vb] = *reinterpret_cast<const bf16x8_t*>(dblk + d_row[vb]);
 #pragma unroll
       for (int kb = 0; kb < (KB > VB ? KB : VB); ++kb) {
-        if (kb < KB)
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(qblk + q_row[kb]), kf[kb], s,
-                                                      0, 0, 0);
-        if (kb < VB)
-          da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(dblk + d_row[kb]), vf[kb],
-                                                       da, 0, 0, 0);
+        if (kb < KB) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[kb], kf[kb], s, 0, 0, 0);
+        if (kb < VB) da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr[kb], vf[kb], da, 0, 0, 0);
       }
+      // the previous block's dV, dK products, then this block's transposed
+      // fragments for its own (one block later)
+      late_products();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const char* dst = dblk + kk * 16 * DCH * 16;
+        const char* qst = qblk + kk * 16 * QCH * 16;
+#pragma unroll
+        for (int nb = 0; nb < NV; ++nb)
+          ob_prev[kk * NV + nb] =
+              __builtin_shufflevector(tr_read(dst + d_tr0[nb]), tr_read(dst + d_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int nb = 0; nb < NQ; ++nb)
+          qt_prev[kk * NQ + nb] =
+              __builtin_shufflevector(tr_read(qst + q_tr0[nb]), tr_read(qst + q_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // the products above go out before the P / dS arithmetic
       // s[4g+e], da[4g+e]: query row qa + 8g + 4lh + e, key `key`
       float p[16], ds[16];
       if (!active) {
@@ -382,30 +426,15 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
           }
         }
       }
-      // dV += P^T dO, dK += dS^T Q over the block's 32 query rows (two 16-row steps)
+      // P and dS of this block's 32 query rows (two 16-row steps), for the
+      // late products
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8_t pa, sa;
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          pa[i] = static_cast<__bf16>(p[kk * 8 + i]);
-          sa[i] = static_cast<__bf16>(ds[kk * 8 + i]);
+          pa_prev[kk][i] = static_cast<__bf16>(p[kk * 8 + i]);
+          sa_prev[kk][i] = static_cast<__bf16>(ds[kk * 8 + i]);
         }
-        const char* dst = dblk + kk * 16 * DCH * 16;
-        const char* qst = qblk + kk * 16 * QCH * 16;
-#pragma unroll
-        for (int nb = 0; nb < NV; ++nb) {
-          const bf16x8_t ob = __builtin_shufflevector(tr_read(dst + d_tr0[nb]), tr_read(dst + d_tr1[nb]), 0, 1, 2, 3,
-                                                      4, 5, 6, 7);
-          dva[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, ob, dva[nb], 0, 0, 0);
-        }
-#pragma unroll
-        for (int nb = 0; nb < NQ; ++nb) {
-          const bf16x8_t qb16 = __builtin_shufflevector(tr_read(qst + q_tr0[nb]), tr_read(qst + q_tr1[nb]), 0, 1, 2,
-                                                        3, 4, 5, 6, 7);
-          dka[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, qb16, dka[nb], 0, 0, 0);
-        }
-      }
     }
   };
 
@@ -420,6 +449,8 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
     wait_vmcnt(0);
     tile_barrier();
   }
+
+  late_products();   // the last block's
 
   // ---- dK, dV: accumulator [i][r] holds key kw + 8(r/4) + 4 lh + r%4, column 32 i + lr
   const float inv_n = a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n);
