@@ -357,6 +357,91 @@ def layer_fwd_rows(x, params: dict, seq_offsets, rows, *, num_heads: int, dqk: i
     return out
 
 
+def layer_norm_bwd(x, gamma, d_y, eps: float):
+    """Gradients of y = LN(x) * gamma + beta (over the last axis) for upstream
+    d_y, float64: with xhat = (x - mean) / sqrt(var + eps), g = d_y * gamma,
+        dx = (g - mean(g) - xhat * mean(g * xhat)) / sqrt(var + eps)
+    (mean over the normalised axis), d_gamma = sum over rows of d_y * xhat,
+    d_beta = sum over rows of d_y. Returns (dx, d_gamma, d_beta)."""
+    x = np.asarray(x, dtype=np.float64)
+    d_y = np.asarray(d_y, dtype=np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(((x - mu) ** 2).mean(axis=-1, keepdims=True) + eps)
+    xhat = (x - mu) * rstd
+    g = d_y * _f64(gamma)
+    dx = (g - g.mean(axis=-1, keepdims=True) - xhat * (g * xhat).mean(axis=-1, keepdims=True)) * rstd
+    return dx, (d_y * xhat).sum(axis=0), d_y.sum(axis=0)
+
+
+def layer_bwd(x, params: dict, seq_offsets, d_out, *, num_heads: int, dqk: int, dv: int,
+              timestamps=None, eps: float = 1e-6, alpha: float = 1.0, divisor: float = 0.0):
+    """Gradients of sum(X' * d_out) for ``layer_fwd``, float64, by the chain
+    rule through its four steps in reverse (the layer of the daiwk
+    reproduction notes' flowchart and core formula, trained at every position
+    as their core formula describes):
+
+      4. X' = X + Y W_out^T + b_out:  d_b_out = sum_t d_out,
+         d_W_out = d_out^T Y,  dY = d_out W_out,  and d_out reaches X directly.
+      3. Y = LN(O; g2, b2) * u:  du = dY * LN(O),  then ``layer_norm_bwd`` of
+         O with upstream dY * u gives dO, d_g2, d_b2.
+      2. O = attention(q, k, v):  ``attn_bwd`` gives dq, dk, dv and the bias
+         tables' gradients.
+      1. G = SiLU(Z), Z = LN(X; g1, b1) W_uvqk^T + b_uvqk:  dG = [du|dv|dq|dk]
+         (the split order), dZ = dG * SiLU'(Z) with SiLU'(z) = sig(z) (1 +
+         z (1 - sig(z))),  d_b_uvqk = sum_t dZ,  d_W_uvqk = dZ^T LN(X),
+         d LN(X) = dZ W_uvqk, then ``layer_norm_bwd`` of X.
+
+    Returns (dX, dict of parameter gradients with the keys of ``params``
+    prefixed "d_"; a table absent from ``params`` has no gradient entry).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    T, D = x.shape
+    H = num_heads
+    w_uvqk, w_out = _f64(params["w_uvqk"]), _f64(params["w_out"])
+    # forward, keeping what the backward reads
+    xn = layer_norm(x, params["ln_in_gamma"], params["ln_in_beta"], eps)
+    z = xn @ w_uvqk.T
+    if params.get("b_uvqk") is not None:
+        z = z + _f64(params["b_uvqk"])
+    g = silu(z)
+    c_v, c_q, c_k = H * dv, 2 * H * dv, 2 * H * dv + H * dqk
+    u = g[:, 0:c_v]
+    vv = g[:, c_v:c_q].reshape(T, H, dv)
+    qq = g[:, c_q:c_k].reshape(T, H, dqk)
+    kk = g[:, c_k:c_k + H * dqk].reshape(T, H, dqk)
+    attn_kw = dict(alpha=alpha, divisor=divisor, pos_table=params.get("pos_table"),
+                   time_table=params.get("time_table"), timestamps=timestamps)
+    o = attn_fwd(qq, kk, vv, seq_offsets, **attn_kw).reshape(T, H * dv)
+    on = layer_norm(o, params["ln_out_gamma"], params["ln_out_beta"], eps)
+    y = on * u
+    grads = {}
+    # 4. output projection and residual
+    grads["d_b_out"] = d_out.sum(axis=0)
+    grads["d_w_out"] = d_out.T @ y
+    d_y = d_out @ w_out
+    # 3. post-pooling norm and U gate
+    d_u = d_y * on
+    d_o, grads["d_ln_out_gamma"], grads["d_ln_out_beta"] = layer_norm_bwd(
+        o, params["ln_out_gamma"], d_y * u, eps)
+    # 2. attention
+    dq, dk, dvv, dP, dTt = attn_bwd(qq, kk, vv, d_o.reshape(T, H, dv), seq_offsets, **attn_kw)
+    if params.get("pos_table") is not None:
+        grads["d_pos_table"] = dP
+    if params.get("time_table") is not None:
+        grads["d_time_table"] = dTt
+    # 1. projection with SiLU, input norm
+    d_g = np.concatenate([d_u, dvv.reshape(T, H * dv), dq.reshape(T, H * dqk),
+                          dk.reshape(T, H * dqk)], axis=1)
+    sig = sigmoid(z)
+    d_z = d_g * sig * (1.0 + z * (1.0 - sig))
+    grads["d_b_uvqk"] = d_z.sum(axis=0)
+    grads["d_w_uvqk"] = d_z.T @ xn
+    d_x_ln, grads["d_ln_in_gamma"], grads["d_ln_in_beta"] = layer_norm_bwd(
+        x, params["ln_in_gamma"], d_z @ w_uvqk, eps)
+    return d_out + d_x_ln, grads
+
+
 def stack_fwd(x, layers, seq_offsets, *, num_heads: int, dqk: int, dv: int,
               timestamps=None, eps: float = 1e-6):
     """A stack of HSTU layers applied in order (the neurarch model card lists

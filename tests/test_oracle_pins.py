@@ -438,3 +438,80 @@ def test_exponential_timestamps_mean_gap():
     ts = exponential_timestamps(rng, [200000])
     gap = np.diff(ts).mean()
     assert 3550 < gap < 3650   # floor() lowers the mean by ~0.5 s
+
+
+# ----------------------------------------------------------------------------
+# layer backward
+# ----------------------------------------------------------------------------
+def _layer_loss(x, p, off, ts, d_out, H, d, eps=1e-6):
+    out, _ = O.layer_fwd(x, p, off, num_heads=H, dqk=d, dv=d, timestamps=ts, eps=eps)
+    return float(np.sum(out * d_out))
+
+
+@pytest.mark.parametrize("time", [True, False])
+def test_layer_bwd_finite_differences(time):
+    """Every entry of X and of every parameter (both norms, both projections
+    and their biases, both bias tables) against central differences of
+    sum(X' * dOut), fp64, h = 1e-6, two jagged sequences."""
+    H, d, D = 2, 3, 6
+    x, p, off, ts = _tiny_layer(31, [3, 4], D=D, H=H, d=d, time=time)
+    rng = np.random.default_rng(32)
+    d_out = rng.standard_normal(x.shape)
+    dx, grads = O.layer_bwd(x, p, off, d_out, num_heads=H, dqk=d, dv=d, timestamps=ts)
+    h = 1e-6
+
+    def fd_of(get, put):
+        base = get().copy()
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            for sgn in (1, -1):
+                a = base.copy()
+                a[idx] += sgn * h
+                put(a)
+                fd[idx] += sgn * _layer_loss(x_cur[0], p, off, ts, d_out, H, d)
+            fd[idx] /= 2 * h
+        put(base)
+        return fd
+
+    x_cur = [x.copy()]
+    fd = fd_of(lambda: x_cur[0], lambda a: x_cur.__setitem__(0, a))
+    assert _rel(fd, dx) < 1e-6
+    for key in ("w_uvqk", "b_uvqk", "w_out", "b_out", "ln_in_gamma", "ln_in_beta",
+                "ln_out_gamma", "ln_out_beta", "pos_table", "time_table"):
+        if p.get(key) is None:
+            assert ("d_" + key) not in grads
+            continue
+        fd = fd_of(lambda k=key: p[k], lambda a, k=key: p.__setitem__(k, a))
+        assert _rel(fd, grads["d_" + key]) < 1e-6, key
+
+
+def test_layer_norm_bwd_rows_are_mean_free_and_orthogonal_to_xhat():
+    """LN's input gradient has zero mean and, with eps = 0 and gamma = 1, is
+    orthogonal to the normalised row (the projection of the upstream gradient
+    onto the complement of span{1, xhat}, scaled by 1/sigma)."""
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((7, 16)) * 3 + 1
+    dy = rng.standard_normal((7, 16))
+    dx, dg, db = O.layer_norm_bwd(x, np.ones(16), dy, 0.0)
+    mu = x.mean(1, keepdims=True)
+    xhat = (x - mu) / np.sqrt(((x - mu) ** 2).mean(1, keepdims=True))
+    assert np.abs(dx.sum(1)).max() < 1e-12
+    assert np.abs((dx * xhat).sum(1)).max() < 1e-10
+    assert np.allclose(db, dy.sum(0)) and np.allclose(dg, (dy * xhat).sum(0))
+
+
+def test_layer_bwd_zero_out_projection_leaves_only_residual_and_weight_grads():
+    """W_out = 0: dX = dOut exactly, and every gradient upstream of the output
+    projection (norms, W_uvqk, tables) is exactly zero, while d_W_out = dOut^T Y."""
+    H, d, D = 2, 3, 6
+    x, p, off, ts = _tiny_layer(34, [5, 2], D=D, H=H, d=d)
+    p["w_out"] = np.zeros_like(p["w_out"])
+    d_out = np.random.default_rng(35).standard_normal(x.shape)
+    dx, grads = O.layer_bwd(x, p, off, d_out, num_heads=H, dqk=d, dv=d, timestamps=ts)
+    assert np.array_equal(dx, d_out)
+    for key in ("d_w_uvqk", "d_b_uvqk", "d_ln_in_gamma", "d_ln_in_beta", "d_ln_out_gamma",
+                "d_ln_out_beta", "d_pos_table", "d_time_table"):
+        assert not np.any(grads[key]), key
+    _, inter = O.layer_fwd(x, p, off, num_heads=H, dqk=d, dv=d, timestamps=ts)
+    assert _rel(grads["d_w_out"], d_out.T @ inter["y"]) < 1e-13
+    assert _rel(grads["d_b_out"], d_out.sum(0)) < 1e-13
