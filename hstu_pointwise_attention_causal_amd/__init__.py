@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     attn_bwd,
     attn_fwd,
     attn_workspace_size,
+    layer_bwd,
     layer_fwd,
     make_layer_params,
     timing_enable,
@@ -19,4 +20,4 @@ from .ops import (  # noqa: F401
 )
 
 __all__ = ["HstuError", "load", "attn_fwd", "attn_bwd", "attn_workspace_size", "layer_fwd",
-           "make_layer_params", "timing_enable", "timing_read"]
+           "layer_bwd", "make_layer_params", "timing_enable", "timing_read"]

@@ -24,6 +24,7 @@ STATUS_NAMES = {
 EXPORTED = (
     "hstu_attn_workspace_size", "hstu_attn_fwd", "hstu_attn_bwd",
     "hstu_layer_workspace_size", "hstu_layer_fwd",
+    "hstu_layer_bwd_workspace_size", "hstu_layer_bwd",
     "hstu_timing_enable", "hstu_timing_read",
     "hstu_status_string", "hstu_last_error", "hstu_version",
 )
@@ -75,6 +76,12 @@ class LayerParams(ctypes.Structure):
     ]
 
 
+class LayerGrads(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "d_ln_in_gamma", "d_ln_in_beta", "d_w_uvqk", "d_b_uvqk", "d_ln_out_gamma",
+        "d_ln_out_beta", "d_w_out", "d_b_out", "d_pos_table", "d_time_table")]
+
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
@@ -104,6 +111,10 @@ def load() -> ctypes.CDLL:
     lib.hstu_layer_workspace_size.restype = c
     lib.hstu_layer_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.hstu_layer_fwd.restype = c
+    lib.hstu_layer_bwd_workspace_size.argtypes = [_P, _P, ctypes.POINTER(_SZ)]
+    lib.hstu_layer_bwd_workspace_size.restype = c
+    lib.hstu_layer_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.hstu_layer_bwd.restype = c
     lib.hstu_timing_enable.argtypes = [c]
     lib.hstu_timing_enable.restype = c
     lib.hstu_timing_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]

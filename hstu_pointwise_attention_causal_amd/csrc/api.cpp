@@ -4,6 +4,7 @@
 // enqueued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -326,6 +327,81 @@ hstu_status_t check_layer(const hstu_layer_params_t* p, const hstu_jagged_t* j) 
   return ok();
 }
 
+// Backward of one layer: rows per block of the LayerNorm-backward and
+// column-sum kernels (their partial rows are summed in a fixed order), and the
+// K splits of the two weight-gradient GEMMs (K = tokens).
+constexpr int kLnBwdRows = 64;
+constexpr int kColSumRows = 64;
+
+int weight_grad_splits(int64_t M, int64_t N, int64_t T) {
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t ksteps = (T + 63) / 64;
+  int64_t s = (512 + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, ksteps / 8));
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 64)));
+}
+
+struct LayerBwdLayout {
+  hstu::WorklistLayout attn;
+  BwdLayout abwd;
+  size_t xn_off = 0, z_off = 0, g_off = 0, o_off = 0, y_off = 0, dyy_off = 0, do_off = 0, dg_off = 0, dxn_off = 0;
+  size_t part_off = 0, scratch_off = 0, bytes = 0;
+  int splits_uvqk = 1, splits_out = 1;
+};
+
+LayerBwdLayout layer_bwd_layout(const hstu_layer_params_t* p, const hstu_jagged_t* j) {
+  LayerBwdLayout L;
+  const int64_t T = j->total_tokens, H = p->attn.num_heads, D = p->embed_dim;
+  const int64_t n1 = H * (2 * p->attn.dv + 2 * p->attn.dqk), hv = H * p->attn.dv;
+  L.attn = hstu::worklist_layout(j->num_seqs, T, static_cast<int>(H), hstu::kAttnBM);
+  L.abwd = bwd_layout(L.attn, &p->attn, &p->bias);
+  L.splits_uvqk = weight_grad_splits(n1, D, T);
+  L.splits_out = weight_grad_splits(D, hv, T);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  take(L.abwd.bytes);   // the attention's work list, metadata and bias partials first
+  L.xn_off = take(static_cast<size_t>(T * D * 2));
+  L.z_off = take(static_cast<size_t>(T * n1 * 2));
+  L.g_off = take(static_cast<size_t>(T * n1 * 2));
+  L.o_off = take(static_cast<size_t>(T * hv * 2));
+  L.y_off = take(static_cast<size_t>(T * hv * 2));
+  L.dyy_off = take(static_cast<size_t>(T * hv * 2));
+  L.do_off = take(static_cast<size_t>(T * hv * 2));
+  L.dg_off = take(static_cast<size_t>(T * n1 * 2));
+  L.dxn_off = take(static_cast<size_t>(T * D * 2));
+  // fp32 partial rows, reused stage by stage (stream order), and the sums' scratch
+  const int64_t pl = hstu::ln_bwd_partial_rows(T, kLnBwdRows), pc = hstu::colsum_partial_rows(T, kColSumRows);
+  const int64_t part = std::max({pl * 2 * hv, pl * 2 * D, pc * n1, pc * D, L.splits_uvqk * n1 * D,
+                                 static_cast<int64_t>(L.splits_out) * D * hv});
+  const int64_t scratch = std::max({hstu::sum_rows_scratch_floats(pl, 2 * hv), hstu::sum_rows_scratch_floats(pl, 2 * D),
+                                    hstu::sum_rows_scratch_floats(pc, n1), hstu::sum_rows_scratch_floats(pc, D),
+                                    hstu::sum_rows_scratch_floats(L.splits_uvqk, n1 * D),
+                                    hstu::sum_rows_scratch_floats(L.splits_out, D * hv)});
+  L.part_off = take(static_cast<size_t>(part) * 4);
+  L.scratch_off = take(static_cast<size_t>(std::max<int64_t>(scratch, 1)) * 4);
+  L.bytes = off;
+  return L;
+}
+
+hstu_status_t check_layer_grads(const hstu_layer_params_t* p, const hstu_layer_grads_t* g) {
+  if (!g) return fail(HSTU_E_NULL, "gradient outputs are NULL");
+  if (!g->d_ln_in_gamma || !g->d_ln_in_beta || !g->d_w_uvqk || !g->d_b_uvqk || !g->d_ln_out_gamma ||
+      !g->d_ln_out_beta || !g->d_w_out || !g->d_b_out)
+    return fail(HSTU_E_NULL, "a parameter gradient output is NULL");
+  const bool has_pos = p->bias.pos_table != nullptr, has_time = p->bias.time_table != nullptr;
+  if (has_pos != (g->d_pos_table != nullptr) || has_time != (g->d_time_table != nullptr))
+    return fail(HSTU_E_NULL, "a table gradient must be given exactly when its table is");
+  const float* outs[] = {g->d_ln_in_gamma, g->d_ln_in_beta, g->d_w_uvqk, g->d_b_uvqk, g->d_ln_out_gamma,
+                         g->d_ln_out_beta, g->d_w_out, g->d_b_out};
+  for (const float* o : outs)
+    if (!aligned16(o)) return fail(HSTU_E_ALIGN, "parameter gradients must be 16-byte aligned");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -410,6 +486,171 @@ hstu_status_t hstu_layer_fwd(const hstu_layer_params_t* p, const hstu_jagged_t* 
   g2.a = yy; g2.lda = hv; g2.b = p->w_out; g2.ldb = hv; g2.c = y; g2.ldc = D; g2.bias = p->b_out;
   g2.r = x; g2.ldr = D; g2.M = static_cast<int>(T); g2.N = static_cast<int>(D); g2.K = static_cast<int>(hv);
   if ((e = hstu::launch_gemm_nt(g2, hstu::kEpiResidual, stream)) != hipSuccess) return hip_fail(e, "output projection");
+  return ok();
+}
+
+hstu_status_t hstu_layer_bwd_workspace_size(const hstu_layer_params_t* params, const hstu_jagged_t* jag,
+                                            size_t* bytes) {
+  if (!bytes) return fail(HSTU_E_NULL, "bytes is NULL");
+  hstu_status_t st = check_layer(params, jag);
+  if (st != HSTU_OK) return st;
+  if ((st = check_bwd_support(&params->attn, &params->bias)) != HSTU_OK) return st;
+  *bytes = layer_bwd_layout(params, jag).bytes;
+  return ok();
+}
+
+hstu_status_t hstu_layer_bwd(const hstu_layer_params_t* p, const hstu_jagged_t* jag, const void* x,
+                             const void* d_out, void* dx, const hstu_layer_grads_t* grads, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+  hstu_status_t st = check_layer(p, jag);
+  if (st != HSTU_OK) return st;
+  if ((st = check_bwd_support(&p->attn, &p->bias)) != HSTU_OK) return st;
+  if ((st = check_layer_grads(p, grads)) != HSTU_OK) return st;
+  const int64_t T = jag->total_tokens, H = p->attn.num_heads, D = p->embed_dim;
+  const int64_t dqk = p->attn.dqk, dv = p->attn.dv;
+  const int64_t n1 = H * (2 * dv + 2 * dqk), hv = H * dv;
+  if (T > 0 && (!x || !d_out || !dx)) return fail(HSTU_E_NULL, "x, d_out or dx is NULL");
+  if (T > 0 && (!aligned16(x) || !aligned16(d_out) || !aligned16(dx)))
+    return fail(HSTU_E_ALIGN, "x, d_out and dx must be 16-byte aligned");
+  const Range rdx = view_range(dx, T, D, D, 2);
+  if (overlaps(rdx, view_range(x, T, D, D, 2)) || overlaps(rdx, view_range(d_out, T, D, D, 2)))
+    return fail(HSTU_E_ALIAS, "dx overlaps x or d_out");
+  const LayerBwdLayout L = layer_bwd_layout(p, jag);
+  if (workspace_bytes < L.bytes || (L.bytes > 0 && !workspace))
+    return fail(HSTU_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, L.bytes);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e;
+  if (T == 0 || jag->num_seqs == 0) {
+    // no tokens: every parameter gradient is zero
+    const std::pair<float*, int64_t> z[] = {
+        {grads->d_ln_in_gamma, D}, {grads->d_ln_in_beta, D}, {grads->d_w_uvqk, n1 * D}, {grads->d_b_uvqk, n1},
+        {grads->d_ln_out_gamma, hv}, {grads->d_ln_out_beta, hv}, {grads->d_w_out, D * hv}, {grads->d_b_out, D},
+        {grads->d_pos_table, p->bias.pos_table ? H * p->bias.pos_buckets : 0},
+        {grads->d_time_table, p->bias.time_table ? H * p->bias.time_buckets : 0}};
+    for (const auto& pr : z)
+      if (pr.first && pr.second > 0 && (e = hstu::launch_fill_f32(pr.first, pr.second, 0.f, stream)) != hipSuccess)
+        return hip_fail(e, "zeroing the parameter gradients");
+    return ok();
+  }
+  if (!aligned16(workspace)) return fail(HSTU_E_ALIGN, "workspace must be 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  auto bf = [&](size_t o) { return static_cast<void*>(ws + o); };
+  void *xn = bf(L.xn_off), *z = bf(L.z_off), *g = bf(L.g_off), *o = bf(L.o_off), *yy = bf(L.y_off);
+  void *dyy = bf(L.dyy_off), *dob = bf(L.do_off), *dg = bf(L.dg_off), *dxn = bf(L.dxn_off);
+  float* part = reinterpret_cast<float*>(ws + L.part_off);
+  float* scratch = reinterpret_cast<float*>(ws + L.scratch_off);
+  const int64_t pl = hstu::ln_bwd_partial_rows(T, kLnBwdRows), pc = hstu::colsum_partial_rows(T, kColSumRows);
+
+  // ---- forward again, keeping Z = LN(X) W_uvqk^T + b beside G = SiLU(Z)
+  hstu::LnArgs ln{};
+  ln.x = x; ln.ldx = D; ln.y = xn; ln.ldy = D;
+  ln.gamma = p->ln_in_gamma; ln.beta = p->ln_in_beta; ln.eps = p->ln_eps; ln.rows = T;
+  if ((e = hstu::launch_ln_rows(ln, static_cast<int>(D), stream)) != hipSuccess) return hip_fail(e, "input LayerNorm");
+  hstu::GemmArgs g1{};
+  g1.a = xn; g1.lda = D; g1.b = p->w_uvqk; g1.ldb = D; g1.c = g; g1.ldc = n1; g1.bias = p->b_uvqk;
+  g1.c2 = z; g1.ldc2 = n1; g1.M = static_cast<int>(T); g1.N = static_cast<int>(n1); g1.K = static_cast<int>(D);
+  if ((e = hstu::launch_gemm(g1, hstu::kEpiSiluPair, false, false, 1, stream)) != hipSuccess)
+    return hip_fail(e, "UVQK projection");
+  if ((e = hstu::launch_build_worklist(jag->seq_offsets, jag->num_seqs, static_cast<int>(H), hstu::kAttnBM, L.attn, ws,
+                                       stream)) != hipSuccess)
+    return hip_fail(e, "work-list launch");
+  const __bf16* gb = static_cast<const __bf16*>(g);
+  const void *uq = gb + 2 * hv, *uk = gb + 2 * hv + H * dqk, *uv = gb + hv;
+  hstu::AttnArgs a = make_args(&p->attn, jag, &p->bias, uq, n1, uk, n1, uv, n1);
+  a.items = ws + L.attn.items_off;
+  a.item_count = reinterpret_cast<const int*>(ws + L.attn.hdr_off);
+  a.capacity = L.attn.capacity;
+  a.tile_base = reinterpret_cast<const int*>(ws + L.attn.tile_base_off);
+  a.meta = ws + L.attn.meta_off;
+  a.meta_blocks = L.attn.meta_blocks;
+  a.o = o;
+  a.ldo = hv;
+  if ((e = hstu::launch_attn_fwd_bf16(a, static_cast<int>(dqk), static_cast<int>(dv), stream)) != hipSuccess)
+    return hip_fail(e, "attention forward launch");
+  hstu::LnArgs lo{};
+  lo.x = o; lo.ldx = hv; lo.gate = g; lo.ldg = n1; lo.y = yy; lo.ldy = hv;
+  lo.gamma = p->ln_out_gamma; lo.beta = p->ln_out_beta; lo.eps = p->ln_eps; lo.rows = T;
+  if ((e = hstu::launch_ln_rows(lo, static_cast<int>(hv), stream)) != hipSuccess)
+    return hip_fail(e, "post-pooling LayerNorm");
+
+  // ---- X' = X + Y W_out^T + b_out: d_b_out, d_W_out = d_out^T Y, dY = d_out W_out
+  hstu::ColGradArgs cs{};
+  cs.dg = const_cast<void*>(d_out); cs.ldg = D; cs.z = nullptr; cs.rows = T; cs.N = static_cast<int>(D);
+  cs.partial = part; cs.rows_per_block = kColSumRows;
+  if ((e = hstu::launch_silu_bwd_colsum(cs, stream)) != hipSuccess) return hip_fail(e, "output-bias gradient");
+  if ((e = hstu::launch_sum_rows(part, pc, D, D, 1.0f, grads->d_b_out, scratch, stream)) != hipSuccess)
+    return hip_fail(e, "output-bias gradient sum");
+  hstu::GemmArgs gw{};
+  gw.a = d_out; gw.lda = D; gw.b = yy; gw.ldb = hv; gw.c = part; gw.ldc = hv; gw.split_stride = D * hv;
+  gw.M = static_cast<int>(D); gw.N = static_cast<int>(hv); gw.K = static_cast<int>(T);
+  if ((e = hstu::launch_gemm(gw, hstu::kEpiF32, true, true, L.splits_out, stream)) != hipSuccess)
+    return hip_fail(e, "output-projection weight gradient");
+  if ((e = hstu::launch_sum_rows(part, L.splits_out, D * hv, D * hv, 1.0f, grads->d_w_out, scratch, stream)) != hipSuccess)
+    return hip_fail(e, "output-projection weight gradient sum");
+  hstu::GemmArgs gd{};
+  gd.a = d_out; gd.lda = D; gd.b = p->w_out; gd.ldb = hv; gd.c = dyy; gd.ldc = hv;
+  gd.M = static_cast<int>(T); gd.N = static_cast<int>(hv); gd.K = static_cast<int>(D);
+  if ((e = hstu::launch_gemm(gd, hstu::kEpiNone, false, true, 1, stream)) != hipSuccess)
+    return hip_fail(e, "gradient through the output projection");
+
+  // ---- Y = LN(O) * u: dO, du (into dG's u columns), d gamma2, d beta2
+  hstu::LnBwdArgs lb{};
+  lb.x = o; lb.ldx = hv; lb.gate = g; lb.ldg = n1; lb.dy = dyy; lb.lddy = hv; lb.dx = dob; lb.lddx = hv;
+  lb.dgate = dg; lb.lddg = n1; lb.gamma = p->ln_out_gamma; lb.beta = p->ln_out_beta; lb.eps = p->ln_eps;
+  lb.rows = T; lb.partial = part; lb.rows_per_block = kLnBwdRows;
+  if ((e = hstu::launch_ln_bwd(lb, static_cast<int>(hv), stream)) != hipSuccess)
+    return hip_fail(e, "post-pooling LayerNorm backward");
+  if ((e = hstu::launch_sum_rows(part, pl, hv, 2 * hv, 1.0f, grads->d_ln_out_gamma, scratch, stream)) != hipSuccess ||
+      (e = hstu::launch_sum_rows(part + hv, pl, hv, 2 * hv, 1.0f, grads->d_ln_out_beta, scratch, stream)) != hipSuccess)
+    return hip_fail(e, "post-pooling LayerNorm parameter gradient sum");
+
+  // ---- attention backward: dv, dq, dk into dG's columns, bias-table gradients
+  hstu::AttnBwdArgs ab{};
+  ab.f = a;
+  ab.d_o = dob; ab.lddo = hv;
+  __bf16* dgb = static_cast<__bf16*>(dg);
+  ab.dv = dgb + hv; ab.lddv = n1;
+  ab.dq = dgb + 2 * hv; ab.lddq = n1;
+  ab.dk = dgb + 2 * hv + H * dqk; ab.lddk = n1;
+  ab.d_pos = grads->d_pos_table;
+  ab.d_time = grads->d_time_table;
+  ab.partial = L.abwd.grad_stride > 0 ? reinterpret_cast<float*>(ws + L.abwd.partial_off) : nullptr;
+  ab.grad_stride = L.abwd.grad_stride;
+  ab.tile_rows = L.abwd.tile_rows;
+  ab.num_seqs = jag->num_seqs;
+  if ((e = hstu::launch_attn_bwd_bf16(ab, static_cast<int>(dqk), static_cast<int>(dv), stream)) != hipSuccess)
+    return hip_fail(e, "attention backward launch");
+
+  // ---- G = SiLU(Z): dZ in place, d_b_uvqk, d_W_uvqk = dZ^T LN(X), d LN(X) = dZ W_uvqk
+  hstu::ColGradArgs sb{};
+  sb.dg = dg; sb.ldg = n1; sb.z = z; sb.ldz = n1; sb.rows = T; sb.N = static_cast<int>(n1);
+  sb.partial = part; sb.rows_per_block = kColSumRows;
+  if ((e = hstu::launch_silu_bwd_colsum(sb, stream)) != hipSuccess) return hip_fail(e, "SiLU backward");
+  if ((e = hstu::launch_sum_rows(part, pc, n1, n1, 1.0f, grads->d_b_uvqk, scratch, stream)) != hipSuccess)
+    return hip_fail(e, "projection-bias gradient sum");
+  hstu::GemmArgs gu{};
+  gu.a = dg; gu.lda = n1; gu.b = xn; gu.ldb = D; gu.c = part; gu.ldc = D; gu.split_stride = n1 * D;
+  gu.M = static_cast<int>(n1); gu.N = static_cast<int>(D); gu.K = static_cast<int>(T);
+  if ((e = hstu::launch_gemm(gu, hstu::kEpiF32, true, true, L.splits_uvqk, stream)) != hipSuccess)
+    return hip_fail(e, "projection weight gradient");
+  if ((e = hstu::launch_sum_rows(part, L.splits_uvqk, n1 * D, n1 * D, 1.0f, grads->d_w_uvqk, scratch, stream)) != hipSuccess)
+    return hip_fail(e, "projection weight gradient sum");
+  hstu::GemmArgs gx{};
+  gx.a = dg; gx.lda = n1; gx.b = p->w_uvqk; gx.ldb = D; gx.c = dxn; gx.ldc = D;
+  gx.M = static_cast<int>(T); gx.N = static_cast<int>(D); gx.K = static_cast<int>(n1);
+  if ((e = hstu::launch_gemm(gx, hstu::kEpiNone, false, true, 1, stream)) != hipSuccess)
+    return hip_fail(e, "gradient through the projection");
+
+  // ---- Xn = LN(X): dX = d_out + LN backward, d gamma1, d beta1
+  hstu::LnBwdArgs li{};
+  li.x = x; li.ldx = D; li.gate = nullptr; li.dy = dxn; li.lddy = D; li.resid = d_out; li.ldr = D;
+  li.dx = dx; li.lddx = D; li.gamma = p->ln_in_gamma; li.beta = p->ln_in_beta; li.eps = p->ln_eps;
+  li.rows = T; li.partial = part; li.rows_per_block = kLnBwdRows;
+  if ((e = hstu::launch_ln_bwd(li, static_cast<int>(D), stream)) != hipSuccess)
+    return hip_fail(e, "input LayerNorm backward");
+  if ((e = hstu::launch_sum_rows(part, pl, D, 2 * D, 1.0f, grads->d_ln_in_gamma, scratch, stream)) != hipSuccess ||
+      (e = hstu::launch_sum_rows(part + D, pl, D, 2 * D, 1.0f, grads->d_ln_in_beta, scratch, stream)) != hipSuccess)
+    return hip_fail(e, "input LayerNorm parameter gradient sum");
   return ok();
 }
 

@@ -19,6 +19,7 @@
 // LayerNorm. One wave per token row; the row lives in registers (8 features
 // per lane per 512), mean and variance by wave butterflies (two passes, fp32),
 // output rounded to bf16.
+#include "attn_common.h"
 #include "common.h"
 #include "layer.h"
 #include "timing.h"
@@ -26,9 +27,6 @@
 namespace hstu {
 
 namespace {
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-constexpr int kRsrcFlags = 0x00020000;
 
 constexpr int GBK = 64;            // K per stage
 constexpr int kChunks = GBK / 8;   // 16-byte chunks per tile row
@@ -46,8 +44,10 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 
 // GEMM tile shape: BM x BN outputs per workgroup, WM x WN per wave
 // ((WM/32) x (WN/32) blocks of v_mfma_f32_32x32x16_bf16), `ST` K stages of 64
-// in LDS.
-template <int BM, int BN, int WM, int WN, int ST>
+// in LDS. AT / BT: the operand is stored K-major ([K][M] / [K][N], i.e. the
+// product uses its transpose); its stage tile is then 64 K-rows of BM (BN)
+// columns, read back with transposed LDS reads.
+template <int BM, int BN, int WM, int WN, int ST, bool AT, bool BT>
 struct GemmShape {
   static constexpr int kWavesM = BM / WM, kWavesN = BN / WN, kWaves = kWavesM * kWavesN;
   static constexpr int kThreads = kWaves * 64;
@@ -57,34 +57,90 @@ struct GemmShape {
   static constexpr int kAPer = kAInst / kWaves, kBPer = kBInst / kWaves;
   static constexpr int kLoadsPerStage = kAPer + kBPer;   // per wave
   static constexpr int kStagesAhead = ST - 1;
+  static constexpr int ACH = AT ? BM / 8 : kChunks;     // 16-byte chunks per LDS row of a stage tile
+  static constexpr int BCH = BT ? BN / 8 : kChunks;
+  static constexpr bool kAT = AT, kBT = BT;
   static_assert(kAInst % kWaves == 0 && kBInst % kWaves == 0, "loads spread evenly over the waves");
   static_assert(ST >= 2 && ST <= 4, "stages");
 };
 
-// One K stage of A and B tiles, direct to LDS. Instruction i fills LDS slots
-// [64 i, 64 i + 64) of its operand: slot s holds chunk (s % 8) ^ (row & 7) of
-// row s / 8 (rows past M / N arrive as zeros).
-template <class S>
-__device__ __forceinline__ void gemm_issue(const char* abase, int64_t lda, uint32_t arecs, const char* bbase,
-                                           int64_t ldb, uint32_t brecs, int k0, int w, int lane,
-                                           char* __restrict__ sa, char* __restrict__ sb) {
-  __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase + k0 * 2), 0,
-                                                                 static_cast<int>(arecs), kRsrcFlags);
-  __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(bbase + k0 * 2), 0,
-                                                                 static_cast<int>(brecs), kRsrcFlags);
+// Swizzle of the 16-byte chunks of one LDS row of a stage tile. Row-major
+// (K-contiguous) tiles: chunk ^ (row & 7), so the ds_read_b128 of 32
+// consecutive rows hits distinct banks. K-major tiles: chunk ^ (4 row mod CH),
+// so the transposed reads of 4 rows x 4 chunks per 16 lanes hit distinct banks.
+template <bool KMAJOR, int CH>
+__device__ __forceinline__ int stage_swizzle(int r) {
+  if constexpr (KMAJOR) return (4 * r) & (CH - 1);
+  else return r & 7;
+}
+
+// Direct loads of one operand's stage tile: instruction i fills LDS slots
+// [64 i, 64 i + 64); slot s holds chunk (s % CH) ^ swizzle(row) of row s / CH.
+template <class S, bool KMAJOR, int CH, int PER>
+__device__ __forceinline__ void issue_operand(__amdgpu_buffer_rsrc_t rs, int64_t ld, int w, int lane,
+                                              char* __restrict__ dst) {
 #pragma unroll
-  for (int j = 0; j < S::kAPer; ++j) {
-    const int i = w + S::kWaves * j, sl = i * 64 + lane, r = sl / kChunks, c = (sl % kChunks) ^ (r & 7);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sa + i * 1024), 16,
-                                             static_cast<uint32_t>(r * lda * 2 + c * 16), 0, 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < S::kBPer; ++j) {
-    const int i = w + S::kWaves * j, sl = i * 64 + lane, r = sl / kChunks, c = (sl % kChunks) ^ (r & 7);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sb + i * 1024), 16,
-                                             static_cast<uint32_t>(r * ldb * 2 + c * 16), 0, 0, 0);
+  for (int j = 0; j < PER; ++j) {
+    const int i = w + S::kWaves * j, sl = i * 64 + lane, r = sl / CH,
+              c = (sl % CH) ^ stage_swizzle<KMAJOR, CH>(r);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + i * 1024), 16,
+                                             static_cast<uint32_t>(r * ld * 2 + c * 16), 0, 0, 0);
   }
 }
+
+// Buffer resource over an operand's stage tile at K offset k0. Row-major: the
+// tile's rows start at `base` (row m0 of the operand), K offset k0; rows past
+// the operand's end read as zeros. K-major: rows k0 .. k_end-1 of the operand,
+// columns from the tile's first one; rows past k_end and columns past the last
+// row's end read as zeros.
+template <bool KMAJOR>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const char* base, int64_t ld, int rows_left,
+                                                               int cols_left, int k0, int k_end, int K) {
+  if constexpr (!KMAJOR) {
+    const int64_t bytes = rows_left > 0 ? static_cast<int64_t>(rows_left - 1) * ld * 2 + (K - k0) * 2 : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + k0 * 2), 0,
+                                             static_cast<int>(clamp_u32(bytes)), kRsrcFlags);
+  } else {
+    const int64_t bytes =
+        (k_end > k0 && cols_left > 0) ? static_cast<int64_t>(k_end - k0 - 1) * ld * 2 + cols_left * 2 : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + static_cast<int64_t>(k0) * ld * 2), 0,
+                                             static_cast<int>(clamp_u32(bytes)), kRsrcFlags);
+  }
+}
+
+// One operand's fragment geometry. Row-major: one ds_read_b128 of the lane's
+// row, chunk 2 k16 + lh (the row's swizzle folded into `o0`). K-major: two
+// transposed reads (K rows 8 lh + i16/4 and + 4 of the 16-row step) of the
+// lane's column; each lane gets the same 8 consecutive K of its column as the
+// row-major read would.
+template <bool KMAJOR, int CH>
+struct Frag {
+  uint32_t o0, o1;
+  __device__ __forceinline__ void init(int col0, int lane) {   // col0: first row (column) of the 32-block
+    const int lr = lane & 31, lh = lane >> 5;
+    if constexpr (!KMAJOR) {
+      const int r = col0 + lr;
+      o0 = static_cast<uint32_t>(r * CH * 16 + (stage_swizzle<false, CH>(r) << 4));
+      o1 = 0;
+    } else {
+      const int g16 = lane >> 4, i16 = lane & 15;
+      const int r1 = 8 * lh + (i16 >> 2);
+      const int c = col0 / 8 + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+      const int half = (i16 & 1) * 8;
+      o0 = static_cast<uint32_t>((r1 * CH + (c ^ stage_swizzle<true, CH>(r1))) * 16 + half);
+      o1 = static_cast<uint32_t>(((r1 + 4) * CH + (c ^ stage_swizzle<true, CH>(r1 + 4))) * 16 + half);
+    }
+  }
+  __device__ __forceinline__ bf16x8_t read(const char* stage, int k16, int lh) const {
+    if constexpr (!KMAJOR) {
+      return *reinterpret_cast<const bf16x8_t*>(stage + (o0 ^ static_cast<uint32_t>((2 * k16 + lh) * 16)));
+    } else {
+      // 16 K rows further keeps the swizzle (it depends on row mod CH / 4 <= 16)
+      const char* p = stage + k16 * 16 * CH * 16;
+      return __builtin_shufflevector(tr_read(p + o0), tr_read(p + o1), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+};
 
 // One K step: MFMAs on stage (rs_a, rs_b) while the stage ST - 1 steps ahead
 // streams into (ds_a, ds_b), then wait for the next stage and synchronize.
@@ -94,22 +150,26 @@ __device__ __forceinline__ void gemm_issue(const char* abase, int64_t lda, uint3
 template <class S>
 __device__ __forceinline__ void gemm_step(const GemmArgs& g, const char* __restrict__ rs_a,
                                           const char* __restrict__ rs_b, char* __restrict__ ds_a,
-                                          char* __restrict__ ds_b, int kt, int nsteps, const char* abase,
-                                          uint32_t arecs, const char* bbase, uint32_t brecs, int w, int lane,
-                                          const uint32_t (&a_lds)[S::MB], const uint32_t (&b_lds)[S::NB],
+                                          char* __restrict__ ds_b, int kt, int nsteps, int kbase_elems, int k_end,
+                                          const char* abase, int arows, const char* bbase, int brows, int w,
+                                          int lane, const Frag<S::kAT, S::ACH> (&af_)[S::MB],
+                                          const Frag<S::kBT, S::BCH> (&bf_)[S::NB],
                                           f32x16_t (&acc)[S::MB][S::NB]) {
-  const bool issue = kt + S::kStagesAhead < nsteps;
-  if (issue) gemm_issue<S>(abase, g.lda, arecs, bbase, g.ldb, brecs, (kt + S::kStagesAhead) * GBK, w, lane, ds_a, ds_b);
+  if (kt + S::kStagesAhead < nsteps) {
+    const int k0 = kbase_elems + (kt + S::kStagesAhead) * GBK;
+    issue_operand<S, S::kAT, S::ACH, S::kAPer>(operand_rsrc<S::kAT>(abase, g.lda, arows, arows, k0, k_end, g.K),
+                                              g.lda, w, lane, ds_a);
+    issue_operand<S, S::kBT, S::BCH, S::kBPer>(operand_rsrc<S::kBT>(bbase, g.ldb, brows, brows, k0, k_end, g.K),
+                                              g.ldb, w, lane, ds_b);
+  }
   const int lh = lane >> 5;
 #pragma unroll
   for (int k16 = 0; k16 < 4; ++k16) {
-    // logical chunk 2 k16 + lh of each row; the row's swizzle is folded into the offsets
-    const uint32_t cx = static_cast<uint32_t>((2 * k16 + lh) * 16);
     bf16x8_t af[S::MB], bfr[S::NB];
 #pragma unroll
-    for (int mb = 0; mb < S::MB; ++mb) af[mb] = *reinterpret_cast<const bf16x8_t*>(rs_a + (a_lds[mb] ^ cx));
+    for (int mb = 0; mb < S::MB; ++mb) af[mb] = af_[mb].read(rs_a, k16, lh);
 #pragma unroll
-    for (int nb = 0; nb < S::NB; ++nb) bfr[nb] = *reinterpret_cast<const bf16x8_t*>(rs_b + (b_lds[nb] ^ cx));
+    for (int nb = 0; nb < S::NB; ++nb) bfr[nb] = bf_[nb].read(rs_b, k16, lh);
 #pragma unroll
     for (int mb = 0; mb < S::MB; ++mb)
 #pragma unroll
@@ -132,9 +192,9 @@ __device__ __forceinline__ void gemm_step(const GemmArgs& g, const char* __restr
   asm volatile("" ::: "memory");
 }
 
-template <int EPI, int BM, int BN, int WM, int WN, int ST>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_nt_kernel(GemmArgs g) {
-  using S = GemmShape<BM, BN, WM, WN, ST>;
+template <int EPI, int BM, int BN, int WM, int WN, int ST, bool AT, bool BT>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_kernel(GemmArgs g) {
+  using S = GemmShape<BM, BN, WM, WN, ST, AT, BT>;
   __shared__ __attribute__((aligned(16))) char sa[ST][BM * GBK * 2];
   __shared__ __attribute__((aligned(16))) char sb[ST][BN * GBK * 2];
 
@@ -151,11 +211,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_nt_kernel(
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
   const int wm = w / S::kWavesN, wn = w % S::kWavesN;
 
-  const char* abase = static_cast<const char*>(g.a) + static_cast<int64_t>(m0) * g.lda * 2;
-  const char* bbase = static_cast<const char*>(g.b) + static_cast<int64_t>(n0) * g.ldb * 2;
-  // rows past M (N) are out of range: records end right after the last valid row's K range
-  const uint32_t arecs = g.M > m0 ? clamp_u32(static_cast<int64_t>(g.M - m0 - 1) * g.lda * 2 + g.K * 2) : 0u;
-  const uint32_t brecs = g.N > n0 ? clamp_u32(static_cast<int64_t>(g.N - n0 - 1) * g.ldb * 2 + g.K * 2) : 0u;
+  // K range of this split (blockIdx.y of gridDim.y); only K-major operands split K
+  const int ksteps_all = (g.K + GBK - 1) / GBK;
+  const int per = (ksteps_all + gridDim.y - 1) / gridDim.y;
+  const int ks0 = blockIdx.y * per;
+  const int nsteps = max(0, min(per, ksteps_all - ks0));
+  const int kbase_elems = ks0 * GBK, k_end = min(g.K, (ks0 + nsteps) * GBK);
+
+  // operand bases: row-major -> first row of the tile; K-major -> first column of the tile
+  const char* abase = static_cast<const char*>(g.a) + (AT ? static_cast<int64_t>(m0) * 2 : static_cast<int64_t>(m0) * g.lda * 2);
+  const char* bbase = static_cast<const char*>(g.b) + (BT ? static_cast<int64_t>(n0) * 2 : static_cast<int64_t>(n0) * g.ldb * 2);
+  const int arows = g.M - m0, brows = g.N - n0;   // rows (row-major) or columns (K-major) left
 
   f32x16_t acc[S::MB][S::NB];
 #pragma unroll
@@ -163,25 +229,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_nt_kernel(
 #pragma unroll
     for (int nb = 0; nb < S::NB; ++nb) acc[mb][nb] = f32x16_t{};
 
-  // byte offset of this lane's row in a stage, with the row's chunk swizzle
-  // (r & 7) << 4 folded in: fragment offset = row offset ^ (chunk << 4)
-  uint32_t a_lds[S::MB], b_lds[S::NB];
+  Frag<AT, S::ACH> af_[S::MB];
+  Frag<BT, S::BCH> bf_[S::NB];
 #pragma unroll
-  for (int mb = 0; mb < S::MB; ++mb) {
-    const int r = wm * WM + mb * 32 + lr;
-    a_lds[mb] = static_cast<uint32_t>(r * kChunks * 16 + ((r & 7) << 4));
-  }
+  for (int mb = 0; mb < S::MB; ++mb) af_[mb].init(wm * WM + mb * 32, lane);
 #pragma unroll
-  for (int nb = 0; nb < S::NB; ++nb) {
-    const int r = wn * WN + nb * 32 + lr;
-    b_lds[nb] = static_cast<uint32_t>(r * kChunks * 16 + ((r & 7) << 4));
-  }
+  for (int nb = 0; nb < S::NB; ++nb) bf_[nb].init(wn * WN + nb * 32, lane);
 
-  const int nsteps = g.K / GBK;
   // stages 0 .. ST-2 in flight, wait for stage 0
 #pragma unroll
   for (int s_ = 0; s_ < ST - 1; ++s_)
-    if (s_ < nsteps) gemm_issue<S>(abase, g.lda, arecs, bbase, g.ldb, brecs, s_ * GBK, w, lane, sa[s_], sb[s_]);
+    if (s_ < nsteps) {
+      const int k0 = kbase_elems + s_ * GBK;
+      issue_operand<S, AT, S::ACH, S::kAPer>(operand_rsrc<AT>(abase, g.lda, arows, arows, k0, k_end, g.K), g.lda, w,
+                                            lane, sa[s_]);
+      issue_operand<S, BT, S::BCH, S::kBPer>(operand_rsrc<BT>(bbase, g.ldb, brows, brows, k0, k_end, g.K), g.ldb, w,
+                                            lane, sb[s_]);
+    }
   wait_vm_lgkm0<0>();
   __syncthreads();
   // stages rotate statically; step t reads stage t % ST and fills (t + ST - 1) % ST
@@ -189,8 +253,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_nt_kernel(
 #pragma unroll
     for (int u = 0; u < ST; ++u) {
       if (kt + u >= nsteps) break;
-      gemm_step<S>(g, sa[u], sb[u], sa[(u + ST - 1) % ST], sb[(u + ST - 1) % ST], kt + u, nsteps, abase, arecs,
-                   bbase, brecs, w, lane, a_lds, b_lds, acc);
+      gemm_step<S>(g, sa[u], sb[u], sa[(u + ST - 1) % ST], sb[(u + ST - 1) % ST], kt + u, nsteps, kbase_elems,
+                   k_end, abase, arows, bbase, brows, w, lane, af_, bf_, acc);
     }
   }
 
@@ -198,9 +262,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_nt_kernel(
   // C[m][n + i] for m = 32 mb + lr, n = 32 nb + 8 jq + 4 lh (wave-tile
   // coordinates). Each 32-row slice (one mb) goes through a wave-private fp32
   // staging area of 32 rows x WN columns in the (now idle) A stage buffers,
-  // 16-byte chunks XOR-swizzled by row, and leaves as row-contiguous 16-byte
-  // stores of 8 bf16: one instruction covers 8 rows x 128 bytes. Bias and SiLU
-  // apply before staging, the residual after it; bf16 rounding happens once.
+  // 16-byte chunks XOR-swizzled by row, and leaves as row-contiguous stores
+  // of 8 values per lane (one instruction covers 8 rows). Bias and SiLU apply
+  // before staging, the residual after it; bf16 rounding happens once.
   constexpr int kRowChunks = WN / 4;             // 16-byte fp32 chunks per staged row
   static_assert(kRowChunks == 16, "staging swizzle assumes 64-column wave tiles");
   static_assert(S::kWaves * 32 * WN * 4 <= sizeof(sa), "staging fits in the A stage buffers");
@@ -212,7 +276,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_nt_kernel(
     for (int jq = 0; jq < 4; ++jq) {
       const int n = n0 + wn * WN + nb * 32 + 8 * jq + 4 * lh;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bias[nb][jq][i] = (g.bias && n + i < g.N) ? g.bias[n + i] : 0.f;
+      for (int i = 0; i < 4; ++i) bias[nb][jq][i] = (EPI != kEpiF32 && g.bias && n + i < g.N) ? g.bias[n + i] : 0.f;
     }
   char* cp = static_cast<char*>(g.c);
   const char* rp = static_cast<const char*>(g.r);
@@ -240,6 +304,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_nt_kernel(
       const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stage + row * (WN * 4) + (((2 * rc + 1) ^ (row & 15)) << 4));
       const int m = m0 + wm * WM + mb * 32 + row, n = n0 + wn * WN + 8 * rc;
       if (m >= g.M || n >= g.N) continue;
+      if constexpr (EPI == kEpiF32) {
+        float* op = reinterpret_cast<float*>(cp) + static_cast<int64_t>(blockIdx.y) * g.split_stride +
+                    static_cast<int64_t>(m) * g.ldc + n;
+        *reinterpret_cast<f32x4_t*>(op) = lo;
+        *reinterpret_cast<f32x4_t*>(op + 4) = hi;
+        continue;
+      }
       float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       if (EPI == kEpiResidual) {
         const bf16x8_t rv = *reinterpret_cast<const bf16x8_t*>(rp + (static_cast<int64_t>(m) * g.ldr + n) * 2);
@@ -247,8 +318,18 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_nt_kernel(
         for (int i = 0; i < 8; ++i) x[i] += static_cast<float>(rv[i]);
       }
       bf16x8_t out;
+      if (EPI == kEpiSiluPair) {
+        bf16x8_t pre;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) out[i] = static_cast<__bf16>(x[i]);
+        for (int i = 0; i < 8; ++i) {
+          pre[i] = static_cast<__bf16>(x[i]);
+          out[i] = static_cast<__bf16>(silu_f32(x[i]));
+        }
+        *reinterpret_cast<bf16x8_t*>(static_cast<char*>(g.c2) + (static_cast<int64_t>(m) * g.ldc2 + n) * 2) = pre;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = static_cast<__bf16>(x[i]);
+      }
       *reinterpret_cast<bf16x8_t*>(cp + (static_cast<int64_t>(m) * g.ldc + n) * 2) = out;
     }
   }
@@ -306,32 +387,53 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(LnArgs a) {
 }  // namespace
 
 namespace {
-template <int EPI, int BM, int BN, int WM, int WN, int ST>
-hipError_t launch_gemm_shape(const GemmArgs& g, hipStream_t stream) {
+template <int EPI, int BM, int BN, int WM, int WN, int ST, bool AT, bool BT>
+hipError_t launch_gemm_shape(const GemmArgs& g, int splits, hipStream_t stream) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_nt_kernel<EPI, BM, BN, WM, WN, ST>), dim3(tiles), dim3((BM / WM) * (BN / WN) * 64), 0,
-                     stream, g);
+  hipLaunchKernelGGL((gemm_kernel<EPI, BM, BN, WM, WN, ST, AT, BT>), dim3(tiles, splits),
+                     dim3((BM / WM) * (BN / WN) * 64), 0, stream, g);
   return hipGetLastError();
 }
-template <int EPI>
-hipError_t launch_gemm_epi(const GemmArgs& g, hipStream_t stream) {
+template <int EPI, bool AT, bool BT>
+hipError_t launch_gemm_epi(const GemmArgs& g, int splits, hipStream_t stream) {
   // wide outputs: 256 x 256 tiles, 8 waves of 128 x 64; narrow ones: 128 x 128, 4 waves of 64 x 64
-  if (g.N >= 1024) return launch_gemm_shape<EPI, 256, 256, 128, 64, 2>(g, stream);
-  return launch_gemm_shape<EPI, 128, 128, 64, 64, 2>(g, stream);
+  if (g.N >= 1024) return launch_gemm_shape<EPI, 256, 256, 128, 64, 2, AT, BT>(g, splits, stream);
+  return launch_gemm_shape<EPI, 128, 128, 64, 64, 2, AT, BT>(g, splits, stream);
 }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 }  // namespace
 
-hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream) {
+hipError_t launch_gemm(const GemmArgs& g, int epi, bool a_kmajor, bool b_kmajor, int splits, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  // a row-major operand steps through K in whole stages; K-major ones take any K
+  if ((!a_kmajor || !b_kmajor) && g.K % GBK != 0) return hipErrorInvalidValue;
+  if (splits < 1 || (splits > 1 && epi != kEpiF32) || g.K <= 0) return hipErrorInvalidValue;
   // 16-byte epilogue accesses: eight-column groups, 16-byte aligned rows
-  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  if (g.K % GBK != 0 || g.N % 8 != 0 || g.ldc % 8 != 0 || !a16(g.c) ||
-      (epi == kEpiResidual && (g.ldr % 8 != 0 || !a16(g.r))))
+  if (g.N % 8 != 0 || !aligned(g.c, 16)) return hipErrorInvalidValue;
+  if (epi == kEpiF32) {
+    if (g.ldc % 4 != 0 || (splits > 1 && g.split_stride % 4 != 0)) return hipErrorInvalidValue;
+  } else if (g.ldc % 8 != 0) {
     return hipErrorInvalidValue;
+  }
+  if (epi == kEpiResidual && (g.ldr % 8 != 0 || !aligned(g.r, 16))) return hipErrorInvalidValue;
+  if (epi == kEpiSiluPair && (g.ldc2 % 8 != 0 || !aligned(g.c2, 16))) return hipErrorInvalidValue;
   TimedScope timed(epi == kEpiResidual ? kTimedGemmOut : kTimedGemmUvqk, stream);
-  if (epi == kEpiSilu) return launch_gemm_epi<kEpiSilu>(g, stream);
-  if (epi == kEpiResidual) return launch_gemm_epi<kEpiResidual>(g, stream);
-  return launch_gemm_epi<kEpiNone>(g, stream);
+  if (!a_kmajor && !b_kmajor) {
+    switch (epi) {
+      case kEpiSilu: return launch_gemm_epi<kEpiSilu, false, false>(g, splits, stream);
+      case kEpiResidual: return launch_gemm_epi<kEpiResidual, false, false>(g, splits, stream);
+      case kEpiNone: return launch_gemm_epi<kEpiNone, false, false>(g, splits, stream);
+      case kEpiSiluPair: return launch_gemm_epi<kEpiSiluPair, false, false>(g, splits, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (!a_kmajor && b_kmajor && epi == kEpiNone) return launch_gemm_epi<kEpiNone, false, true>(g, splits, stream);
+  if (a_kmajor && b_kmajor && epi == kEpiF32) return launch_gemm_epi<kEpiF32, true, true>(g, splits, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream) {
+  return launch_gemm(g, epi, false, false, 1, stream);
 }
 
 hipError_t launch_ln_rows(const LnArgs& a, int width, hipStream_t stream) {

@@ -200,6 +200,55 @@ def layer_fwd(x: torch.Tensor, seq_offsets: torch.Tensor, params: "_lib.LayerPar
     return out
 
 
+LAYER_GRAD_NAMES = ("d_ln_in_gamma", "d_ln_in_beta", "d_w_uvqk", "d_b_uvqk", "d_ln_out_gamma",
+                    "d_ln_out_beta", "d_w_out", "d_b_out", "d_pos_table", "d_time_table")
+
+
+def layer_bwd(x: torch.Tensor, d_out: torch.Tensor, seq_offsets: torch.Tensor,
+              params: "_lib.LayerParams", *, timestamps: Optional[torch.Tensor] = None,
+              dx: Optional[torch.Tensor] = None, grads: Optional[dict] = None,
+              workspace: Optional[torch.Tensor] = None):
+    """hstu_layer_bwd: gradients of sum(X' * d_out) for the layer with these
+    parameters at input x (bf16 [T, D]). Returns (dx, dict of fp32 parameter
+    gradients keyed as LAYER_GRAD_NAMES; the table entries are present when the
+    layer has that table). `grads` may supply the output tensors."""
+    lib = _lib.load()
+    for name, t in (("x", x), ("d_out", d_out)):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 [T, D] tensor")
+    if d_out.shape != x.shape:
+        raise ValueError("d_out must have the shape of x")
+    T, D = x.shape
+    H, dqk, dv = params.attn.num_heads, params.attn.dqk, params.attn.dv
+    n1, hv = H * (2 * dv + 2 * dqk), H * dv
+    if dx is None:
+        dx = torch.empty_like(x)
+    shapes = {"d_ln_in_gamma": (D,), "d_ln_in_beta": (D,), "d_w_uvqk": (n1, D), "d_b_uvqk": (n1,),
+              "d_ln_out_gamma": (hv,), "d_ln_out_beta": (hv,), "d_w_out": (D, hv), "d_b_out": (D,)}
+    if params.bias.pos_table:
+        shapes["d_pos_table"] = (H, params.bias.pos_buckets)
+    if params.bias.time_table:
+        shapes["d_time_table"] = (H, params.bias.time_buckets)
+    grads = dict(grads or {})
+    for name, shp in shapes.items():
+        if name not in grads:
+            grads[name] = torch.empty(shp, dtype=torch.float32, device=x.device)
+    g = _lib.LayerGrads()
+    for name in LAYER_GRAD_NAMES:
+        t = grads.get(name) if name in shapes else None
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shapes[name]):
+            raise ValueError(f"{name} must be a contiguous fp32 tensor of shape {shapes[name]}")
+        setattr(g, name, None if t is None else t.data_ptr())
+    j = _jagged(seq_offsets, T, timestamps)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.hstu_layer_bwd_workspace_size(ctypes.byref(params), ctypes.byref(j), ctypes.byref(need)))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=x.device)
+    _lib.check(lib.hstu_layer_bwd(ctypes.byref(params), ctypes.byref(j), _ptr(x), _ptr(d_out), _ptr(dx),
+                                  ctypes.byref(g), _ptr(workspace), workspace.numel(), _stream_handle(x.device)))
+    return dx, {k: grads[k] for k in shapes}
+
+
 def timing_enable(enable: bool = True) -> None:
     """hstu_timing_enable: bracket every timed kernel launch with HIP events."""
     _lib.check(_lib.load().hstu_timing_enable(int(bool(enable))))

@@ -187,6 +187,46 @@ hstu_status_t hstu_layer_fwd(const hstu_layer_params_t* params, const hstu_jagge
                              const void* x, void* y, void* uvqk_out, void* o_out,
                              void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Parameter gradients of one layer (device fp32, row-major, overwritten -- not
+ * accumulated). Shapes follow hstu_layer_params_t; d_pos_table [H, Bp] and
+ * d_time_table [H, Bt] must be non-NULL exactly when the layer has that table. */
+typedef struct {
+  float* d_ln_in_gamma;       /* [D] */
+  float* d_ln_in_beta;        /* [D] */
+  float* d_w_uvqk;            /* [H(2dv+2dqk), D] */
+  float* d_b_uvqk;            /* [H(2dv+2dqk)] (written also when b_uvqk is NULL) */
+  float* d_ln_out_gamma;      /* [H dv] */
+  float* d_ln_out_beta;       /* [H dv] */
+  float* d_w_out;             /* [D, H dv] */
+  float* d_b_out;             /* [D] (written also when b_out is NULL) */
+  float* d_pos_table;         /* [H, Bp] or NULL */
+  float* d_time_table;        /* [H, Bt] or NULL */
+} hstu_layer_grads_t;
+
+/* ---------------------------------------------------------------------------
+ * hstu_layer_bwd_workspace_size -- device workspace bytes for hstu_layer_bwd.
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_layer_bwd_workspace_size(const hstu_layer_params_t* params,
+                                            const hstu_jagged_t* jag, size_t* bytes);
+
+/* ---------------------------------------------------------------------------
+ * hstu_layer_bwd -- gradients of sum(X' * d_out) for hstu_layer_fwd with the
+ * same parameters and input: the chain rule through the layer's steps in
+ * reverse (daiwk reproduction notes, flowchart and core formula; the pages
+ * train every position generatively). The forward is recomputed from x
+ * inside the call (nothing is kept between calls).
+ *   x [T,D] bf16: the layer input. d_out [T,D] bf16: gradient of the output X'.
+ *   dx [T,D] bf16: overwritten with the input gradient; must not alias x or d_out.
+ *   grads: fp32 parameter gradients (hstu_layer_grads_t), 16-byte aligned.
+ *   workspace: at least hstu_layer_bwd_workspace_size bytes.
+ * Built for bf16 with at most 1024 position buckets (as hstu_attn_bwd).
+ * Results are deterministic run to run. Errors: as hstu_layer_fwd.
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_layer_bwd(const hstu_layer_params_t* params, const hstu_jagged_t* jag,
+                             const void* x, const void* d_out, void* dx,
+                             const hstu_layer_grads_t* grads,
+                             void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* ---------------------------------------------------------------------------
  * Kernel timing for measurement tools. While enabled (process-wide), every
  * launch of a timed kernel is bracketed by two HIP events recorded on the

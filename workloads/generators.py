@@ -236,11 +236,12 @@ def _layer_params(rng, D, H, dqk, dv, Bp, Bt, time):
 
 
 def _layer_recipe(name, seed, *, lengths=None, draw_lengths=None, num_layers=1, D=512,
-                  H=4, d=128, Bp=128, Bt=128, time=False, note=""):
+                  H=4, d=128, Bp=128, Bt=128, time=False, backward=False, note=""):
     """Layer / stack inputs.
 
     Draw order: [lengths], token ids U[0, VOCAB), [timestamps], then per layer
-    W_uvqk, W_out, position table, [time table]. X = embedding rows of the ids.
+    W_uvqk, W_out, position table, [time table], then [dOut ~ N(0, 1) [T, D]
+    for a backward]. X = embedding rows of the ids.
     """
     rng = np.random.default_rng(seed)
     if draw_lengths is not None:
@@ -252,11 +253,12 @@ def _layer_recipe(name, seed, *, lengths=None, draw_lengths=None, num_layers=1, 
     ids = rng.integers(0, VOCAB, size=T)
     ts = exponential_timestamps(rng, lengths) if time else None
     layers = [_layer_params(rng, D, H, d, d, Bp, Bt, time) for _ in range(num_layers)]
+    d_out = round_to_bf16(normal(rng, (T, D), 1.0)) if backward else None
     x = round_to_bf16(embedding_rows(ids, D))
     return Workload(
-        name=name, kind="stack" if num_layers > 1 else "layer", dtype="bf16",
-        num_heads=H, dqk=d, dv=d, seq_offsets=off, timestamps=ts, x=x, embed_dim=D,
-        layers=layers, note=note)
+        name=name, kind="layer_bwd" if backward else ("stack" if num_layers > 1 else "layer"),
+        dtype="bf16", num_heads=H, dqk=d, dv=d, seq_offsets=off, timestamps=ts, x=x, embed_dim=D,
+        layers=layers, d_o=d_out, note=note)
 
 
 def _c0(seed=0):
@@ -302,6 +304,15 @@ WORKLOADS = {
     "c4_small": lambda seed=14: _attn_recipe(
         "c4_small", seed, None, 2, 128, draw_lengths=(1, 400, 6), backward=True,
         note="attention fwd+bwd, 6 ragged sequences"),
+    # --- one layer forward + backward (a training step's layer): the jagged
+    #     fwd+bwd workload's length recipe with the jagged layer's shape ---
+    "c5": lambda seed=5: _layer_recipe(
+        "c5", seed, draw_lengths=(64, 2048, 32), num_layers=1, time=True, backward=True,
+        note="one layer forward + backward, 32 sequences log-uniform in [64, 2048], D 512, H 4, "
+             "d 128, pos + time bias"),
+    "c5_small": lambda seed=15: _layer_recipe(
+        "c5_small", seed, draw_lengths=(1, 500, 7), num_layers=1, time=True, backward=True,
+        note="one layer forward + backward, 7 ragged sequences"),
 }
 
 
