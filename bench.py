@@ -252,6 +252,61 @@ def secondary_fwd_bwd(hstu, name: str, steps: int, warmup: int, dev):
     }
 
 
+def secondary_layer_fwd_bwd(hstu, name: str, steps: int, warmup: int, dev):
+    """One layer forward + backward (a training step's layer) of a layer
+    workload with an upstream gradient. Credited flops: the forward's and,
+    for the backward, the attention backward plus two GEMMs per forward GEMM
+    (the backward's recompute of the forward is not credited)."""
+    import torch
+    from workloads import make_workload
+    wl = make_workload(name)
+    p = wl.layers[0]
+    dvt = {}
+    for k in ("w_uvqk", "w_out"):
+        dvt[k] = torch.from_numpy(p[k]).to(dev).to(torch.bfloat16)
+    for k in ("b_uvqk", "b_out", "ln_in_gamma", "ln_in_beta", "ln_out_gamma", "ln_out_beta",
+              "pos_table", "time_table"):
+        dvt[k] = None if p.get(k) is None else torch.from_numpy(p[k]).to(dev).to(torch.float32)
+    params = hstu.make_layer_params(wl.embed_dim, wl.num_heads, wl.dqk, wl.dv, ln_eps=wl.ln_eps, **dvt)
+    x = torch.from_numpy(wl.x).to(dev).to(torch.bfloat16)
+    d_out = torch.from_numpy(wl.d_o).to(dev).to(torch.bfloat16)
+    off = torch.from_numpy(wl.seq_offsets).to(dev)
+    ts = torch.from_numpy(wl.timestamps).to(dev) if wl.timestamps is not None else None
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    ws = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # >= either workspace size
+    dx_, grads = hstu.layer_bwd(x, d_out, off, params, timestamps=ts, dx=dx, workspace=ws)
+
+    def fwd():
+        hstu.layer_fwd(x, off, params, timestamps=ts, out=y, workspace=ws)
+
+    def bwd():
+        hstu.layer_bwd(x, d_out, off, params, timestamps=ts, dx=dx, grads=grads, workspace=ws)
+
+    def step():
+        fwd()
+        bwd()
+
+    stream = torch.cuda.current_stream(dev)
+    ms_f = max(time_steps(fwd, steps, warmup, stream))
+    ms_b = max(time_steps(bwd, steps, warmup, stream))
+    ms = max(time_steps(step, steps, warmup, stream))
+    kern = kernel_ms(hstu, bwd, steps, ["attn_fwd", "attn_bwd_kv", "attn_bwd_q", "layer_gemm_uvqk",
+                                        "layer_gemm_out", "layer_norm"])
+    F_f = wl.attn_fwd_flops() + wl.layer_gemm_flops()
+    F_b = wl.attn_bwd_flops() + 2.0 * wl.layer_gemm_flops()
+    return {
+        "workload": f"{name}: {wl.note}",
+        "tokens_per_s": round(wl.total_tokens / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 5),
+        "fwd_ms": round(ms_f, 5),
+        "bwd_ms": round(ms_b, 5),
+        "credited_tflops": round((F_f + F_b) / (ms * 1e-3) / 1e12, 2),
+        "total_tokens": wl.total_tokens,
+        "bwd_kernel_ms": {k: (None if v is None else round(v, 5)) for k, v in kern.items()},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,6 +395,8 @@ def main():
             "layer_stack": secondary_layers(hstu, "c1", args.steps, args.warmup, dev),
             "layer_jagged": secondary_layers(hstu, "c2", max(5, args.steps // 5), max(2, args.warmup // 10), dev),
             "attn_fwd_bwd": secondary_fwd_bwd(hstu, "c4", args.steps, args.warmup, dev),
+            "layer_fwd_bwd": secondary_layer_fwd_bwd(hstu, "c5", max(5, args.steps // 5),
+                                                     max(2, args.warmup // 10), dev),
         }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
