@@ -330,8 +330,8 @@ hstu_status_t check_layer(const hstu_layer_params_t* p, const hstu_jagged_t* j) 
 // Backward of one layer: rows per block of the LayerNorm-backward and
 // column-sum kernels (their partial rows are summed in a fixed order), and the
 // K splits of the two weight-gradient GEMMs (K = tokens).
-constexpr int kLnBwdRows = 64;
-constexpr int kColSumRows = 64;
+constexpr int kLnBwdRows = 16;
+constexpr int kColSumRows = 16;
 
 int weight_grad_splits(int64_t M, int64_t N, int64_t T) {
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);

@@ -144,15 +144,19 @@ __device__ __forceinline__ float silu_grad(float z) {
   return sg * fmaf(z, 1.0f - sg, 1.0f);
 }
 
-// Thread t of block (x, y) owns columns 8 (256 y + t) .. + 7 of rows
-// [x rpb, (x + 1) rpb); it writes their sums to partial row x.
+// A block covers `rows_per_block` rows. Thread t owns 8 columns: column group
+// (t % CT) + CT y with CT = min(256, N / 8) column threads, and row lane t / CT
+// of 256 / CT lanes that take every (256 / CT)-th row, four rows in flight.
+// The row lanes are summed in LDS in a fixed order: one partial row per block.
 __global__ __launch_bounds__(256) void silu_bwd_colsum_kernel(ColGradArgs a) {
-  const int col = (blockIdx.y * 256 + threadIdx.x) * 8;
-  if (col >= a.N) return;
+  const int ct = min(256, a.N / 8), lanes = 256 / ct;
+  const int cg = threadIdx.x % ct, rl = threadIdx.x / ct;
+  const int col = (blockIdx.y * ct + cg) * 8;
+  const bool live = col < a.N && rl < lanes;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * a.rows_per_block;
   const int64_t r1 = min(a.rows, r0 + a.rows_per_block);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int64_t row = r0; row < r1; ++row) {
+  auto one_row = [&](int64_t row) {
     __bf16* gp = static_cast<__bf16*>(a.dg) + row * a.ldg + col;
     float g[8];
     load8(gp, g);
@@ -170,21 +174,47 @@ __global__ __launch_bounds__(256) void silu_bwd_colsum_kernel(ColGradArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += g[i];
+  };
+  if (live) {
+    int64_t row = r0 + rl;
+    for (; row + 3 * lanes < r1; row += 4 * lanes) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) one_row(row + u * lanes);
+    }
+    for (; row < r1; row += lanes) one_row(row);
   }
-  float* pr = a.partial + static_cast<int64_t>(blockIdx.x) * a.N + col;
-  *reinterpret_cast<f32x4_t*>(pr) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
-  *reinterpret_cast<f32x4_t*>(pr + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+  __shared__ f32x4_t red[256][2];
+  red[threadIdx.x][0] = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+  red[threadIdx.x][1] = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+  __syncthreads();
+  if (rl == 0 && col < a.N) {
+    f32x4_t lo = red[cg][0], hi = red[cg][1];
+    for (int l = 1; l < lanes; ++l) {
+      lo += red[l * ct + cg][0];
+      hi += red[l * ct + cg][1];
+    }
+    float* pr = a.partial + static_cast<int64_t>(blockIdx.x) * a.N + col;
+    *reinterpret_cast<f32x4_t*>(pr) = lo;
+    *reinterpret_cast<f32x4_t*>(pr + 4) = hi;
+  }
 }
 
-// out[g * W + c] = scale * sum of in[p * ld + c] for p in [g G, min(P, (g + 1) G)).
+// One level of the partial-row sums: block (x, y) takes columns
+// [64 x, 64 x + 64) of rows [G y, G y + G); its 4 row slices take every
+// fourth row, then combine in LDS in a fixed order:
+// out[y * W + c] = scale * sum of in[p * ld + c] over the block's rows.
 __global__ __launch_bounds__(256) void sum_rows_kernel(const float* __restrict__ in, int64_t P, int64_t W,
                                                        int64_t ld, int G, float scale, float* __restrict__ out) {
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (c >= W) return;
+  const int cl = threadIdx.x & 63, sl = threadIdx.x >> 6;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cl;
   const int64_t p0 = static_cast<int64_t>(blockIdx.y) * G, p1 = min(P, p0 + G);
   float s = 0.f;
-  for (int64_t p = p0; p < p1; ++p) s += in[p * ld + c];
-  out[static_cast<int64_t>(blockIdx.y) * W + c] = s * scale;
+  if (c < W)
+    for (int64_t p = p0 + sl; p < p1; p += 4) s += in[p * ld + c];
+  __shared__ float red[4][64];
+  red[sl][cl] = s;
+  __syncthreads();
+  if (sl == 0 && c < W) out[static_cast<int64_t>(blockIdx.y) * W + c] = (((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl]) * scale;
 }
 
 constexpr int kSumGroup = 64;
@@ -228,25 +258,35 @@ hipError_t launch_silu_bwd_colsum(const ColGradArgs& a, hipStream_t stream) {
 }
 
 int64_t sum_rows_scratch_floats(int64_t P, int64_t W) {
-  return P > kSumGroup ? ((P + kSumGroup - 1) / kSumGroup) * W : 0;
+  // levels of 64 rows each, ping-ponging between two halves
+  int64_t need = 0;
+  for (int64_t p = P; p > kSumGroup; p = (p + kSumGroup - 1) / kSumGroup) need = max(need, (p + kSumGroup - 1) / kSumGroup);
+  return 2 * need * W;
 }
 
 hipError_t launch_sum_rows(const float* in, int64_t P, int64_t W, int64_t ld, float scale, float* out, float* scratch,
                            hipStream_t stream) {
   if (W <= 0) return hipSuccess;
-  const unsigned cols = static_cast<unsigned>((W + 255) / 256);
-  if (P <= kSumGroup) {
-    hipLaunchKernelGGL(sum_rows_kernel, dim3(cols, 1), dim3(256), 0, stream, in, P, W, ld, kSumGroup, scale, out);
-    return hipGetLastError();
+  const unsigned cols = static_cast<unsigned>((W + 63) / 64);
+  const int64_t half = sum_rows_scratch_floats(P, W) / 2;
+  const float* src = in;
+  int64_t rows = P, src_ld = ld;
+  int flip = 0;
+  // levels: 64 rows into one, until at most 64 rows are left
+  while (rows > kSumGroup) {
+    const int64_t groups = (rows + kSumGroup - 1) / kSumGroup;
+    float* dst = scratch + flip * half;
+    hipLaunchKernelGGL(sum_rows_kernel, dim3(cols, static_cast<unsigned>(groups)), dim3(256), 0, stream, src, rows, W,
+                       src_ld, kSumGroup, 1.0f, dst);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    src = dst;
+    rows = groups;
+    src_ld = W;
+    flip ^= 1;
   }
-  // level 1: groups of 64 partial rows into scratch rows; level 2: the groups
-  const int64_t groups = (P + kSumGroup - 1) / kSumGroup;
-  hipLaunchKernelGGL(sum_rows_kernel, dim3(cols, static_cast<unsigned>(groups)), dim3(256), 0, stream, in, P, W, ld,
-                     kSumGroup, 1.0f, scratch);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sum_rows_kernel, dim3(cols, 1), dim3(256), 0, stream, scratch, groups, W, W,
-                     static_cast<int>(groups), scale, out);
+  hipLaunchKernelGGL(sum_rows_kernel, dim3(cols, 1), dim3(256), 0, stream, src, rows, W, src_ld,
+                     static_cast<int>(kSumGroup), scale, out);
   return hipGetLastError();
 }
 
