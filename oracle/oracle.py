@@ -263,6 +263,42 @@ def attn_bwd(q, k, v, d_o, seq_offsets, *, alpha: float = 1.0, divisor: float = 
     return dq, dk, dv, dP, dTt
 
 
+def attn_fwd_candidates(q_c, k_c, v_c, cand_offsets, k_hist, v_hist, q_hist, seq_offsets, *,
+                        alpha: float = 1.0, divisor: float = 0.0, pos_table=None,
+                        time_table=None, timestamps=None, cand_timestamps=None):
+    """Candidate scoring against a history with cached keys and values, float64
+    (M-FALCON, "micro-batched candidate scoring with KV reuse": briansu.co
+    explainer, section 6 "Why it works"). The pages give no formula; the
+    reading used here: candidate c of sequence b, with an n-token history,
+    is scored exactly as if it alone were appended at position n, i.e. its
+    output is the last row of ``attn_fwd`` applied to (history ++ [c]) -- it
+    attends to every history token and to itself, never to another candidate,
+    and is divided by n + 1 (or by the fixed divisor).
+
+    History tensors are [T_h, H, d] with ``seq_offsets``; candidates are
+    [T_c, H, d] with ``cand_offsets`` (same number of sequences). ``q_hist``
+    only fills the history rows of the per-candidate sequences (their outputs
+    are discarded). Returns O for the candidates, [T_c, H, dv].
+    """
+    q_c, k_c, v_c = _f64(q_c), _f64(k_c), _f64(v_c)
+    k_hist, v_hist, q_hist = _f64(k_hist), _f64(v_hist), _f64(q_hist)
+    hoff = np.asarray(seq_offsets, dtype=np.int64)
+    coff = np.asarray(cand_offsets, dtype=np.int64)
+    ts = None if timestamps is None else np.asarray(timestamps, dtype=np.int64)
+    cts = None if cand_timestamps is None else np.asarray(cand_timestamps, dtype=np.int64)
+    out = np.zeros_like(v_c)
+    for b in range(hoff.size - 1):
+        h0, h1 = int(hoff[b]), int(hoff[b + 1])
+        for c in range(int(coff[b]), int(coff[b + 1])):
+            sl = lambda hist, cand: np.concatenate([hist[h0:h1], cand[c:c + 1]], axis=0)
+            t_seq = None if ts is None else np.concatenate([ts[h0:h1], cts[c:c + 1]])
+            o = attn_fwd(sl(q_hist, q_c), sl(k_hist, k_c), sl(v_hist, v_c),
+                         np.array([0, h1 - h0 + 1]), alpha=alpha, divisor=divisor,
+                         pos_table=pos_table, time_table=time_table, timestamps=t_seq)
+            out[c] = o[-1]
+    return out
+
+
 # ----------------------------------------------------------------------------
 # layer
 # ----------------------------------------------------------------------------

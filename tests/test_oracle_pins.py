@@ -515,3 +515,68 @@ def test_layer_bwd_zero_out_projection_leaves_only_residual_and_weight_grads():
     _, inter = O.layer_fwd(x, p, off, num_heads=H, dqk=d, dv=d, timestamps=ts)
     assert _rel(grads["d_w_out"], d_out.T @ inter["y"]) < 1e-13
     assert _rel(grads["d_b_out"], d_out.sum(0)) < 1e-13
+
+
+# ----------------------------------------------------------------------------
+# candidate scoring against a cached history
+# ----------------------------------------------------------------------------
+def _cand_case(seed, hist_lengths, cand_counts, H=2, d=3, Bp=5, Bt=6):
+    rng = np.random.default_rng(seed)
+    hoff = offsets_from_lengths(hist_lengths)
+    coff = offsets_from_lengths(cand_counts)
+    Th, Tc = int(hoff[-1]), int(coff[-1])
+    qh, kh, vh = (rng.standard_normal((Th, H, d)) for _ in range(3))
+    qc, kc, vc = (rng.standard_normal((Tc, H, d)) for _ in range(3))
+    ts = np.concatenate([np.sort(rng.integers(0, 2000, n)) for n in hist_lengths]).astype(np.int64)
+    cts = np.concatenate([np.full(m, 2100 + 7 * i) for i, m in enumerate(cand_counts)]).astype(np.int64)
+    pt = rng.standard_normal((H, Bp)) * 0.3
+    tt = rng.standard_normal((H, Bt)) * 0.3
+    return dict(qc=qc, kc=kc, vc=vc, coff=coff, kh=kh, vh=vh, qh=qh, hoff=hoff, ts=ts, cts=cts, pt=pt, tt=tt)
+
+
+def _cand(c, **kw):
+    return O.attn_fwd_candidates(c["qc"], c["kc"], c["vc"], c["coff"], c["kh"], c["vh"], c["qh"], c["hoff"],
+                                 pos_table=c["pt"], time_table=c["tt"], timestamps=c["ts"],
+                                 cand_timestamps=c["cts"], **kw)
+
+
+def test_candidates_equal_appending_each_one_to_its_history_by_brute_force():
+    """Each candidate's output against the pure-Python loops of the forward on
+    (history ++ [candidate]) -- an independent transcription of the pages'
+    expression -- for several histories, including an empty one."""
+    c = _cand_case(51, [4, 0, 6], [2, 3, 1])
+    got = _cand(c, alpha=0.8)
+    for b in range(3):
+        h0, h1 = int(c["hoff"][b]), int(c["hoff"][b + 1])
+        for j in range(int(c["coff"][b]), int(c["coff"][b + 1])):
+            cat = lambda hist, cand: np.concatenate([hist[h0:h1], cand[j:j + 1]])
+            ts = np.concatenate([c["ts"][h0:h1], c["cts"][j:j + 1]])
+            ref = B.attn_fwd(cat(c["qh"], c["qc"]), cat(c["kh"], c["kc"]), cat(c["vh"], c["vc"]),
+                             np.array([0, h1 - h0 + 1]), 0.8, 0.0, c["pt"], c["tt"], ts)
+            assert _rel(got[j], ref[-1]) < 1e-12
+
+
+def test_candidates_do_not_see_each_other():
+    """Changing one candidate's q, k, v leaves every other candidate's output
+    bitwise unchanged; permuting candidates permutes outputs."""
+    c = _cand_case(52, [5, 3], [4, 3])
+    base = _cand(c)
+    c2 = dict(c)
+    for key in ("qc", "kc", "vc"):
+        c2[key] = c[key].copy()
+        c2[key][1] += 3.0
+    other = _cand(c2)
+    keep = [i for i in range(base.shape[0]) if i != 1]
+    assert np.array_equal(base[keep], other[keep])
+    perm = np.array([2, 0, 3, 1, 5, 6, 4])
+    c3 = dict(c, qc=c["qc"][perm], kc=c["kc"][perm], vc=c["vc"][perm], cts=c["cts"][perm])
+    assert _rel(_cand(c3), base[perm]) < 1e-13
+
+
+def test_candidates_with_zero_history_are_self_attention_of_one_token():
+    """No history: O_c = SiLU(alpha q.k + P[0] + Tt[0]) v_c / 1, a closed form."""
+    c = _cand_case(53, [0], [3], H=1, d=4)
+    got = _cand(c, alpha=1.3)
+    s = 1.3 * np.einsum("thd,thd->th", c["qc"], c["kc"]) + c["pt"][0, 0] + c["tt"][0, 0]
+    ref = (s / (1 + np.exp(-s)))[..., None] * c["vc"]
+    assert _rel(got, ref) < 1e-13
