@@ -11,6 +11,7 @@ from ._lib import HstuError, load  # noqa: F401
 from .ops import (  # noqa: F401
     attn_bwd,
     attn_fwd,
+    attn_fwd_candidates,
     attn_workspace_size,
     layer_bwd,
     layer_fwd,
@@ -19,5 +20,5 @@ from .ops import (  # noqa: F401
     timing_read,
 )
 
-__all__ = ["HstuError", "load", "attn_fwd", "attn_bwd", "attn_workspace_size", "layer_fwd",
+__all__ = ["HstuError", "load", "attn_fwd", "attn_fwd_candidates", "attn_bwd", "attn_workspace_size", "layer_fwd",
            "layer_bwd", "make_layer_params", "timing_enable", "timing_read"]

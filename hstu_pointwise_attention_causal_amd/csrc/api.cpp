@@ -278,6 +278,56 @@ hstu_status_t hstu_attn_bwd(const hstu_attn_desc_t* desc, const hstu_jagged_t* j
   return ok();
 }
 
+hstu_status_t hstu_attn_fwd_candidates(const hstu_attn_desc_t* desc, const hstu_jagged_t* hist,
+                                       const hstu_jagged_t* cand, int32_t max_candidates, const hstu_bias_t* bias,
+                                       const void* k_hist, int64_t ldkh, const void* v_hist, int64_t ldvh,
+                                       const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
+                                       int64_t ldv, void* o, int64_t ldo, void* hip_stream) {
+  hstu_status_t st = check_attn_common(desc, hist, bias);
+  if (st != HSTU_OK) return st;
+  if (!cand) return fail(HSTU_E_NULL, "candidate batch is NULL");
+  if (desc->dtype != HSTU_BF16) return fail(HSTU_E_UNSUPPORTED, "candidate scoring is built for bf16 only");
+  if (cand->num_seqs != hist->num_seqs) return fail(HSTU_E_SHAPE, "history and candidates differ in num_seqs");
+  if (cand->total_tokens < 0 || max_candidates < 0) return fail(HSTU_E_SHAPE, "negative candidate counts");
+  if (cand->num_seqs > 0 && !cand->seq_offsets) return fail(HSTU_E_NULL, "candidate offsets are NULL");
+  if (cand->total_tokens >= (int64_t(1) << 27)) return fail(HSTU_E_UNSUPPORTED, "too many candidates");
+  if (cand->num_seqs > 65535) return fail(HSTU_E_UNSUPPORTED, "at most 65535 sequences");
+  const bool has_time = bias && bias->time_table;
+  if (has_time && cand->total_tokens > 0 && !cand->timestamps)
+    return fail(HSTU_E_NULL, "time_table given without candidate timestamps");
+  const int64_t Th = hist->total_tokens, Tc = cand->total_tokens, H = desc->num_heads, d = desc->dqk;
+  const hstu_dtype_t dt = desc->dtype;
+  if ((st = check_view("k_hist", k_hist, ldkh, H * d, Th, dt)) != HSTU_OK) return st;
+  if ((st = check_view("v_hist", v_hist, ldvh, H * d, Th, dt)) != HSTU_OK) return st;
+  if ((st = check_view("q", q, ldq, H * d, Tc, dt)) != HSTU_OK) return st;
+  if ((st = check_view("k", k, ldk, H * d, Tc, dt)) != HSTU_OK) return st;
+  if ((st = check_view("v", v, ldv, H * d, Tc, dt)) != HSTU_OK) return st;
+  if ((st = check_view("o", o, ldo, H * d, Tc, dt)) != HSTU_OK) return st;
+  const Range ro = view_range(o, Tc, ldo, H * d, 2);
+  const Range ins[5] = {view_range(k_hist, Th, ldkh, H * d, 2), view_range(v_hist, Th, ldvh, H * d, 2),
+                        view_range(q, Tc, ldq, H * d, 2), view_range(k, Tc, ldk, H * d, 2),
+                        view_range(v, Tc, ldv, H * d, 2)};
+  for (const Range& r : ins)
+    if (overlaps(ro, r)) return fail(HSTU_E_ALIAS, "o overlaps an input");
+  if (cand->num_seqs == 0 || Tc == 0 || max_candidates == 0) return ok();
+  hstu::CandArgs a{};
+  a.q_c = q; a.k_c = k; a.v_c = v; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv;
+  a.k_h = k_hist; a.v_h = v_hist; a.ldkh = ldkh; a.ldvh = ldvh;
+  a.o = o; a.ldo = ldo;
+  a.hist_off = hist->seq_offsets; a.cand_off = cand->seq_offsets;
+  a.ts_h = has_time ? hist->timestamps : nullptr;
+  a.ts_c = has_time ? cand->timestamps : nullptr;
+  a.pos_table = bias ? bias->pos_table : nullptr;
+  a.pos_buckets = bias && bias->pos_table ? bias->pos_buckets : 0;
+  a.time_table = has_time ? bias->time_table : nullptr;
+  a.time_buckets = has_time ? bias->time_buckets : 0;
+  a.alpha = desc->qk_scale; a.divisor = desc->divisor; a.num_heads = static_cast<int>(H);
+  hipError_t e = hstu::launch_attn_cand_bf16(a, static_cast<int>(d), cand->num_seqs, max_candidates,
+                                             static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "candidate scoring launch");
+  return ok();
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

@@ -1,0 +1,291 @@
+// Candidate scoring against a history with cached keys and values (M-FALCON,
+// "micro-batched candidate scoring with KV reuse": briansu.co explainer,
+// section 6 "Why it works"). Candidate c of sequence b, whose history has n
+// tokens, is scored as if it alone were appended at position n:
+//     O_c = ( sum_{j<n} SiLU(S_cj) v_j + SiLU(S_cc) v_c ) / N,   N = n + 1 (or the divisor)
+//     S_cj = alpha q_c.k_j + P[h][min(n - j, Bp-1)] + Tt[h][bucket(t_c - t_j)]
+//     S_cc = alpha q_c.k_c + P[h][0] + Tt[h][0]
+// (the forward's pointwise aggregation of the neurarch model card, "Exported
+// PyTorch", with the relative biases of the briansu.co explainer, section 3).
+// Candidates never see each other, so one pass over the history's K and V
+// serves a whole micro-batch of candidates.
+//
+// A workgroup holds 128 candidates of one (sequence, head), 4 waves of 32.
+// History K / V / timestamp tiles of 64 keys go HBM -> LDS with direct loads,
+// double-buffered. Per 32-key block: S^T = K Q^T on v_mfma_f32_32x32x16_bf16
+// (Q in registers), P = SiLU(S + bias) in fp32, O += P V with P straight from
+// the S^T accumulators and V^T read transposed from LDS (the operand layouts
+// of the forward kernel). Bias per block: a constant position term when every
+// key is at least Bp-1 positions back, else one lookup per key (all
+// candidates share position n); a constant time term when the block's bucket
+// range is one bucket, else one per pair. The candidates' own keys come last,
+// as one 32-key block per wave whose mask keeps the diagonal only.
+#include "attn_common.h"
+#include "common.h"
+#include "launch.h"
+#include "timing.h"
+
+namespace hstu {
+
+namespace {
+
+constexpr int kCWaves = 4;
+constexpr int kCBM = 32 * kCWaves;   // candidates per workgroup
+constexpr int kCBN = 64;             // keys per LDS tile
+constexpr int kCPosLds = 1024;
+constexpr int kCTimeLds = 64;
+
+template <int D>
+struct CandSmem {
+  __attribute__((aligned(16))) char k[2][kCBN * D * 2];
+  __attribute__((aligned(16))) char v[2][kCBN * D * 2];
+  __attribute__((aligned(16))) int64_t t[2][kCBN];
+  float pos[kCPosLds];    // log2(e) P[h][.]
+  float time[kCTimeLds];  // log2(e) Tt[h][.]
+};
+
+// Direct loads of 64 rows of D bf16 (row stride ld) from `base`; rows past
+// `rows_left` read as zeros. Instruction i (of CH) is issued by wave i % 4 and
+// fills LDS slots [64 i, 64 i + 64); slot s holds chunk (s % CH) ^ swz(row) of
+// row s / CH: swz = row mod CH for K (row reads), 4 row mod CH for V
+// (transposed reads).
+template <int CH, bool VSWZ>
+__device__ __forceinline__ void issue_rows64(const char* base, int64_t ld, int rows_left, int w, int lane,
+                                             char* __restrict__ dst) {
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(base, rows_left > 0 ? static_cast<int64_t>(rows_left - 1) * ld * 2 + CH * 16 : 0);
+#pragma unroll
+  for (int j = 0; j < (CH + kCWaves - 1) / kCWaves; ++j) {
+    const int i = w + kCWaves * j;
+    if (CH % kCWaves == 0 || i < CH) {
+      const int sl = i * 64 + lane, r = sl / CH;
+      const int c = (sl % CH) ^ (VSWZ ? ((4 * r) & (CH - 1)) : (r & (CH - 1)));
+      load_lds16(rs, dst + i * 1024, static_cast<uint32_t>(r * ld * 2 + c * 16));
+    }
+  }
+}
+
+__device__ __forceinline__ float silu2(float x) {   // 2 g(x') with g(x') = log2(e) SiLU(x), x' = log2(e) x
+  return x * __builtin_amdgcn_rcpf(fmaf(__builtin_amdgcn_exp2f(-x), 0.5f, 0.5f));
+}
+
+template <int D>
+__global__ __launch_bounds__(kCWaves * 64, 2) void attn_cand_kernel(CandArgs a) {
+  static_assert(D % 32 == 0, "head dim");
+  constexpr int KB = D / 16, NB = D / 32, CH = D / 8;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int64_t h0 = a.hist_off[b], c0 = a.cand_off[b];
+  const int n = static_cast<int>(a.hist_off[b + 1] - h0), m = static_cast<int>(a.cand_off[b + 1] - c0);
+  const int ct0 = blockIdx.x * kCBM;
+  if (ct0 >= m) return;
+
+  __shared__ CandSmem<D> sm;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+  const int cw = ct0 + 32 * w;       // first candidate of this wave
+  const int crow = cw + lr;          // this lane's candidate (column of S^T)
+  const bool has_pos = a.pos_table != nullptr, has_time = a.time_table != nullptr;
+  const int Bp = a.pos_buckets, Bt = a.time_buckets;
+
+  if (has_pos)
+    for (int i = tid; i < min(Bp, kCPosLds); i += kCWaves * 64) sm.pos[i] = kLog2e * a.pos_table[h * Bp + i];
+  if (has_time)
+    for (int i = tid; i < min(Bt, kCTimeLds); i += kCWaves * 64) sm.time[i] = kLog2e * a.time_table[h * Bt + i];
+  const float pos_far = has_pos ? kLog2e * a.pos_table[h * Bp + Bp - 1] : 0.f;
+  const float pos_self = has_pos ? kLog2e * a.pos_table[h * Bp] : 0.f;
+  const float time_self = has_time ? kLog2e * a.time_table[h * Bt] : 0.f;
+  const float alpha_l = a.alpha * kLog2e;
+
+  // Q fragments of the wave's candidates (B operands of S^T = K Q^T)
+  const __bf16* qp = static_cast<const __bf16*>(a.q_c);
+  bf16x8_t qf[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    qf[kb] = crow < m ? *reinterpret_cast<const bf16x8_t*>(qp + (c0 + crow) * a.ldq + h * D + kb * 16 + lh * 8)
+                      : bf16x8_t{};
+  const int64_t tc = (has_time && crow < m) ? a.ts_c[c0 + crow] : 0;
+  // the wave's candidate timestamp range (over its valid candidates)
+  int64_t tc_min = crow < m ? tc : INT64_MAX, tc_max = crow < m ? tc : INT64_MIN;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y0 = __shfl_xor(tc_min, o, 64), y1 = __shfl_xor(tc_max, o, 64);
+    tc_min = y0 < tc_min ? y0 : tc_min;
+    tc_max = y1 > tc_max ? y1 : tc_max;
+  }
+  tc_min = uniform_i64(tc_min);
+  tc_max = uniform_i64(tc_max);
+
+  f32x16_t oacc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16_t{};
+
+  // LDS byte offsets of this lane's fragments inside one tile buffer
+  uint32_t k_lds[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) k_lds[kb] = (lr * CH + ((2 * kb + lh) ^ (lr & (CH - 1)))) * 16;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  uint32_t v_lds[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r1 = 4 * lh + (i16 >> 2);
+    const int c = nb * 4 + (g16 & 1) * 2 + ((i16 & 3) >> 1);
+    v_lds[nb] = (r1 * CH + (c ^ ((4 * r1) & (CH - 1)))) * 16 + (i16 & 1) * 8;
+  }
+
+  auto scores = [&] __device__(const char* kbuf, int kvb) __attribute__((always_inline)) {
+    f32x16_t s = f32x16_t{};
+    const char* kb0 = kbuf + kvb * 32 * CH * 16;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(kb0 + k_lds[kb]), qf[kb], s,
+                                                  0, 0, 0);
+    return s;
+  };
+  auto pv = [&] __device__(const char* vbuf, int kvb, const float* p) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t pa;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pa[i] = static_cast<__bf16>(p[kk * 8 + i]);
+      const char* vb0 = vbuf + (kvb * 32 + kk * 16) * CH * 16;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const bf16x8_t vf =
+            __builtin_shufflevector(tr_read(vb0 + v_lds[nb]), tr_read(vb0 + v_lds[nb] + 8 * CH * 16), 0, 1, 2, 3, 4, 5,
+                                    6, 7);
+        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vf, oacc[nb], 0, 0, 0);
+      }
+    }
+  };
+
+  const char* khb = static_cast<const char*>(a.k_h) + (h0 * a.ldkh + h * D) * 2;
+  const char* vhb = static_cast<const char*>(a.v_h) + (h0 * a.ldvh + h * D) * 2;
+  const int64_t* thb = has_time ? a.ts_h + h0 : nullptr;
+  auto issue_hist = [&] __device__(int t, char* dk, char* dv, int64_t* dt) __attribute__((always_inline)) {
+    const int k0 = t * kCBN;
+    issue_rows64<CH, false>(khb + static_cast<int64_t>(k0) * a.ldkh * 2, a.ldkh, n - k0, w, lane, dk);
+    issue_rows64<CH, true>(vhb + static_cast<int64_t>(k0) * a.ldvh * 2, a.ldvh, n - k0, w, lane, dv);
+    if (w == 0 && lane < kCBN / 2) {
+      const __amdgpu_buffer_rsrc_t rt = make_rsrc(thb ? thb + k0 : nullptr, thb ? static_cast<int64_t>(n - k0) * 8 : 0);
+      load_lds16(rt, reinterpret_cast<char*>(dt), lane * 16);
+    }
+  };
+
+  // ---- history: every key is visible to every candidate (all sit at position n)
+  const int ntiles = (n + kCBN - 1) / kCBN;
+  if (ntiles > 0) issue_hist(0, sm.k[0], sm.v[0], sm.t[0]);
+  wait_vmcnt(0);
+  __syncthreads();   // also publishes the staged bias tables
+  auto tile_step = [&] __device__(const char* __restrict__ rk, const char* __restrict__ rv,
+                                  const int64_t* __restrict__ rt, char* __restrict__ dk, char* __restrict__ dv,
+                                  int64_t* __restrict__ dt, const float* __restrict__ spos,
+                                  const float* __restrict__ stime, int t) __attribute__((always_inline)) {
+    if (t + 1 < ntiles) issue_hist(t + 1, dk, dv, dt);
+    // timestamp range of each 32-key block (lanes 0-31: block 0, 32-63: block 1)
+    int64_t kmin = INT64_MAX, kmax = INT64_MIN;
+    if (has_time && t * kCBN + lane < n) kmin = kmax = rt[lane];
+    for (int o = 1; o < 32; o <<= 1) {
+      const int64_t y0 = __shfl_xor(kmin, o, 64), y1 = __shfl_xor(kmax, o, 64);
+      kmin = y0 < kmin ? y0 : kmin;
+      kmax = y1 > kmax ? y1 : kmax;
+    }
+#pragma unroll
+    for (int kvb = 0; kvb < 2; ++kvb) {
+      const int ka = t * kCBN + kvb * 32;   // first history key of the block
+      if (ka >= n) break;
+      const f32x16_t s = scores(rk, kvb);
+      // position term: constant when every key of the block is >= Bp-1 back
+      const bool pos_const = !has_pos || (n - (ka + 31) >= Bp - 1);
+      // time term: constant when the block's bucket range is one bucket
+      int tlo = 0;
+      bool time_const = true;
+      if (has_time) {
+        const int64_t bmin = __shfl(kmin, 32 * kvb, 64), bmax = __shfl(kmax, 32 * kvb, 64);
+        tlo = time_bucket64(uniform_i64(tc_min) - uniform_i64(bmax), Bt);
+        const int thi = time_bucket64(uniform_i64(tc_max) - uniform_i64(bmin), Bt);
+        time_const = __builtin_amdgcn_readfirstlane(tlo) == __builtin_amdgcn_readfirstlane(thi);
+        tlo = __builtin_amdgcn_readfirstlane(tlo);
+      }
+      const bool tail = ka + 31 >= n;   // keys past the history: masked
+      float p[16];
+      if (pos_const && time_const && !tail) {
+        const float c = (has_pos ? pos_far : 0.f) + (has_time ? stime[tlo] : 0.f);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) p[j] = silu2(fmaf(s[j], alpha_l, c));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int kl = kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);   // key within the tile
+          const int key = t * kCBN + kl;
+          float c = 0.f;
+          if (has_pos) {
+            const int pb = min(max(n - key, 0), Bp - 1);
+            c = pos_const ? pos_far : (pb < kCPosLds ? spos[pb] : kLog2e * a.pos_table[h * Bp + pb]);
+          }
+          if (has_time) c += time_const ? stime[tlo] : stime[time_bucket64(tc - rt[kl], Bt)];
+          p[j] = key < n ? silu2(fmaf(s[j], alpha_l, c)) : 0.f;
+        }
+      }
+      pv(rv, kvb, p);
+    }
+    wait_vmcnt(0);
+    tile_barrier();
+  };
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1, nxt = buf ^ 1;
+    tile_step(sm.k[buf], sm.v[buf], sm.t[buf], sm.k[nxt], sm.v[nxt], sm.t[nxt], sm.pos, sm.time, t);
+  }
+
+  // ---- each candidate's own key: the workgroup's 128 candidates as two
+  //      64-key tiles; wave w reads its 32 from tile w / 2, half w % 2
+  {
+    const char* kcb = static_cast<const char*>(a.k_c) + (c0 * a.ldk + h * D) * 2;
+    const char* vcb = static_cast<const char*>(a.v_c) + (c0 * a.ldv + h * D) * 2;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r0 = ct0 + u * kCBN;
+      issue_rows64<CH, false>(kcb + static_cast<int64_t>(r0) * a.ldk * 2, a.ldk, m - r0, w, lane, sm.k[u]);
+      issue_rows64<CH, true>(vcb + static_cast<int64_t>(r0) * a.ldv * 2, a.ldv, m - r0, w, lane, sm.v[u]);
+    }
+    wait_vmcnt(0);
+    __syncthreads();
+    const char* kbuf = sm.k[w >> 1];
+    const char* vbuf = sm.v[w >> 1];
+    const int kvb = w & 1;
+    const f32x16_t s = scores(kbuf, kvb);
+    float p[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kk = 8 * (j >> 2) + 4 * lh + (j & 3);   // candidate key within the wave's 32
+      p[j] = (kk == lr && crow < m) ? silu2(fmaf(s[j], alpha_l, pos_self + time_self)) : 0.f;
+    }
+    pv(vbuf, kvb, p);
+  }
+
+  // ---- epilogue: oacc[nb][j] = 2 log2(e) N O[cw + 8(j/4) + 4 lh + j%4][nb*32 + lr]
+  const float scale = (a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n + 1)) / (2.0f * kLog2e);
+  __bf16* op = static_cast<__bf16*>(a.o) + (c0 + cw) * a.ldo + h * D + lr;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 8 * (j >> 2) + 4 * lh + (j & 3);
+      if (cw + r < m) op[r * a.ldo + nb * 32] = static_cast<__bf16>(oacc[nb][j] * scale);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_cand_bf16(const CandArgs& a, int d, int num_seqs, int max_candidates, hipStream_t stream) {
+  if (num_seqs <= 0 || max_candidates <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((max_candidates + kCBM - 1) / kCBM), static_cast<unsigned>(a.num_heads),
+                  static_cast<unsigned>(num_seqs));
+  TimedScope timed(kTimedAttnCand, stream);
+  if (d == 128) hipLaunchKernelGGL(attn_cand_kernel<128>, grid, dim3(kCWaves * 64), 0, stream, a);
+  else if (d == 64) hipLaunchKernelGGL(attn_cand_kernel<64>, grid, dim3(kCWaves * 64), 0, stream, a);
+  else if (d == 32) hipLaunchKernelGGL(attn_cand_kernel<32>, grid, dim3(kCWaves * 64), 0, stream, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace hstu

@@ -64,6 +64,32 @@ struct BlockMeta {
 };
 static_assert(sizeof(BlockMeta) == 32, "BlockMeta layout");
 
+// Candidate scoring against a cached history (M-FALCON reading): candidates
+// [T_c, H, d] with cand_off, history keys / values [T_h, H, d] with hist_off.
+struct CandArgs {
+  const void* q_c;
+  const void* k_c;
+  const void* v_c;
+  int64_t ldq, ldk, ldv;
+  const void* k_h;
+  const void* v_h;
+  int64_t ldkh, ldvh;
+  void* o;
+  int64_t ldo;
+  const int64_t* hist_off;
+  const int64_t* cand_off;
+  const int64_t* ts_h;      // history timestamps, NULL without a time table
+  const int64_t* ts_c;      // candidate timestamps, NULL without a time table
+  const float* pos_table;
+  int pos_buckets;
+  const float* time_table;
+  int time_buckets;
+  float alpha;
+  float divisor;
+  int num_heads;
+};
+hipError_t launch_attn_cand_bf16(const CandArgs& a, int d, int num_seqs, int max_candidates, hipStream_t stream);
+
 hipError_t launch_attn_block_meta(const AttnArgs& a, int dqk, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int dqk, int dv, hipStream_t stream);

@@ -12,7 +12,7 @@ namespace hstu {
 namespace {
 
 const char* const kNames[kNumTimed] = {"attn_fwd", "attn_bwd_kv", "attn_bwd_q",
-                                       "layer_gemm_uvqk", "layer_gemm_out", "layer_norm"};
+                                       "layer_gemm_uvqk", "layer_gemm_out", "layer_norm", "attn_cand"};
 
 struct Pending {
   int kernel;

@@ -15,6 +15,7 @@ enum TimedKernel : int {
   kTimedGemmUvqk,
   kTimedGemmOut,
   kTimedLayerNorm,
+  kTimedAttnCand,
   kNumTimed
 };
 

@@ -121,6 +121,41 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets: tor
     return out
 
 
+def attn_fwd_candidates(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cand_offsets: torch.Tensor,
+                        k_hist: torch.Tensor, v_hist: torch.Tensor, hist_offsets: torch.Tensor, *,
+                        timestamps: Optional[torch.Tensor] = None,
+                        cand_timestamps: Optional[torch.Tensor] = None,
+                        pos_table: Optional[torch.Tensor] = None, time_table: Optional[torch.Tensor] = None,
+                        alpha: float = 1.0, divisor: float = 0.0, max_candidates: Optional[int] = None,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """hstu_attn_fwd_candidates: candidates q, k, v [T_c, H, d] (offsets
+    cand_offsets) scored against a history with cached k_hist, v_hist
+    [T_h, H, d] (offsets hist_offsets). max_candidates defaults to the largest
+    per-sequence candidate count (read from cand_offsets on the host)."""
+    lib = _lib.load()
+    Tc, H = q.shape[0], q.shape[1]
+    d, ldq = _token_view("q", q, H)
+    _, ldk = _token_view("k", k, H)
+    _, ldv = _token_view("v", v, H)
+    _, ldkh = _token_view("k_hist", k_hist, H)
+    _, ldvh = _token_view("v_hist", v_hist, H)
+    if out is None:
+        out = torch.empty((Tc, H, d), dtype=v.dtype, device=v.device)
+    _, ldo = _token_view("o", out, H)
+    if max_candidates is None:
+        c = cand_offsets.cpu()
+        max_candidates = int((c[1:] - c[:-1]).max()) if c.numel() > 1 else 0
+    desc = _desc(H, d, d, q.dtype, alpha, divisor)
+    jh = _jagged(hist_offsets, k_hist.shape[0], timestamps)
+    jc = _jagged(cand_offsets, Tc, cand_timestamps)
+    b = _bias(pos_table, time_table)
+    _lib.check(lib.hstu_attn_fwd_candidates(ctypes.byref(desc), ctypes.byref(jh), ctypes.byref(jc),
+                                            int(max_candidates), ctypes.byref(b), _ptr(k_hist), ldkh,
+                                            _ptr(v_hist), ldvh, _ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv,
+                                            _ptr(out), ldo, _stream_handle(q.device)))
+    return out
+
+
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tensor,
              seq_offsets: torch.Tensor, *, timestamps: Optional[torch.Tensor] = None,
              pos_table: Optional[torch.Tensor] = None, time_table: Optional[torch.Tensor] = None,

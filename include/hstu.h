@@ -147,6 +147,34 @@ hstu_status_t hstu_attn_bwd(const hstu_attn_desc_t* desc, const hstu_jagged_t* j
                             float* d_pos_table, float* d_time_table,
                             void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * hstu_attn_fwd_candidates -- candidate scoring against a history whose keys
+ * and values are cached (M-FALCON, "micro-batched candidate scoring with KV
+ * reuse": briansu.co explainer, section 6 "Why it works"; the pages give no
+ * formula, the reading here): candidate c of sequence b, whose history has n
+ * tokens, is scored exactly as if it alone were appended at position n --
+ *   O_c = ( sum_{j<n} SiLU(S_cj) v_j + SiLU(S_cc) v_c ) / N,  N = n + 1
+ *         (divisor <= 0) or the divisor,
+ *   S_cj = qk_scale q_c.k_j + P[h][min(n-j, Bp-1)] + Tt[h][bucket(t_c - t_j)],
+ *   S_cc = qk_scale q_c.k_c + P[h][0] + Tt[h][0];
+ * candidates never attend to each other.
+ *   hist: history batch (offsets; timestamps when there is a time table).
+ *   cand: candidate batch, same num_seqs (offsets; candidate timestamps).
+ *   max_candidates: host upper bound on any sequence's candidate count; it
+ *     sizes the grid -- candidates past it in a sequence are not scored.
+ *   k_hist, v_hist [T_h,H,d] (ldkh, ldvh): the history's cached keys / values.
+ *   q, k, v [T_c,H,d]: the candidates' projections. o [T_c,H,d]: output.
+ * bf16 only (dqk == dv in {32, 64, 128}); no workspace. Errors: as
+ * hstu_attn_fwd.
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_attn_fwd_candidates(const hstu_attn_desc_t* desc, const hstu_jagged_t* hist,
+                                       const hstu_jagged_t* cand, int32_t max_candidates,
+                                       const hstu_bias_t* bias,
+                                       const void* k_hist, int64_t ldkh, const void* v_hist, int64_t ldvh,
+                                       const void* q, int64_t ldq, const void* k, int64_t ldk,
+                                       const void* v, int64_t ldv, void* o, int64_t ldo,
+                                       void* hip_stream);
+
 /* Parameters of one HSTU layer (bf16 weights, fp32 norms and biases). Weight
  * matrices use the nn.Linear layout [out_features, in_features] of the
  * neurarch exported block (row-major, contiguous). */

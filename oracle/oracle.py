@@ -287,15 +287,18 @@ def attn_fwd_candidates(q_c, k_c, v_c, cand_offsets, k_hist, v_hist, q_hist, seq
     ts = None if timestamps is None else np.asarray(timestamps, dtype=np.int64)
     cts = None if cand_timestamps is None else np.asarray(cand_timestamps, dtype=np.int64)
     out = np.zeros_like(v_c)
+    H = q_c.shape[1]
     for b in range(hoff.size - 1):
         h0, h1 = int(hoff[b]), int(hoff[b + 1])
         for c in range(int(coff[b]), int(coff[b + 1])):
             sl = lambda hist, cand: np.concatenate([hist[h0:h1], cand[c:c + 1]], axis=0)
             t_seq = None if ts is None else np.concatenate([ts[h0:h1], cts[c:c + 1]])
-            o = attn_fwd(sl(q_hist, q_c), sl(k_hist, k_c), sl(v_hist, v_c),
-                         np.array([0, h1 - h0 + 1]), alpha=alpha, divisor=divisor,
-                         pos_table=pos_table, time_table=time_table, timestamps=t_seq)
-            out[c] = o[-1]
+            qs, ks, vs = sl(q_hist, q_c), sl(k_hist, k_c), sl(v_hist, v_c)
+            # the appended row only (attn_fwd_rows evaluates attn_fwd's rows one by one)
+            for hh in range(H):
+                out[c, hh] = attn_fwd_rows(qs, ks, vs, np.array([0, h1 - h0 + 1]), 0, hh, [h1 - h0],
+                                           alpha=alpha, divisor=divisor, pos_table=pos_table,
+                                           time_table=time_table, timestamps=t_seq)[0]
     return out
 
 

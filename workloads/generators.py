@@ -145,6 +145,7 @@ class Workload:
     divisor: float = 0.0        # <= 0: per-sequence length n; > 0: fixed constant
     ln_eps: float = 1e-6
     note: str = ""
+    cand: Optional[dict] = None               # candidate scoring: offsets, q, k, v, timestamps
 
     @property
     def num_seqs(self) -> int:
@@ -261,6 +262,42 @@ def _layer_recipe(name, seed, *, lengths=None, draw_lengths=None, num_layers=1, 
         layers=layers, d_o=d_out, note=note)
 
 
+def _cand_recipe(name, seed, *, lengths=None, draw_lengths=None, cands=1024, H=4, d=128,
+                 Bp=128, Bt=128, table_std=0.02, note=""):
+    """Candidate-scoring inputs: histories with cached k, v and a micro-batch
+    of candidates per history.
+
+    Draw order: [history lengths], history k, v, candidate q, k, v, history
+    timestamps, candidate gaps ~ Exponential(mean 3600 s) after each history's
+    last timestamp (one per sequence: the request time), position table, time
+    table. q, k, v ~ N(0, 1/d) rounded to bf16. The history's q (not read by
+    candidate scoring) is all zeros.
+    """
+    rng = np.random.default_rng(seed)
+    if draw_lengths is not None:
+        lo, hi, count = draw_lengths
+        lengths = log_uniform_lengths(rng, count, lo, hi)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    m = np.full(lengths.size, cands, np.int64) if np.isscalar(cands) else np.asarray(cands, np.int64)
+    hoff, coff = offsets_from_lengths(lengths), offsets_from_lengths(m)
+    Th, Tc = int(hoff[-1]), int(coff[-1])
+    std = 1.0 / np.sqrt(d)
+    kh, vh = (round_to_bf16(normal(rng, (Th, H, d), std)) for _ in range(2))
+    qc, kc, vc = (round_to_bf16(normal(rng, (Tc, H, d), std)) for _ in range(3))
+    ts = exponential_timestamps(rng, np.maximum(lengths, 1))
+    # per sequence the history's timestamps; an empty history keeps its one drawn value as a base
+    base = offsets_from_lengths(np.maximum(lengths, 1))
+    ts_h = np.concatenate([ts[base[b]:base[b] + lengths[b]] for b in range(lengths.size)]).astype(np.int64)
+    last = np.array([ts[base[b + 1] - 1] for b in range(lengths.size)], np.int64)
+    gaps = np.floor(rng.exponential(3600.0, size=lengths.size)).astype(np.int64)
+    ts_c = np.repeat(last + gaps, m).astype(np.int64)
+    pt = normal(rng, (H, Bp), table_std)
+    tt = normal(rng, (H, Bt), table_std)
+    return Workload(name=name, kind="cand", dtype="bf16", num_heads=H, dqk=d, dv=d, seq_offsets=hoff,
+                    timestamps=ts_h, pos_table=pt, time_table=tt, q=np.zeros_like(kh), k=kh, v=vh,
+                    note=note, cand=dict(offsets=coff, q=qc, k=kc, v=vc, timestamps=ts_c))
+
+
 def _c0(seed=0):
     """fp32 attention, one sequence n=256, H=2, d=32, q,k,v ~ N(0,1),
     64-bucket position table ~ N(0, 0.02), no time bias."""
@@ -310,6 +347,14 @@ WORKLOADS = {
         "c5", seed, draw_lengths=(64, 2048, 32), num_layers=1, time=True, backward=True,
         note="one layer forward + backward, 32 sequences log-uniform in [64, 2048], D 512, H 4, "
              "d 128, pos + time bias"),
+    # --- candidate scoring against cached histories (M-FALCON reading) ---
+    "c6": lambda seed=6: _cand_recipe(
+        "c6", seed, draw_lengths=(1024, 8192, 16), cands=1024, H=4, d=128,
+        note="candidate scoring: 16 histories log-uniform in [1024, 8192], 1024 candidates each, "
+             "H 4, d 128, pos + time bias"),
+    "c6_small": lambda seed=16: _cand_recipe(
+        "c6_small", seed, lengths=[300, 0, 77, 1, 140], cands=[5, 3, 0, 130, 64], H=2, d=128,
+        note="candidate scoring, ragged histories incl. empty and one-token, 0 to 130 candidates"),
     "c5_small": lambda seed=15: _layer_recipe(
         "c5_small", seed, draw_lengths=(1, 500, 7), num_layers=1, time=True, backward=True,
         note="one layer forward + backward, 7 ragged sequences"),
