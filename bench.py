@@ -32,6 +32,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -307,6 +309,45 @@ def secondary_layer_fwd_bwd(hstu, name: str, steps: int, warmup: int, dev):
     }
 
 
+def secondary_candidates(hstu, name: str, steps: int, warmup: int, dev):
+    """Candidate scoring against cached histories: candidates/s and
+    causal-effective TFLOP/s (each candidate attends its history plus itself:
+    512 flop per (candidate, key) pair per head at d = 128)."""
+    import torch
+    from workloads import make_workload
+    wl = make_workload(name)
+    c = wl.cand
+    bf = torch.bfloat16
+    t = lambda a, dt=None: torch.from_numpy(a).to(dev) if dt is None else torch.from_numpy(a).to(dev).to(dt)
+    q, k, v = t(c["q"], bf), t(c["k"], bf), t(c["v"], bf)
+    kh, vh = t(wl.k, bf), t(wl.v, bf)
+    coff, hoff = t(c["offsets"]), t(wl.seq_offsets)
+    ts, cts = t(wl.timestamps), t(c["timestamps"])
+    pt, tt = t(wl.pos_table, torch.float32), t(wl.time_table, torch.float32)
+    out = torch.empty_like(v)
+    m = np.diff(c["offsets"])
+    mmax = int(m.max())
+
+    def step():
+        hstu.attn_fwd_candidates(q, k, v, coff, kh, vh, hoff, timestamps=ts, cand_timestamps=cts,
+                                 pos_table=pt, time_table=tt, max_candidates=mmax, out=out)
+
+    stream = torch.cuda.current_stream(dev)
+    ms_ev, ms_wall = time_steps(step, steps, warmup, stream)
+    ms = max(ms_ev, ms_wall)
+    kern = kernel_ms(hstu, step, steps, ["attn_cand"])["attn_cand"]
+    pairs = float(np.sum(m * (np.diff(wl.seq_offsets) + 1))) * wl.num_heads
+    F = pairs * 2.0 * (wl.dqk + wl.dv)
+    return {
+        "workload": f"{name}: {wl.note}",
+        "candidates_per_s": round(float(m.sum()) / (ms * 1e-3), 1),
+        "tflops": round(F / (ms * 1e-3) / 1e12, 2),
+        "ms_per_step": round(ms, 5),
+        "kernel_ms": round(kern, 5) if kern else None,
+        "kernel_tflops": round(F / (kern * 1e-3) / 1e12, 2) if kern else None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -397,6 +438,7 @@ def main():
             "attn_fwd_bwd": secondary_fwd_bwd(hstu, "c4", args.steps, args.warmup, dev),
             "layer_fwd_bwd": secondary_layer_fwd_bwd(hstu, "c5", max(5, args.steps // 5),
                                                      max(2, args.warmup // 10), dev),
+            "candidates": secondary_candidates(hstu, "c6", max(5, args.steps // 2), max(5, args.warmup // 4), dev),
         }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
