@@ -10,6 +10,8 @@ Sources, cited by page title and section:
   the per-head views, and the pointwise aggregation -- SiLU of q.k^T divided
   by the sequence length, lower-triangular (causal, diagonal kept) mask taken
   after the SiLU, then multiplied by v. No softmax.
+* neurarch model card, sections "Structure" and "Machine access" (graph
+  JSON): the final RMSNorm (eps 1e-6) and the tied, bias-free retrieval head.
 * briansu.co "HSTU: Hierarchical Sequential Transduction Units", section 3
   "How it works": the three steps of a layer (pointwise projection to
   U, V, Q, K; spatial aggregation by pointwise SiLU attention with relative
@@ -491,3 +493,32 @@ def stack_fwd(x, layers, seq_offsets, *, num_heads: int, dqk: int, dv: int,
         h, _ = layer_fwd(h, p, seq_offsets, num_heads=num_heads, dqk=dqk, dv=dv,
                          timestamps=timestamps, eps=eps)
     return h
+
+
+# ----------------------------------------------------------------------------
+# final norm and retrieval head
+# ----------------------------------------------------------------------------
+def rms_norm(x, gamma=None, eps: float = 1e-6) -> np.ndarray:
+    """RMSNorm over the last axis, float64: x / sqrt(mean(x^2) + eps) * gamma.
+
+    The norm between the last HSTU block and the head in the neurarch model
+    card (structure table row "RMSNorm", 512 features; the graph JSON's norm
+    node gives eps 1e-6; the exported code builds ``nn.RMSNorm(512)``). Unlike
+    LayerNorm no mean is subtracted and there is no shift. gamma None means
+    ones (the initial value)."""
+    x = np.asarray(x, dtype=np.float64)
+    y = x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    return y if gamma is None else y * _f64(gamma)
+
+
+def head_fwd(x, table, gamma=None, eps: float = 1e-6) -> np.ndarray:
+    """Catalogue logits of the retrieval head, float64:
+        logits[t, i] = sum_d RMSNorm(x)[t, d] * table[i, d].
+
+    The neurarch model card's head maps 512 features to 200000 item logits
+    with a bias-free linear map (structure table row "Retrieval Head";
+    exported code ``nn.Linear(512, 200000, bias=False)``), and its graph JSON
+    marks the head's weights as tied, read here as: the [vocab, D] weight is
+    the token-embedding table itself. A subset of items is scored by passing
+    those rows of the table."""
+    return rms_norm(x, gamma, eps) @ _f64(table).T

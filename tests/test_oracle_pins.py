@@ -580,3 +580,75 @@ def test_candidates_with_zero_history_are_self_attention_of_one_token():
     s = 1.3 * np.einsum("thd,thd->th", c["qc"], c["kc"]) + c["pt"][0, 0] + c["tt"][0, 0]
     ref = (s / (1 + np.exp(-s)))[..., None] * c["vc"]
     assert _rel(got, ref) < 1e-13
+
+
+# ----------------------------------------------------------------------------
+# final RMSNorm and tied retrieval head
+# ----------------------------------------------------------------------------
+def test_head_matches_torch_rms_norm_and_linear():
+    """The library's own RMSNorm and bias-free linear map, in float64 on the CPU."""
+    import torch
+    rng = np.random.default_rng(70)
+    x = rng.standard_normal((37, 64)) * rng.uniform(0.01, 3.0, size=(37, 1))
+    gamma = 1 + 0.3 * rng.standard_normal(64)
+    table = 0.02 * rng.standard_normal((301, 64))
+    eps = 1e-6
+    ref = torch.nn.functional.linear(
+        torch.nn.functional.rms_norm(torch.from_numpy(x), (64,), torch.from_numpy(gamma), eps),
+        torch.from_numpy(table)).numpy()
+    got = O.head_fwd(x, table, gamma, eps)
+    assert got.shape == (37, 301)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_rms_norm_constant_row_and_unit_rms():
+    """eps = 0: a constant row c maps to sign(c) * gamma; any nonzero row has
+    mean square exactly 1 with gamma = 1; a zero row stays zero (eps > 0)."""
+    rng = np.random.default_rng(71)
+    gamma = rng.standard_normal(32)
+    for c in (3.5, -0.25):
+        np.testing.assert_allclose(O.rms_norm(np.full((1, 32), c), gamma, 0.0)[0], np.sign(c) * gamma,
+                                   rtol=1e-14)
+    y = O.rms_norm(rng.standard_normal((9, 32)) * 7.0, None, 0.0)
+    np.testing.assert_allclose((y * y).mean(axis=1), 1.0, rtol=1e-13)
+    z = O.rms_norm(np.zeros((2, 32)), gamma, 1e-6)
+    assert np.all(z == 0.0)
+
+
+def test_head_scale_invariance_and_sign():
+    """eps = 0: scaling a token row by s > 0 leaves its logits unchanged, a
+    negative s negates them (the norm divides by the root mean square, not by
+    the variance about the mean)."""
+    rng = np.random.default_rng(72)
+    x = rng.standard_normal((5, 48)) + 2.0
+    table = rng.standard_normal((20, 48))
+    gamma = rng.uniform(0.5, 1.5, 48)
+    base = O.head_fwd(x, table, gamma, 0.0)
+    np.testing.assert_allclose(O.head_fwd(13.0 * x, table, gamma, 0.0), base, rtol=1e-12)
+    np.testing.assert_allclose(O.head_fwd(-0.5 * x, table, gamma, 0.0), -base, rtol=1e-12)
+
+
+def test_head_with_basis_table_is_a_gather_of_the_normalised_row():
+    """Table row i = unit vector e_{p(i)}: logit i is feature p(i) of the normalised row."""
+    rng = np.random.default_rng(73)
+    D = 16
+    x = rng.standard_normal((4, D))
+    gamma = rng.standard_normal(D)
+    perm = rng.permutation(D)
+    table = np.eye(D)[perm]
+    y = O.rms_norm(x, gamma, 1e-6)
+    np.testing.assert_array_equal(O.head_fwd(x, table, gamma, 1e-6), y[:, perm])
+
+
+def test_tied_head_retrieves_each_token_own_item():
+    """Tied weights: tokens are rows of the same table the head scores
+    against. With equal-norm rows, gamma = 1 and eps = 0, the own item's logit
+    is sqrt(D) * |e| (Cauchy-Schwarz maximum) and it is the arg max."""
+    rng = np.random.default_rng(74)
+    V, D, r = 500, 64, 0.3
+    table = rng.standard_normal((V, D))
+    table *= r / np.linalg.norm(table, axis=1, keepdims=True)
+    ids = rng.integers(0, V, size=40)
+    logits = O.head_fwd(table[ids], table, None, 0.0)
+    np.testing.assert_allclose(logits[np.arange(40), ids], math.sqrt(D) * r, rtol=1e-12)
+    assert np.array_equal(logits.argmax(axis=1), ids)
