@@ -17,7 +17,9 @@ Also on the line:
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload;
   secondary     tokens/s per layer of the 4-layer stack (8 x 1024 tokens) and
                 of one layer over the 64-sequence jagged batch, and the
-                attention forward + backward of the 32-sequence jagged batch.
+                attention forward + backward of the 32-sequence jagged batch, one
+                layer forward + backward, candidate scoring against cached
+                histories, and the final RMSNorm + tied retrieval head.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
     python bench.py --copy-calib      # plain copy of known size, for counter scaling
@@ -348,6 +350,43 @@ def secondary_candidates(hstu, name: str, steps: int, warmup: int, dev):
     }
 
 
+def secondary_head(hstu, name: str, steps: int, warmup: int, dev):
+    """Final RMSNorm + tied retrieval head: token rows/s, TFLOP/s of the
+    logits GEMM (2 D flop per (row, item) pair) and its bf16 logits write rate."""
+    import torch
+    from workloads import make_workload
+    wl = make_workload(name)
+    h = wl.head
+    x = torch.from_numpy(wl.x).to(dev).to(torch.bfloat16)
+    table = torch.from_numpy(h["table"]).to(dev).to(torch.bfloat16)
+    gamma = None if h["gamma"] is None else torch.from_numpy(h["gamma"]).to(dev)
+    rows, vocab = x.shape[0], table.shape[0]
+    out = torch.empty((rows, vocab), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(hstu.head_workspace_size(rows, wl.embed_dim), dtype=torch.uint8, device=dev)
+
+    def step():
+        hstu.head_fwd(x, table, gamma=gamma, eps=h["eps"], out=out, workspace=ws)
+
+    stream = torch.cuda.current_stream(dev)
+    ms_ev, ms_wall = time_steps(step, steps, warmup, stream)
+    ms = max(ms_ev, ms_wall)
+    kern = kernel_ms(hstu, step, steps, ["head_rms_norm", "head_gemm"])
+    F = 2.0 * rows * vocab * wl.embed_dim
+    kg = kern["head_gemm"]
+    return {
+        "workload": f"{name}: {wl.note}",
+        "rows_per_s": round(rows / (ms * 1e-3), 1),
+        "tflops": round(F / (ms * 1e-3) / 1e12, 2),
+        "ms_per_step": round(ms, 5),
+        "kernel_ms": {k: (round(v, 5) if v else None) for k, v in kern.items()},
+        "gemm_tflops": round(F / (kg * 1e-3) / 1e12, 2) if kg else None,
+        "gemm_logits_write_gbs": round(rows * vocab * 2 / (kg * 1e-3) / 1e9, 1) if kg else None,
+    }
+
+
+SECONDARY = ("layer_stack", "layer_jagged", "attn_fwd_bwd", "layer_fwd_bwd", "candidates", "head")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,6 +395,8 @@ def main():
     ap.add_argument("--workload", default="c3", help="attention-forward workload of the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary", default=",".join(SECONDARY),
+                    help="comma-separated secondary figures to run (default: all)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true")
     args = ap.parse_args()
@@ -432,14 +473,22 @@ def main():
         },
     }
     if not args.no_secondary:
-        res["secondary"] = {
-            "layer_stack": secondary_layers(hstu, "c1", args.steps, args.warmup, dev),
-            "layer_jagged": secondary_layers(hstu, "c2", max(5, args.steps // 5), max(2, args.warmup // 10), dev),
-            "attn_fwd_bwd": secondary_fwd_bwd(hstu, "c4", args.steps, args.warmup, dev),
-            "layer_fwd_bwd": secondary_layer_fwd_bwd(hstu, "c5", max(5, args.steps // 5),
+        runs = {
+            "layer_stack": lambda: secondary_layers(hstu, "c1", args.steps, args.warmup, dev),
+            "layer_jagged": lambda: secondary_layers(hstu, "c2", max(5, args.steps // 5),
                                                      max(2, args.warmup // 10), dev),
-            "candidates": secondary_candidates(hstu, "c6", max(5, args.steps // 2), max(5, args.warmup // 4), dev),
+            "attn_fwd_bwd": lambda: secondary_fwd_bwd(hstu, "c4", args.steps, args.warmup, dev),
+            "layer_fwd_bwd": lambda: secondary_layer_fwd_bwd(hstu, "c5", max(5, args.steps // 5),
+                                                             max(2, args.warmup // 10), dev),
+            "candidates": lambda: secondary_candidates(hstu, "c6", max(5, args.steps // 2),
+                                                       max(5, args.warmup // 4), dev),
+            "head": lambda: secondary_head(hstu, "c7", max(5, args.steps // 4), max(5, args.warmup // 10), dev),
         }
+        wanted = [w for w in args.secondary.split(",") if w]
+        unknown = sorted(set(wanted) - set(runs))
+        if unknown:
+            ap.error(f"unknown secondary figure(s): {unknown}")
+        res["secondary"] = {w: runs[w]() for w in wanted}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)

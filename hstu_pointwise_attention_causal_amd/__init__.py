@@ -13,6 +13,8 @@ from .ops import (  # noqa: F401
     attn_fwd,
     attn_fwd_candidates,
     attn_workspace_size,
+    head_fwd,
+    head_workspace_size,
     layer_bwd,
     layer_fwd,
     make_layer_params,
@@ -21,4 +23,4 @@ from .ops import (  # noqa: F401
 )
 
 __all__ = ["HstuError", "load", "attn_fwd", "attn_fwd_candidates", "attn_bwd", "attn_workspace_size", "layer_fwd",
-           "layer_bwd", "make_layer_params", "timing_enable", "timing_read"]
+           "layer_bwd", "head_fwd", "head_workspace_size", "make_layer_params", "timing_enable", "timing_read"]

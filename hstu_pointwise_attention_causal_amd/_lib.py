@@ -25,6 +25,7 @@ EXPORTED = (
     "hstu_attn_workspace_size", "hstu_attn_fwd", "hstu_attn_bwd", "hstu_attn_fwd_candidates",
     "hstu_layer_workspace_size", "hstu_layer_fwd",
     "hstu_layer_bwd_workspace_size", "hstu_layer_bwd",
+    "hstu_head_workspace_size", "hstu_head_fwd",
     "hstu_timing_enable", "hstu_timing_read",
     "hstu_status_string", "hstu_last_error", "hstu_version",
 )
@@ -118,6 +119,10 @@ def load() -> ctypes.CDLL:
     lib.hstu_layer_bwd_workspace_size.restype = c
     lib.hstu_layer_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.hstu_layer_bwd.restype = c
+    lib.hstu_head_workspace_size.argtypes = [_I64, c, ctypes.POINTER(_SZ)]
+    lib.hstu_head_workspace_size.restype = c
+    lib.hstu_head_fwd.argtypes = [_I64, c, _I64, ctypes.c_float, _P, _I64, _P, _P, _I64, _P, _I64, _P, _SZ, _P]
+    lib.hstu_head_fwd.restype = c
     lib.hstu_timing_enable.argtypes = [c]
     lib.hstu_timing_enable.restype = c
     lib.hstu_timing_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]

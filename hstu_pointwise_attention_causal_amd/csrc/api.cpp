@@ -382,6 +382,10 @@ hstu_status_t check_layer(const hstu_layer_params_t* p, const hstu_jagged_t* j) 
 // K splits of the two weight-gradient GEMMs (K = tokens).
 constexpr int kLnBwdRows = 16;
 constexpr int kColSumRows = 16;
+// Head GEMM tile order: bands of 8 tile rows (2048 token rows, 2 MB of
+// normalised rows at dim 512) walked column by column, so the 32 workgroups
+// resident on an XCD share that band in L2 and read each table tile together.
+constexpr int kHeadGroupRows = 8;
 
 int weight_grad_splits(int64_t M, int64_t N, int64_t T) {
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
@@ -701,6 +705,57 @@ hstu_status_t hstu_layer_bwd(const hstu_layer_params_t* p, const hstu_jagged_t* 
   if ((e = hstu::launch_sum_rows(part, pl, D, 2 * D, 1.0f, grads->d_ln_in_gamma, scratch, stream)) != hipSuccess ||
       (e = hstu::launch_sum_rows(part + D, pl, D, 2 * D, 1.0f, grads->d_ln_in_beta, scratch, stream)) != hipSuccess)
     return hip_fail(e, "input LayerNorm parameter gradient sum");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// final RMSNorm + retrieval head
+// ---------------------------------------------------------------------------
+hstu_status_t hstu_head_workspace_size(int64_t rows, int32_t dim, size_t* bytes) {
+  if (!bytes) return fail(HSTU_E_NULL, "bytes is NULL");
+  if (rows < 0 || dim < 1) return fail(HSTU_E_SHAPE, "negative rows or dim < 1");
+  *bytes = static_cast<size_t>(rows) * static_cast<size_t>(dim) * 2;
+  return ok();
+}
+
+hstu_status_t hstu_head_fwd(int64_t rows, int32_t dim, int64_t vocab, float eps, const void* x, int64_t ldx,
+                            const float* gamma, const void* table, int64_t ldt, void* logits, int64_t ldl,
+                            void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (rows < 0 || vocab < 0) return fail(HSTU_E_SHAPE, "negative rows or vocab");
+  if (dim != 512 && dim != 1024) return fail(HSTU_E_UNSUPPORTED, "dim must be 512 or 1024 (got %d)", dim);
+  if (!(eps >= 0.f)) return fail(HSTU_E_SHAPE, "eps must be >= 0");
+  if (rows == 0 || vocab == 0) return ok();
+  if (!x || !table || !logits) return fail(HSTU_E_NULL, "x, table or logits is NULL");
+  if (ldx < dim || ldt < dim || ldl < vocab) return fail(HSTU_E_SHAPE, "a row stride is below its row width");
+  if (vocab % 8 != 0) return fail(HSTU_E_UNSUPPORTED, "vocab must be a multiple of 8 (got %lld)", (long long)vocab);
+  const int64_t tiles = ((rows + 255) / 256) * ((vocab + 255) / 256);
+  if (rows >= (int64_t(1) << 31) || vocab >= (int64_t(1) << 31) || tiles >= (int64_t(1) << 31))
+    return fail(HSTU_E_UNSUPPORTED, "rows x vocab too large for one launch");
+  if (!aligned16(x) || !aligned16(table) || !aligned16(logits) || (gamma && !aligned16(gamma)) ||
+      ldx % 8 != 0 || ldt % 8 != 0 || ldl % 8 != 0)
+    return fail(HSTU_E_ALIGN, "x, table, logits and gamma must be 16-byte aligned and row strides multiples of 8");
+  const Range rl = view_range(logits, rows, ldl, vocab, 2);
+  if (overlaps(rl, view_range(x, rows, ldx, dim, 2)) || overlaps(rl, view_range(table, vocab, ldt, dim, 2)) ||
+      overlaps(rl, view_range(gamma, 1, dim, dim, 4)))
+    return fail(HSTU_E_ALIAS, "logits overlap x, gamma or the table");
+  const size_t need = static_cast<size_t>(rows) * static_cast<size_t>(dim) * 2;
+  if (!workspace || workspace_bytes < need)
+    return fail(HSTU_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(HSTU_E_ALIGN, "workspace must be 16-byte aligned");
+  const Range rw = view_range(workspace, rows, dim, dim, 2);
+  if (overlaps(rw, rl) || overlaps(rw, view_range(x, rows, ldx, dim, 2)) ||
+      overlaps(rw, view_range(table, vocab, ldt, dim, 2)) || overlaps(rw, view_range(gamma, 1, dim, dim, 4)))
+    return fail(HSTU_E_ALIAS, "workspace overlaps an argument");
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e;
+  hstu::LnArgs rn{};
+  rn.x = x; rn.ldx = ldx; rn.y = workspace; rn.ldy = dim; rn.gamma = gamma; rn.eps = eps; rn.rows = rows;
+  if ((e = hstu::launch_rms_rows(rn, dim, stream)) != hipSuccess) return hip_fail(e, "RMSNorm launch");
+  hstu::GemmArgs g{};
+  g.a = workspace; g.lda = dim; g.b = table; g.ldb = ldt; g.c = logits; g.ldc = ldl;
+  g.M = static_cast<int>(rows); g.N = static_cast<int>(vocab); g.K = dim;
+  g.group_m = kHeadGroupRows;
+  if ((e = hstu::launch_head_gemm(g, stream)) != hipSuccess) return hip_fail(e, "head GEMM launch");
   return ok();
 }
 

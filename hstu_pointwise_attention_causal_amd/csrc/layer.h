@@ -34,6 +34,7 @@ struct GemmArgs {
   int64_t ldc2;
   int64_t split_stride;   // elements between split partials (kEpiF32)
   int M, N, K;
+  int group_m;         // > 1: tile order in bands of group_m tile rows, column by column
 };
 
 // y = LN(x) * gamma + beta (optionally * gate), rows of `width` features, bf16 in/out.
@@ -102,5 +103,13 @@ hipError_t launch_sum_rows(const float* in, int64_t P, int64_t W, int64_t ld, fl
 int64_t sum_rows_scratch_floats(int64_t P, int64_t W);
 hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream);
 hipError_t launch_ln_rows(const LnArgs& a, int width, hipStream_t stream);
+
+// y = x / sqrt(mean(x^2) + eps) * gamma (gamma NULL: ones; beta and gate unused),
+// width 512 or 1024.
+hipError_t launch_rms_rows(const LnArgs& a, int width, hipStream_t stream);
+
+// The retrieval head's C = A B^T (kEpiNone, row-major operands, no bias),
+// timed on its own.
+hipError_t launch_head_gemm(const GemmArgs& g, hipStream_t stream);
 
 }  // namespace hstu

@@ -201,10 +201,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_kernel(Gem
   // Workgroups are dealt to the 8 XCDs in turn (block b to XCD b % 8). Tile t
   // of the row-major tile order goes to a block on XCD t / ceil-share, so each
   // XCD's L2 serves a contiguous band of A rows against all of B.
+  // With group_m > 1 the order walks bands of group_m tile rows column by
+  // column instead, so the workgroups resident on one XCD share a short band
+  // of A rows and a few B tiles (for outputs far wider than tall).
   const int tiles_n = (g.N + BN - 1) / BN;
   const int tiles = gridDim.x, xcd = blockIdx.x % 8, q = tiles / 8, r = tiles % 8;
   const int t = xcd * q + min(xcd, r) + blockIdx.x / 8;
-  const int tm = t / tiles_n, tn = t % tiles_n;
+  int tm, tn;
+  if (g.group_m > 1) {
+    const int tiles_m = (g.M + BM - 1) / BM;
+    const int band = t / (g.group_m * tiles_n), idx = t - band * g.group_m * tiles_n;
+    const int rows = min(g.group_m, tiles_m - band * g.group_m);
+    tm = band * g.group_m + idx % rows;
+    tn = idx / rows;
+  } else {
+    tm = t / tiles_n;
+    tn = t % tiles_n;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -338,7 +351,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_kernel(Gem
 // ----------------------------------------------------------------------------
 // LayerNorm over a token row (optionally times a gate row), one wave per row.
 // ----------------------------------------------------------------------------
-template <int D>
+// RMS: y = x / sqrt(mean(x^2) + eps) * gamma (gamma NULL: ones), no mean, no shift.
+template <int D, bool RMS>
 __global__ __launch_bounds__(256) void ln_rows_kernel(LnArgs a) {
   constexpr int PER = D / 64;          // features per lane
   static_assert(D % 512 == 0, "row width");
@@ -353,11 +367,14 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(LnArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[c * 8 + i] = static_cast<float>(v[i]);
   }
-  float s = 0.f;
+  float mean = 0.f;
+  if (!RMS) {
+    float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) s += x[i];
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  const float mean = s * (1.0f / D);
+    for (int i = 0; i < PER; ++i) s += x[i];
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    mean = s * (1.0f / D);
+  }
   float q = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -376,7 +393,11 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(LnArgs a) {
     bf16x8_t out;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float y = (x[c * 8 + i] - mean) * rstd * a.gamma[f0 + i] + a.beta[f0 + i];
+      float y;
+      if (RMS)
+        y = x[c * 8 + i] * rstd * (a.gamma ? a.gamma[f0 + i] : 1.0f);
+      else
+        y = (x[c * 8 + i] - mean) * rstd * a.gamma[f0 + i] + a.beta[f0 + i];
       if (gp) y *= static_cast<float>(gv[i]);
       out[i] = static_cast<__bf16>(y);
     }
@@ -403,8 +424,8 @@ hipError_t launch_gemm_epi(const GemmArgs& g, int splits, hipStream_t stream) {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& g, int epi, bool a_kmajor, bool b_kmajor, int splits, hipStream_t stream) {
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+namespace {
+hipError_t check_gemm(const GemmArgs& g, int epi, bool a_kmajor, bool b_kmajor, int splits) {
   // a row-major operand steps through K in whole stages; K-major ones take any K
   if ((!a_kmajor || !b_kmajor) && g.K % GBK != 0) return hipErrorInvalidValue;
   if (splits < 1 || (splits > 1 && epi != kEpiF32) || g.K <= 0) return hipErrorInvalidValue;
@@ -417,6 +438,14 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, bool a_kmajor, bool b_kmajor,
   }
   if (epi == kEpiResidual && (g.ldr % 8 != 0 || !aligned(g.r, 16))) return hipErrorInvalidValue;
   if (epi == kEpiSiluPair && (g.ldc2 % 8 != 0 || !aligned(g.c2, 16))) return hipErrorInvalidValue;
+  if (g.group_m < 0) return hipErrorInvalidValue;
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& g, int epi, bool a_kmajor, bool b_kmajor, int splits, hipStream_t stream) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (hipError_t e = check_gemm(g, epi, a_kmajor, b_kmajor, splits); e != hipSuccess) return e;
   TimedScope timed(epi == kEpiResidual ? kTimedGemmOut : kTimedGemmUvqk, stream);
   if (!a_kmajor && !b_kmajor) {
     switch (epi) {
@@ -436,15 +465,34 @@ hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream) {
   return launch_gemm(g, epi, false, false, 1, stream);
 }
 
+hipError_t launch_head_gemm(const GemmArgs& g, hipStream_t stream) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (hipError_t e = check_gemm(g, kEpiNone, false, false, 1); e != hipSuccess) return e;
+  TimedScope timed(kTimedHeadGemm, stream);
+  return launch_gemm_epi<kEpiNone, false, false>(g, 1, stream);
+}
+
+hipError_t launch_rms_rows(const LnArgs& a, int width, hipStream_t stream) {
+  if (a.rows <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((a.rows + 3) / 4));
+  TimedScope timed(kTimedRmsNorm, stream);
+  switch (width) {
+    case 512: hipLaunchKernelGGL((ln_rows_kernel<512, true>), grid, dim3(256), 0, stream, a); break;
+    case 1024: hipLaunchKernelGGL((ln_rows_kernel<1024, true>), grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_ln_rows(const LnArgs& a, int width, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((a.rows + 3) / 4));
   TimedScope timed(kTimedLayerNorm, stream);
   switch (width) {
-    case 512: hipLaunchKernelGGL(ln_rows_kernel<512>, grid, dim3(256), 0, stream, a); break;
-    case 1024: hipLaunchKernelGGL(ln_rows_kernel<1024>, grid, dim3(256), 0, stream, a); break;
-    case 2048: hipLaunchKernelGGL(ln_rows_kernel<2048>, grid, dim3(256), 0, stream, a); break;
-    case 4096: hipLaunchKernelGGL(ln_rows_kernel<4096>, grid, dim3(256), 0, stream, a); break;
+    case 512: hipLaunchKernelGGL((ln_rows_kernel<512, false>), grid, dim3(256), 0, stream, a); break;
+    case 1024: hipLaunchKernelGGL((ln_rows_kernel<1024, false>), grid, dim3(256), 0, stream, a); break;
+    case 2048: hipLaunchKernelGGL((ln_rows_kernel<2048, false>), grid, dim3(256), 0, stream, a); break;
+    case 4096: hipLaunchKernelGGL((ln_rows_kernel<4096, false>), grid, dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

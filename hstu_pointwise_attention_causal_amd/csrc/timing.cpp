@@ -12,7 +12,8 @@ namespace hstu {
 namespace {
 
 const char* const kNames[kNumTimed] = {"attn_fwd", "attn_bwd_kv", "attn_bwd_q",
-                                       "layer_gemm_uvqk", "layer_gemm_out", "layer_norm", "attn_cand"};
+                                       "layer_gemm_uvqk", "layer_gemm_out", "layer_norm", "attn_cand",
+                                       "head_rms_norm", "head_gemm"};
 
 struct Pending {
   int kernel;

@@ -16,6 +16,8 @@ enum TimedKernel : int {
   kTimedGemmOut,
   kTimedLayerNorm,
   kTimedAttnCand,
+  kTimedRmsNorm,
+  kTimedHeadGemm,
   kNumTimed
 };
 

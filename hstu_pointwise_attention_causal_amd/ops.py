@@ -284,6 +284,39 @@ def layer_bwd(x: torch.Tensor, d_out: torch.Tensor, seq_offsets: torch.Tensor,
     return dx, {k: grads[k] for k in shapes}
 
 
+def head_workspace_size(rows: int, dim: int) -> int:
+    """hstu_head_workspace_size: workspace bytes of head_fwd."""
+    need = _lib._SZ(0)
+    _lib.check(_lib.load().hstu_head_workspace_size(int(rows), int(dim), ctypes.byref(need)))
+    return int(need.value)
+
+
+def head_fwd(x: torch.Tensor, table: torch.Tensor, *, gamma: Optional[torch.Tensor] = None,
+             eps: float = 1e-6, out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """hstu_head_fwd: bf16 logits [rows, vocab] = RMSNorm(x; gamma, eps)
+    table^T for token rows x [rows, dim] and an item table [vocab, dim] (the
+    token-embedding table when the head's weights are tied)."""
+    lib = _lib.load()
+    if x.dim() != 2 or table.dim() != 2 or x.shape[1] != table.shape[1]:
+        raise ValueError("x [rows, dim] and table [vocab, dim] must share dim")
+    if x.stride(1) != 1 or table.stride(1) != 1:
+        raise ValueError("x and table rows must be contiguous")
+    rows, dim = x.shape
+    vocab = table.shape[0]
+    if out is None:
+        out = torch.empty((rows, vocab), dtype=torch.bfloat16, device=x.device)
+    if out.dim() != 2 or out.shape[0] != rows or out.shape[1] != vocab or out.stride(1) != 1:
+        raise ValueError("out must be [rows, vocab] with contiguous rows")
+    need = head_workspace_size(rows, dim)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _lib.check(lib.hstu_head_fwd(rows, dim, vocab, float(eps), _ptr(x), x.stride(0), _ptr(gamma),
+                                 _ptr(table), table.stride(0), _ptr(out), out.stride(0),
+                                 _ptr(workspace), workspace.numel(), _stream_handle(x.device)))
+    return out
+
+
 def timing_enable(enable: bool = True) -> None:
     """hstu_timing_enable: bracket every timed kernel launch with HIP events."""
     _lib.check(_lib.load().hstu_timing_enable(int(bool(enable))))

@@ -256,6 +256,40 @@ hstu_status_t hstu_layer_bwd(const hstu_layer_params_t* params, const hstu_jagge
                              void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * hstu_head_workspace_size -- device workspace bytes for hstu_head_fwd
+ * (rows x dim bf16: the normalised rows).
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_head_workspace_size(int64_t rows, int32_t dim, size_t* bytes);
+
+/* ---------------------------------------------------------------------------
+ * hstu_head_fwd -- catalogue logits of the retrieval head over token rows
+ * (neurarch HSTU model card: structure rows "RMSNorm" and "Retrieval Head";
+ * the graph JSON's norm node, eps 1e-6, and head node, tied weights; the
+ * exported code's bias-free linear map):
+ *   Y = X / sqrt(mean over the dim features of X^2 + eps) * gamma
+ *   logits[t, i] = sum_d Y[t, d] table[i, d]     (Y rounded to bf16)
+ *   rows, dim: token rows and features (dim 512 or 1024 built).
+ *   vocab: items scored, a multiple of 8.
+ *   x: bf16 [rows, dim], row stride ldx elements.
+ *   gamma: fp32 [dim], or NULL for ones.
+ *   table: bf16 [vocab, dim], row stride ldt: the item table -- with tied
+ *     weights, the token-embedding table itself.
+ *   logits: bf16 [rows, vocab], row stride ldl >= vocab; must not overlap x,
+ *     gamma or the table.
+ *   workspace: at least hstu_head_workspace_size(rows, dim) bytes, not
+ *     overlapping any argument.
+ * Pointers are device pointers, 16-byte aligned; row strides are multiples
+ * of 8 elements. Nothing is allocated. rows or vocab 0: nothing is launched.
+ * Errors: HSTU_E_NULL, HSTU_E_SHAPE, HSTU_E_ALIGN, HSTU_E_ALIAS,
+ * HSTU_E_WORKSPACE, HSTU_E_UNSUPPORTED (dim not built, vocab not a multiple
+ * of 8, rows or vocab at or above 2^31), HSTU_E_HIP (a launch failed).
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_head_fwd(int64_t rows, int32_t dim, int64_t vocab, float eps,
+                            const void* x, int64_t ldx, const float* gamma,
+                            const void* table, int64_t ldt, void* logits, int64_t ldl,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Kernel timing for measurement tools. While enabled (process-wide), every
  * launch of a timed kernel is bracketed by two HIP events recorded on the
  * caller's stream, which adds a small gap between launches; off by default.
@@ -263,7 +297,8 @@ hstu_status_t hstu_layer_bwd(const hstu_layer_params_t* params, const hstu_jagge
  * number of launches of `kernel` and their summed duration in milliseconds
  * since the last read of that kernel, and resets that kernel's totals.
  * Kernel names: "attn_fwd", "attn_bwd_kv", "attn_bwd_q", "layer_gemm_uvqk",
- * "layer_gemm_out", "layer_norm". Host pointers. Errors: HSTU_E_NULL,
+ * "layer_gemm_out", "layer_norm", "attn_cand", "head_rms_norm", "head_gemm".
+ * Host pointers. Errors: HSTU_E_NULL,
  * HSTU_E_SHAPE (unknown name), HSTU_E_HIP (an event failed).
  * ------------------------------------------------------------------------- */
 hstu_status_t hstu_timing_enable(int enable);

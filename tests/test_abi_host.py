@@ -141,3 +141,29 @@ def test_backward_workspace_adds_bias_partials(lib):
     # one row of 128 position + 64 time slots per (head, key tile)
     tiles = (24321 + 32 * 127) // 128
     assert bwd.value >= fwd.value + 4 * 4 * tiles * (128 + 64)
+
+
+FAKE_X, FAKE_TABLE, FAKE_LOGITS, FAKE_HWS = 0x1000000, 0x2000000, 0x10000000, 0x3000000
+
+
+def _head(lib, rows=300, dim=512, vocab=1000, eps=1e-6, x=FAKE_X, ldx=512, gamma=None, table=FAKE_TABLE,
+          ldt=512, logits=FAKE_LOGITS, ldl=1000, ws=FAKE_HWS, wsb=0):
+    return lib.load().hstu_head_fwd(rows, dim, vocab, eps, x, ldx, gamma, table, ldt, logits, ldl, ws, wsb, None)
+
+
+def test_head_rejections(lib):
+    assert _head(lib, dim=256) == 5                                  # width not built
+    assert _head(lib, vocab=1004, ldl=1008) == 5                              # vocab not a multiple of 8
+    assert _head(lib, x=None) == 1                                   # NULL x
+    assert _head(lib, ldx=500) == 2                                  # stride below the width
+    assert _head(lib, ldl=999) == 2                                  # logits stride below vocab
+    assert _head(lib, eps=-1.0) == 2                                 # negative eps
+    assert _head(lib, table=FAKE_TABLE + 8) == 4                     # misaligned table
+    assert _head(lib, ldt=520 + 4) == 4                              # stride not a multiple of 8
+    assert _head(lib, logits=FAKE_X + 1024) == 7                     # logits overlap x
+    assert _head(lib) == 6                                           # workspace too small
+    need = ctypes.c_size_t(0)
+    assert lib.load().hstu_head_workspace_size(300, 512, ctypes.byref(need)) == 0
+    assert need.value == 300 * 512 * 2
+    assert _head(lib, ws=FAKE_LOGITS + 64, wsb=need.value) == 7      # workspace overlaps logits
+    assert _head(lib, rows=0) == 0 and _head(lib, vocab=0) == 0      # nothing to do, nothing launched

@@ -146,6 +146,7 @@ class Workload:
     ln_eps: float = 1e-6
     note: str = ""
     cand: Optional[dict] = None               # candidate scoring: offsets, q, k, v, timestamps
+    head: Optional[dict] = None               # retrieval head: table [V, D], gamma [D] or None, eps
 
     @property
     def num_seqs(self) -> int:
@@ -298,6 +299,26 @@ def _cand_recipe(name, seed, *, lengths=None, draw_lengths=None, cands=1024, H=4
                     note=note, cand=dict(offsets=coff, q=qc, k=kc, v=vc, timestamps=ts_c))
 
 
+def _head_recipe(name, seed, *, rows, D=512, vocab=VOCAB, gamma=False, eps=1e-6, note=""):
+    """Final RMSNorm + tied retrieval head inputs.
+
+    Draw order: per-row scales log-uniform in [0.01, 10], token rows x =
+    scale * N(0, 1) (the last block's output, whose scale the norm removes),
+    the item table ~ N(0, 0.02) (the token-embedding table's recipe; with
+    tied weights it is that table), [gamma ~ 1 + N(0, 0.1)]. x and the
+    table are rounded to bf16. Without gamma the norm keeps its initial
+    weight (ones).
+    """
+    rng = np.random.default_rng(seed)
+    scale = np.exp(rng.uniform(np.log(0.01), np.log(10.0), size=(rows, 1))).astype(np.float32)
+    x = round_to_bf16(scale * rng.standard_normal((rows, D), dtype=np.float32))
+    table = round_to_bf16(np.float32(0.02) * rng.standard_normal((vocab, D), dtype=np.float32))
+    g = (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32) if gamma else None
+    return Workload(name=name, kind="head", dtype="bf16", num_heads=0, dqk=0, dv=0,
+                    seq_offsets=np.array([0, rows], np.int64), x=x, embed_dim=D, ln_eps=eps,
+                    note=note, head=dict(table=table, gamma=g, eps=eps))
+
+
 def _c0(seed=0):
     """fp32 attention, one sequence n=256, H=2, d=32, q,k,v ~ N(0,1),
     64-bucket position table ~ N(0, 0.02), no time bias."""
@@ -355,6 +376,13 @@ WORKLOADS = {
     "c6_small": lambda seed=16: _cand_recipe(
         "c6_small", seed, lengths=[300, 0, 77, 1, 140], cands=[5, 3, 0, 130, 64], H=2, d=128,
         note="candidate scoring, ragged histories incl. empty and one-token, 0 to 130 candidates"),
+    # --- final RMSNorm + tied retrieval head over the stack's output rows ---
+    "c7": lambda seed=7: _head_recipe(
+        "c7", seed, rows=8192, D=512, vocab=VOCAB,
+        note="final RMSNorm + retrieval head: 8 x 1024 token rows, D 512, 200000 items"),
+    "c7_small": lambda seed=17: _head_recipe(
+        "c7_small", seed, rows=300, D=512, vocab=1000, gamma=True,
+        note="final RMSNorm + retrieval head, ragged against the tiles: 300 rows, 1000 items"),
     "c5_small": lambda seed=15: _layer_recipe(
         "c5_small", seed, draw_lengths=(1, 500, 7), num_layers=1, time=True, backward=True,
         note="one layer forward + backward, 7 ragged sequences"),
