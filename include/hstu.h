@@ -263,9 +263,10 @@ hstu_status_t hstu_head_workspace_size(int64_t rows, int32_t dim, size_t* bytes)
 
 /* ---------------------------------------------------------------------------
  * hstu_head_fwd -- catalogue logits of the retrieval head over token rows
- * (neurarch HSTU model card: structure rows "RMSNorm" and "Retrieval Head";
- * the graph JSON's norm node, eps 1e-6, and head node, tied weights; the
- * exported code's bias-free linear map):
+ * (neurarch HSTU model card, section "Structure": rows "RMSNorm" and
+ * "Retrieval Head", and its exported code's bias-free linear map; the
+ * neurarch graph JSON of the model: "norm" node, eps 1e-6, and "head" node,
+ * tied weights):
  *   Y = X / sqrt(mean over the dim features of X^2 + eps) * gamma
  *   logits[t, i] = sum_d Y[t, d] table[i, d]     (Y rounded to bf16)
  *   rows, dim: token rows and features (dim 512 or 1024 built).

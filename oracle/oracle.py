@@ -10,8 +10,12 @@ Sources, cited by page title and section:
   the per-head views, and the pointwise aggregation -- SiLU of q.k^T divided
   by the sequence length, lower-triangular (causal, diagonal kept) mask taken
   after the SiLU, then multiplied by v. No softmax.
-* neurarch model card, sections "Structure" and "Machine access" (graph
-  JSON): the final RMSNorm (eps 1e-6) and the tied, bias-free retrieval head.
+* neurarch model card, section "Structure", and the neurarch graph JSON of
+  the same model (its "norm" and "head" nodes): the final RMSNorm (eps 1e-6)
+  and the tied, bias-free retrieval head.
+* briansu.co explainer, section 6 "Why it works": Stochastic Length (random
+  shortening of long training histories) and M-FALCON (candidate scoring
+  with the history's keys and values reused).
 * briansu.co "HSTU: Hierarchical Sequential Transduction Units", section 3
   "How it works": the three steps of a layer (pointwise projection to
   U, V, Q, K; spatial aggregation by pointwise SiLU attention with relative
@@ -502,8 +506,9 @@ def rms_norm(x, gamma=None, eps: float = 1e-6) -> np.ndarray:
     """RMSNorm over the last axis, float64: x / sqrt(mean(x^2) + eps) * gamma.
 
     The norm between the last HSTU block and the head in the neurarch model
-    card (structure table row "RMSNorm", 512 features; the graph JSON's norm
-    node gives eps 1e-6; the exported code builds ``nn.RMSNorm(512)``). Unlike
+    card (structure table row "RMSNorm", 512 features; the exported code
+    builds ``nn.RMSNorm(512)``; the neurarch graph JSON's "norm" node gives
+    eps 1e-6). Unlike
     LayerNorm no mean is subtracted and there is no shift. gamma None means
     ones (the initial value)."""
     x = np.asarray(x, dtype=np.float64)
@@ -517,8 +522,43 @@ def head_fwd(x, table, gamma=None, eps: float = 1e-6) -> np.ndarray:
 
     The neurarch model card's head maps 512 features to 200000 item logits
     with a bias-free linear map (structure table row "Retrieval Head";
-    exported code ``nn.Linear(512, 200000, bias=False)``), and its graph JSON
-    marks the head's weights as tied, read here as: the [vocab, D] weight is
+    exported code ``nn.Linear(512, 200000, bias=False)``), and the neurarch
+    graph JSON's "head" node marks its weights as tied, read here as: the [vocab, D] weight is
     the token-embedding table itself. A subset of items is scored by passing
     those rows of the table."""
     return rms_norm(x, gamma, eps) @ _f64(table).T
+
+
+# ----------------------------------------------------------------------------
+# Stochastic Length
+# ----------------------------------------------------------------------------
+def stochastic_length(seq_offsets, keys, max_len: int):
+    """Random shortening of long histories (Stochastic Length, named in the
+    briansu.co explainer, section 6 "Why it works", as what makes training
+    cheap; the pages give no procedure, the reading here): a sequence of n <= max_len
+    tokens is kept whole; a longer one keeps a uniformly random subset of
+    max_len tokens in their original order. The randomness is passed in: one
+    32-bit key per token, and a sequence keeps the max_len tokens whose
+    (key, position in the sequence) pairs are smallest -- with independent
+    uniform keys, every max_len-subset is equally likely.
+
+    Returns (new_offsets int64 [B+1], gather_index int64 [T']): output token
+    r of the shortened batch is input token gather_index[r]."""
+    off = np.asarray(seq_offsets, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.uint32)
+    if max_len < 0:
+        raise ValueError("max_len must be >= 0")
+    new_off = [0]
+    picked = []
+    for b in range(off.size - 1):
+        s, e = int(off[b]), int(off[b + 1])
+        n = e - s
+        if n <= max_len:
+            keep = np.arange(n, dtype=np.int64)
+        else:
+            order = np.lexsort((np.arange(n), keys[s:e]))     # by key, then by position
+            keep = np.sort(order[:max_len]).astype(np.int64)
+        picked.append(s + keep)
+        new_off.append(new_off[-1] + keep.size)
+    idx = np.concatenate(picked) if picked else np.zeros(0, np.int64)
+    return np.asarray(new_off, np.int64), idx.astype(np.int64)

@@ -652,3 +652,72 @@ def test_tied_head_retrieves_each_token_own_item():
     logits = O.head_fwd(table[ids], table, None, 0.0)
     np.testing.assert_allclose(logits[np.arange(40), ids], math.sqrt(D) * r, rtol=1e-12)
     assert np.array_equal(logits.argmax(axis=1), ids)
+
+
+# ----------------------------------------------------------------------------
+# Stochastic Length
+# ----------------------------------------------------------------------------
+def _kept_by_counting(keys, s, e, L):
+    """Brute force: token i of [s, e) is kept iff fewer than L tokens of its
+    sequence have a smaller (key, position) pair."""
+    out = []
+    for i in range(s, e):
+        smaller = sum(1 for j in range(s, e) if (int(keys[j]), j) < (int(keys[i]), i))
+        if smaller < L:
+            out.append(i)
+    return out
+
+
+def test_stochastic_length_matches_pairwise_counting():
+    rng = np.random.default_rng(80)
+    lengths = [0, 1, 7, 8, 9, 30, 3, 64]
+    off = offsets_from_lengths(lengths)
+    keys = rng.integers(0, 1 << 32, size=int(off[-1]), dtype=np.uint64).astype(np.uint32)
+    keys[off[5]:off[6]] %= 4                     # heavy ties in one sequence
+    keys[off[7]:off[7] + 10] = 0xFFFFFFFF        # ties at the largest key
+    L = 8
+    new_off, idx = O.stochastic_length(off, keys, L)
+    assert np.array_equal(new_off, offsets_from_lengths(np.minimum(lengths, L)))
+    want = []
+    for b in range(len(lengths)):
+        want += _kept_by_counting(keys, int(off[b]), int(off[b + 1]), L)
+    assert np.array_equal(idx, np.array(want, np.int64))
+
+
+def test_stochastic_length_short_sequences_and_zero_cap():
+    off = offsets_from_lengths([3, 0, 5])
+    keys = np.arange(8, dtype=np.uint32)[::-1].copy()
+    new_off, idx = O.stochastic_length(off, keys, 5)
+    assert np.array_equal(new_off, off) and np.array_equal(idx, np.arange(8))
+    new_off, idx = O.stochastic_length(off, keys, 0)
+    assert np.array_equal(new_off, np.zeros(4, np.int64)) and idx.size == 0
+    # all keys equal: the first L positions of each long sequence
+    new_off, idx = O.stochastic_length(off, np.zeros(8, np.uint32), 2)
+    assert np.array_equal(idx, [0, 1, 3, 4])
+    # strictly decreasing keys: the last L positions
+    new_off, idx = O.stochastic_length(off, keys, 2)
+    assert np.array_equal(idx, [1, 2, 6, 7])
+
+
+def test_stochastic_length_is_a_uniform_subsample():
+    """Independent uniform keys: each of the n positions is kept with
+    probability L / n, and the kept set's first position follows the
+    hypergeometric minimum, P(first >= m) = C(n - m, L) / C(n, L)."""
+    rng = np.random.default_rng(81)
+    n, L, draws = 40, 10, 4000
+    off = np.array([0, n], np.int64)
+    counts = np.zeros(n)
+    firsts = np.zeros(n + 1)
+    for _ in range(draws):
+        keys = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+        _, idx = O.stochastic_length(off, keys, L)
+        assert idx.size == L and np.all(np.diff(idx) > 0)
+        counts[idx] += 1
+        firsts[idx[0]] += 1
+    p = L / n
+    sd = math.sqrt(p * (1 - p) / draws)
+    assert np.all(np.abs(counts / draws - p) < 5 * sd)
+    for m in (1, 3, 6):
+        exact = math.comb(n - m, L) / math.comb(n, L)
+        seen = firsts[m:].sum() / draws
+        assert abs(seen - exact) < 5 * math.sqrt(exact * (1 - exact) / draws), (m, seen, exact)
