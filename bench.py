@@ -19,7 +19,8 @@ Also on the line:
                 of one layer over the 64-sequence jagged batch, and the
                 attention forward + backward of the 32-sequence jagged batch, one
                 layer forward + backward, candidate scoring against cached
-                histories, and the final RMSNorm + tied retrieval head.
+                histories, the final RMSNorm + tied retrieval head, and
+                Stochastic Length (keyed selection + row gathers).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
     python bench.py --copy-calib      # plain copy of known size, for counter scaling
@@ -384,7 +385,51 @@ def secondary_head(hstu, name: str, steps: int, warmup: int, dev):
     }
 
 
-SECONDARY = ("layer_stack", "layer_jagged", "attn_fwd_bwd", "layer_fwd_bwd", "candidates", "head")
+def secondary_stochastic_length(hstu, name: str, steps: int, warmup: int, dev):
+    """Stochastic Length: one step = the keyed selection (new offsets and
+    gather index) plus the gathers of the kept token rows and timestamps.
+    Input tokens/s, and the step's algorithmic bytes (keys read once, index
+    written once and read by both gathers, rows and timestamps read and
+    written once) per second."""
+    import torch
+    from workloads import make_workload
+    wl = make_workload(name)
+    L = wl.sl["max_len"]
+    off = torch.from_numpy(wl.seq_offsets).to(dev)
+    keys = torch.from_numpy(wl.sl["keys"].view(np.int32)).to(dev)
+    x = torch.from_numpy(wl.x).to(dev).to(torch.bfloat16)
+    ts = torch.from_numpy(wl.timestamps).to(dev)
+    T = wl.total_tokens
+    new_off = torch.empty(wl.num_seqs + 1, dtype=torch.int64, device=dev)
+    idx = torch.empty(T, dtype=torch.int64, device=dev)
+    xo = torch.empty_like(x)
+    tso = torch.empty_like(ts)
+    count = new_off[-1:]
+
+    def step():
+        hstu.stochastic_length(off, keys, L, new_offsets=new_off, gather_index=idx)
+        hstu.gather_rows(x, idx, count, T, out=xo)
+        hstu.gather_rows(ts, idx, count, T, out=tso)
+
+    stream = torch.cuda.current_stream(dev)
+    ms_ev, ms_wall = time_steps(step, steps, warmup, stream)
+    ms = max(ms_ev, ms_wall)
+    kern = kernel_ms(hstu, step, steps, ["sl_select", "gather_rows"])
+    Tn = int(np.minimum(wl.lengths, L).sum())
+    row = wl.embed_dim * 2 + 8
+    nbytes = 4 * T + 8 * Tn + 2 * 8 * Tn + 2 * row * Tn
+    return {
+        "workload": f"{name}: {wl.note}",
+        "input_tokens_per_s": round(T / (ms * 1e-3), 1),
+        "kept_tokens": Tn,
+        "ms_per_step": round(ms, 5),
+        "algorithmic_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+        "kernel_ms": {k: (round(v, 5) if v else None) for k, v in kern.items()},
+    }
+
+
+SECONDARY = ("layer_stack", "layer_jagged", "attn_fwd_bwd", "layer_fwd_bwd", "candidates", "head",
+             "stochastic_length")
 
 
 def main():
@@ -483,6 +528,8 @@ def main():
             "candidates": lambda: secondary_candidates(hstu, "c6", max(5, args.steps // 2),
                                                        max(5, args.warmup // 4), dev),
             "head": lambda: secondary_head(hstu, "c7", max(5, args.steps // 4), max(5, args.warmup // 10), dev),
+            "stochastic_length": lambda: secondary_stochastic_length(hstu, "c8", args.steps,
+                                                                     max(5, args.warmup // 4), dev),
         }
         wanted = [w for w in args.secondary.split(",") if w]
         unknown = sorted(set(wanted) - set(runs))

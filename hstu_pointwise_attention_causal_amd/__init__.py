@@ -14,13 +14,16 @@ from .ops import (  # noqa: F401
     attn_fwd_candidates,
     attn_workspace_size,
     head_fwd,
+    gather_rows,
     head_workspace_size,
     layer_bwd,
     layer_fwd,
     make_layer_params,
+    stochastic_length,
     timing_enable,
     timing_read,
 )
 
 __all__ = ["HstuError", "load", "attn_fwd", "attn_fwd_candidates", "attn_bwd", "attn_workspace_size", "layer_fwd",
-           "layer_bwd", "head_fwd", "head_workspace_size", "make_layer_params", "timing_enable", "timing_read"]
+           "layer_bwd", "head_fwd", "head_workspace_size",
+           "stochastic_length", "gather_rows", "make_layer_params", "timing_enable", "timing_read"]

@@ -26,6 +26,7 @@ EXPORTED = (
     "hstu_layer_workspace_size", "hstu_layer_fwd",
     "hstu_layer_bwd_workspace_size", "hstu_layer_bwd",
     "hstu_head_workspace_size", "hstu_head_fwd",
+    "hstu_stochastic_length", "hstu_gather_rows",
     "hstu_timing_enable", "hstu_timing_read",
     "hstu_status_string", "hstu_last_error", "hstu_version",
 )
@@ -123,6 +124,10 @@ def load() -> ctypes.CDLL:
     lib.hstu_head_workspace_size.restype = c
     lib.hstu_head_fwd.argtypes = [_I64, c, _I64, ctypes.c_float, _P, _I64, _P, _P, _I64, _P, _I64, _P, _SZ, _P]
     lib.hstu_head_fwd.restype = c
+    lib.hstu_stochastic_length.argtypes = [c, _P, _I64, _I64, _P, _P, _P, _P]
+    lib.hstu_stochastic_length.restype = c
+    lib.hstu_gather_rows.argtypes = [_P, _P, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]
+    lib.hstu_gather_rows.restype = c
     lib.hstu_timing_enable.argtypes = [c]
     lib.hstu_timing_enable.restype = c
     lib.hstu_timing_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]

@@ -13,6 +13,7 @@
 #include "../../include/hstu.h"
 #include "launch.h"
 #include "layer.h"
+#include "stochastic_length.h"
 
 namespace {
 
@@ -757,6 +758,58 @@ hstu_status_t hstu_head_fwd(int64_t rows, int32_t dim, int64_t vocab, float eps,
   g.group_m = kHeadGroupRows;
   if ((e = hstu::launch_head_gemm(g, stream)) != hipSuccess) return hip_fail(e, "head GEMM launch");
   return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Stochastic Length and row gathers
+// ---------------------------------------------------------------------------
+hstu_status_t hstu_stochastic_length(int32_t num_seqs, const int64_t* seq_offsets, int64_t total_tokens,
+                                     int64_t max_len, const uint32_t* keys, int64_t* new_offsets,
+                                     int64_t* gather_index, void* hip_stream) {
+  if (num_seqs < 0 || total_tokens < 0) return fail(HSTU_E_SHAPE, "negative num_seqs or total_tokens");
+  if (max_len < 0) return fail(HSTU_E_SHAPE, "max_len must be >= 0");
+  if (total_tokens >= (int64_t(1) << 31)) return fail(HSTU_E_UNSUPPORTED, "total_tokens must be below 2^31");
+  if (!new_offsets) return fail(HSTU_E_NULL, "new_offsets is NULL");
+  if (num_seqs > 0 && !seq_offsets) return fail(HSTU_E_NULL, "seq_offsets is NULL");
+  if (total_tokens > 0 && (!keys || !gather_index)) return fail(HSTU_E_NULL, "keys or gather_index is NULL");
+  if ((reinterpret_cast<uintptr_t>(new_offsets) | reinterpret_cast<uintptr_t>(gather_index) |
+       reinterpret_cast<uintptr_t>(seq_offsets)) & 7u || reinterpret_cast<uintptr_t>(keys) & 3u)
+    return fail(HSTU_E_ALIGN, "offsets and gather_index must be 8-byte aligned, keys 4-byte aligned");
+  const Range ro = view_range(new_offsets, 1, num_seqs + 1, num_seqs + 1, 8);
+  const Range ri = view_range(gather_index, 1, total_tokens, total_tokens, 8);
+  const Range ins[] = {view_range(seq_offsets, 1, num_seqs + 1, num_seqs + 1, 8),
+                       view_range(keys, 1, total_tokens, total_tokens, 4)};
+  for (const Range& r : ins)
+    if (overlaps(ro, r) || overlaps(ri, r)) return fail(HSTU_E_ALIAS, "an output overlaps seq_offsets or keys");
+  if (overlaps(ro, ri)) return fail(HSTU_E_ALIAS, "new_offsets overlaps gather_index");
+  hstu::SlArgs a{};
+  a.seq_offsets = seq_offsets; a.total_tokens = total_tokens; a.num_seqs = num_seqs; a.max_len = max_len;
+  a.keys = keys; a.new_offsets = new_offsets; a.gather_index = gather_index;
+  const hipError_t e = hstu::launch_stochastic_length(a, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "stochastic length launch");
+}
+
+hstu_status_t hstu_gather_rows(const int64_t* index, const int64_t* count, int64_t max_rows, const void* src,
+                               int64_t src_rows, int64_t src_stride, void* dst, int64_t dst_stride,
+                               int64_t row_bytes, void* hip_stream) {
+  if (max_rows < 0 || src_rows < 0 || row_bytes < 0) return fail(HSTU_E_SHAPE, "negative size");
+  if (max_rows == 0 || row_bytes == 0) return ok();
+  if (!index || !count || !dst || (src_rows > 0 && !src)) return fail(HSTU_E_NULL, "a pointer is NULL");
+  if (src_stride < row_bytes || dst_stride < row_bytes) return fail(HSTU_E_SHAPE, "a row stride is below row_bytes");
+  const auto al4 = [](int64_t v) { return (v & 3) == 0; };
+  if (!al4(static_cast<int64_t>(reinterpret_cast<uintptr_t>(src))) ||
+      !al4(static_cast<int64_t>(reinterpret_cast<uintptr_t>(dst))) || !al4(src_stride) || !al4(dst_stride) ||
+      !al4(row_bytes) || (reinterpret_cast<uintptr_t>(index) & 7u) || (reinterpret_cast<uintptr_t>(count) & 7u))
+    return fail(HSTU_E_ALIGN, "rows, strides and bases must be 4-byte aligned; index and count 8-byte aligned");
+  const Range rd = view_range(dst, max_rows, dst_stride, row_bytes, 1);
+  if (overlaps(rd, view_range(src, src_rows, src_stride, row_bytes, 1)) ||
+      overlaps(rd, view_range(index, 1, max_rows, max_rows, 8)) || overlaps(rd, view_range(count, 1, 1, 1, 8)))
+    return fail(HSTU_E_ALIAS, "dst overlaps src, index or count");
+  hstu::GatherArgs g{};
+  g.index = index; g.count = count; g.max_rows = max_rows; g.src_rows = src_rows; g.src = src;
+  g.src_stride = src_stride; g.dst = dst; g.dst_stride = dst_stride; g.row_bytes = row_bytes;
+  const hipError_t e = hstu::launch_gather_rows(g, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "row gather launch");
 }
 
 const char* hstu_status_string(hstu_status_t s) {

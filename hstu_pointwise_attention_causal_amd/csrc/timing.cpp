@@ -13,7 +13,7 @@ namespace {
 
 const char* const kNames[kNumTimed] = {"attn_fwd", "attn_bwd_kv", "attn_bwd_q",
                                        "layer_gemm_uvqk", "layer_gemm_out", "layer_norm", "attn_cand",
-                                       "head_rms_norm", "head_gemm"};
+                                       "head_rms_norm", "head_gemm", "sl_select", "gather_rows"};
 
 struct Pending {
   int kernel;

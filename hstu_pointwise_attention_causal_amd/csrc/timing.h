@@ -18,6 +18,8 @@ enum TimedKernel : int {
   kTimedAttnCand,
   kTimedRmsNorm,
   kTimedHeadGemm,
+  kTimedSlSelect,
+  kTimedGather,
   kNumTimed
 };
 

@@ -317,6 +317,49 @@ def head_fwd(x: torch.Tensor, table: torch.Tensor, *, gamma: Optional[torch.Tens
     return out
 
 
+def stochastic_length(seq_offsets: torch.Tensor, keys: torch.Tensor, max_len: int, *,
+                      new_offsets: Optional[torch.Tensor] = None,
+                      gather_index: Optional[torch.Tensor] = None):
+    """hstu_stochastic_length: (new_offsets int64 [B+1], gather_index int64
+    [T]) for int64 offsets [B+1] and one uint32 key per token (held in an
+    int32 tensor, bit for bit). Only the first new_offsets[-1] entries of
+    gather_index are written; nothing here waits for the device."""
+    lib = _lib.load()
+    if seq_offsets.dtype != torch.int64 or keys.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("seq_offsets must be int64 and keys 32-bit")
+    B, T = seq_offsets.numel() - 1, keys.numel()
+    if new_offsets is None:
+        new_offsets = torch.empty(B + 1, dtype=torch.int64, device=keys.device)
+    if gather_index is None:
+        gather_index = torch.empty(max(T, 1), dtype=torch.int64, device=keys.device)
+    if new_offsets.numel() < B + 1 or gather_index.numel() < T:
+        raise ValueError("new_offsets needs B+1 entries and gather_index T")
+    _lib.check(lib.hstu_stochastic_length(B, _ptr(seq_offsets), T, int(max_len), _ptr(keys), _ptr(new_offsets),
+                                          _ptr(gather_index), _stream_handle(keys.device)))
+    return new_offsets, gather_index
+
+
+def gather_rows(src: torch.Tensor, index: torch.Tensor, count: torch.Tensor, max_rows: int, *,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """hstu_gather_rows: out[r] = src[index[r]] for r < min(count, max_rows),
+    count a one-element int64 device tensor (e.g. new_offsets[-1:]). Rows are
+    src's first axis; each row must be contiguous."""
+    lib = _lib.load()
+    if count.dtype != torch.int64 or index.dtype != torch.int64:
+        raise ValueError("index and count must be int64")
+    row_shape = tuple(src.shape[1:])
+    if out is None:
+        out = torch.empty((max_rows,) + row_shape, dtype=src.dtype, device=src.device)
+    row_bytes = src[0:1].numel() * src.element_size() if src.shape[0] else \
+        int(torch.tensor(row_shape).prod()) * src.element_size()
+    if src.dim() > 1 and not src[0:1].is_contiguous() or out.dim() > 1 and not out[0:1].is_contiguous():
+        raise ValueError("rows must be contiguous")
+    _lib.check(lib.hstu_gather_rows(_ptr(index), _ptr(count), int(max_rows), _ptr(src), src.shape[0],
+                                    src.stride(0) * src.element_size(), _ptr(out),
+                                    out.stride(0) * out.element_size(), row_bytes, _stream_handle(src.device)))
+    return out
+
+
 def timing_enable(enable: bool = True) -> None:
     """hstu_timing_enable: bracket every timed kernel launch with HIP events."""
     _lib.check(_lib.load().hstu_timing_enable(int(bool(enable))))

@@ -291,6 +291,50 @@ hstu_status_t hstu_head_fwd(int64_t rows, int32_t dim, int64_t vocab, float eps,
                             void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * hstu_stochastic_length -- random shortening of long training histories
+ * (Stochastic Length: briansu.co explainer, section 6 "Why it works"; the
+ * pages give no procedure, the reading here): a sequence of n <= max_len
+ * tokens is kept whole; a longer one keeps the max_len tokens whose
+ * (key, position in the sequence) pairs are smallest, in their original
+ * order. With independent uniform keys that is a uniformly random subset.
+ *   num_seqs, seq_offsets: the input batch (device int64 [B+1]); offsets are
+ *     clamped to [0, total_tokens] and made non-decreasing on read.
+ *   total_tokens: T (host), the tokens that keys and gather_index cover.
+ *   keys: device uint32 [T], one random key per token (drawn by the caller).
+ *   new_offsets: device int64 [B+1], overwritten with the shortened batch's
+ *     offsets (new_offsets[B] = T', the kept tokens).
+ *   gather_index: device int64 [T] capacity; entry r < T' is the input token
+ *     of output token r; entries from T' on are not written.
+ * Outputs must not overlap the inputs or each other. Deterministic: the
+ * result depends on the keys alone. Nothing is allocated.
+ * Errors: HSTU_E_NULL, HSTU_E_SHAPE (negative sizes), HSTU_E_ALIGN (offsets
+ * and gather_index 8-byte, keys 4-byte), HSTU_E_ALIAS, HSTU_E_UNSUPPORTED
+ * (T >= 2^31), HSTU_E_HIP.
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_stochastic_length(int32_t num_seqs, const int64_t* seq_offsets, int64_t total_tokens,
+                                     int64_t max_len, const uint32_t* keys, int64_t* new_offsets,
+                                     int64_t* gather_index, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * hstu_gather_rows -- dst row r = src row index[r] for r < min(*count,
+ * max_rows): moves a batch's per-token rows (embeddings, timestamps, ids)
+ * into the shortened batch of hstu_stochastic_length.
+ *   index: device int64 (e.g. its gather_index). count: device int64, the
+ *     rows to copy (e.g. new_offsets + num_seqs), read by the kernel so the
+ *     host need not wait for it. max_rows: host bound on the rows copied.
+ *   src [src_rows rows of row_bytes, stride src_stride bytes]; rows whose
+ *     index lies outside [0, src_rows) are left unwritten.
+ *   dst [max_rows rows, stride dst_stride bytes]; must not overlap src,
+ *     index or count.
+ * Bases, strides and row_bytes 4-byte aligned (16-byte alignment takes the
+ * widest copies); index and count 8-byte aligned. Nothing is allocated.
+ * Errors: HSTU_E_NULL, HSTU_E_SHAPE, HSTU_E_ALIGN, HSTU_E_ALIAS, HSTU_E_HIP.
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_gather_rows(const int64_t* index, const int64_t* count, int64_t max_rows, const void* src,
+                               int64_t src_rows, int64_t src_stride, void* dst, int64_t dst_stride,
+                               int64_t row_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Kernel timing for measurement tools. While enabled (process-wide), every
  * launch of a timed kernel is bracketed by two HIP events recorded on the
  * caller's stream, which adds a small gap between launches; off by default.
@@ -298,7 +342,8 @@ hstu_status_t hstu_head_fwd(int64_t rows, int32_t dim, int64_t vocab, float eps,
  * number of launches of `kernel` and their summed duration in milliseconds
  * since the last read of that kernel, and resets that kernel's totals.
  * Kernel names: "attn_fwd", "attn_bwd_kv", "attn_bwd_q", "layer_gemm_uvqk",
- * "layer_gemm_out", "layer_norm", "attn_cand", "head_rms_norm", "head_gemm".
+ * "layer_gemm_out", "layer_norm", "attn_cand", "head_rms_norm", "head_gemm",
+ * "sl_select", "gather_rows".
  * Host pointers. Errors: HSTU_E_NULL,
  * HSTU_E_SHAPE (unknown name), HSTU_E_HIP (an event failed).
  * ------------------------------------------------------------------------- */

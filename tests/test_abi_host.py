@@ -167,3 +167,26 @@ def test_head_rejections(lib):
     assert need.value == 300 * 512 * 2
     assert _head(lib, ws=FAKE_LOGITS + 64, wsb=need.value) == 7      # workspace overlaps logits
     assert _head(lib, rows=0) == 0 and _head(lib, vocab=0) == 0      # nothing to do, nothing launched
+
+
+def test_stochastic_length_and_gather_rejections(lib):
+    c = lib.load()
+    OFF, KEYS, NOFF, IDX = 0x100000, 0x200000, 0x300000, 0x400000
+    sl = c.hstu_stochastic_length
+    assert sl(-1, OFF, 10, 4, KEYS, NOFF, IDX, None) == 2            # negative num_seqs
+    assert sl(2, OFF, 10, -1, KEYS, NOFF, IDX, None) == 2            # negative cap
+    assert sl(2, OFF, 1 << 31, 4, KEYS, NOFF, IDX, None) == 5        # too many tokens
+    assert sl(2, None, 10, 4, KEYS, NOFF, IDX, None) == 1            # NULL offsets
+    assert sl(2, OFF, 10, 4, KEYS, None, IDX, None) == 1             # NULL new_offsets
+    assert sl(2, OFF, 10, 4, KEYS + 2, NOFF, IDX, None) == 4         # misaligned keys
+    assert sl(2, OFF, 10, 4, KEYS, NOFF, IDX + 4, None) == 4         # misaligned index
+    assert sl(2, OFF, 10, 4, KEYS, OFF + 8, IDX, None) == 7          # new_offsets overlaps offsets
+    assert sl(2, OFF, 10, 4, KEYS, NOFF, NOFF + 8, None) == 7        # the two outputs overlap
+    g = c.hstu_gather_rows
+    SRC, DST, CNT = 0x500000, 0x600000, 0x700000
+    assert g(IDX, CNT, -1, SRC, 10, 1024, DST, 1024, 1024, None) == 2  # negative rows
+    assert g(None, CNT, 4, SRC, 10, 1024, DST, 1024, 1024, None) == 1  # NULL index
+    assert g(IDX, CNT, 4, SRC, 10, 512, DST, 1024, 1024, None) == 2    # stride below row bytes
+    assert g(IDX, CNT, 4, SRC + 2, 10, 1024, DST, 1024, 1024, None) == 4  # misaligned src
+    assert g(IDX, CNT, 4, SRC, 10, 1024, SRC + 4096, 1024, 1024, None) == 7  # dst overlaps src
+    assert g(IDX, CNT, 0, SRC, 10, 1024, DST, 1024, 1024, None) == 0   # nothing to copy

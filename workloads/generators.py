@@ -147,6 +147,7 @@ class Workload:
     note: str = ""
     cand: Optional[dict] = None               # candidate scoring: offsets, q, k, v, timestamps
     head: Optional[dict] = None               # retrieval head: table [V, D], gamma [D] or None, eps
+    sl: Optional[dict] = None                 # Stochastic Length: keys uint32 [T], max_len
 
     @property
     def num_seqs(self) -> int:
@@ -319,6 +320,31 @@ def _head_recipe(name, seed, *, rows, D=512, vocab=VOCAB, gamma=False, eps=1e-6,
                     note=note, head=dict(table=table, gamma=g, eps=eps))
 
 
+def _sl_recipe(name, seed, *, lengths=None, draw_lengths=None, D=512, max_len=2048, ties=False, note=""):
+    """Stochastic Length inputs: a jagged training batch and one random key per token.
+
+    Draw order: [lengths], token rows x ~ N(0, 0.02) (bf16; the embedding
+    table's scale), timestamps, keys ~ U[0, 2^32). With ties, the first
+    sequence's keys keep only their top 4 bits (16 distinct values) and the
+    last sequence's are all 0xFFFFFFFF, so selection has to break ties.
+    """
+    rng = np.random.default_rng(seed)
+    if draw_lengths is not None:
+        lo, hi, count = draw_lengths
+        lengths = log_uniform_lengths(rng, count, lo, hi)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    off = offsets_from_lengths(lengths)
+    T = int(off[-1])
+    x = round_to_bf16(np.float32(0.02) * rng.standard_normal((T, D), dtype=np.float32))
+    ts = exponential_timestamps(rng, lengths)
+    keys = rng.integers(0, 1 << 32, size=T, dtype=np.uint64).astype(np.uint32)
+    if ties and lengths.size:
+        keys[off[0]:off[1]] >>= 28
+        keys[off[-2]:off[-1]] = 0xFFFFFFFF
+    return Workload(name=name, kind="sl", dtype="bf16", num_heads=0, dqk=0, dv=0, seq_offsets=off,
+                    timestamps=ts, x=x, embed_dim=D, note=note, sl=dict(keys=keys, max_len=int(max_len)))
+
+
 def _c0(seed=0):
     """fp32 attention, one sequence n=256, H=2, d=32, q,k,v ~ N(0,1),
     64-bucket position table ~ N(0, 0.02), no time bias."""
@@ -383,6 +409,13 @@ WORKLOADS = {
     "c7_small": lambda seed=17: _head_recipe(
         "c7_small", seed, rows=300, D=512, vocab=1000, gamma=True,
         note="final RMSNorm + retrieval head, ragged against the tiles: 300 rows, 1000 items"),
+    # --- Stochastic Length over a long-history training batch ---
+    "c8": lambda seed=8: _sl_recipe(
+        "c8", seed, draw_lengths=(64, 16384, 64), D=512, max_len=2048,
+        note="Stochastic Length: 64 sequences log-uniform in [64, 16384], D 512, cap 2048"),
+    "c8_small": lambda seed=18: _sl_recipe(
+        "c8_small", seed, lengths=[5000, 0, 1, 300, 299, 301, 77, 2049], D=512, max_len=300, ties=True,
+        note="Stochastic Length, cap 300: lengths around the cap, empty, one-token, tied keys"),
     "c5_small": lambda seed=15: _layer_recipe(
         "c5_small", seed, draw_lengths=(1, 500, 7), num_layers=1, time=True, backward=True,
         note="one layer forward + backward, 7 ragged sequences"),
