@@ -28,8 +28,7 @@ namespace hstu {
 
 namespace {
 
-constexpr int GBK = 64;            // K per stage
-constexpr int kChunks = GBK / 8;   // 16-byte chunks per tile row
+constexpr int GBK = 64;            // K per stage of K-major operands, and the K granularity of row-major ones
 
 __device__ __forceinline__ uint32_t clamp_u32(int64_t bytes) {
   return bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes));
@@ -43,12 +42,15 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 }
 
 // GEMM tile shape: BM x BN outputs per workgroup, WM x WN per wave
-// ((WM/32) x (WN/32) blocks of v_mfma_f32_32x32x16_bf16), `ST` K stages of 64
+// ((WM/32) x (WN/32) blocks of v_mfma_f32_32x32x16_bf16), `ST` K stages of BK
 // in LDS. AT / BT: the operand is stored K-major ([K][M] / [K][N], i.e. the
 // product uses its transpose); its stage tile is then 64 K-rows of BM (BN)
-// columns, read back with transposed LDS reads.
-template <int BM, int BN, int WM, int WN, int ST, bool AT, bool BT>
+// columns, read back with transposed LDS reads. BK = 32 (row-major operands
+// only) halves a stage, so twice as many stages fit and more loads stay in
+// flight when K is short.
+template <int BM, int BN, int WM, int WN, int ST, bool AT, bool BT, int BK = 64>
 struct GemmShape {
+  static constexpr int kBK = BK, kChunks = BK / 8;   // 16-byte chunks per row-major tile row
   static constexpr int kWavesM = BM / WM, kWavesN = BN / WN, kWaves = kWavesM * kWavesN;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int MB = WM / 32, NB = WN / 32;
@@ -62,16 +64,22 @@ struct GemmShape {
   static constexpr bool kAT = AT, kBT = BT;
   static_assert(kAInst % kWaves == 0 && kBInst % kWaves == 0, "loads spread evenly over the waves");
   static_assert(ST >= 2 && ST <= 4, "stages");
+  static_assert(BK == 64 || (BK == 32 && !AT && !BT), "K-major operands take 64-deep stages");
 };
 
-// Swizzle of the 16-byte chunks of one LDS row of a stage tile. Row-major
-// (K-contiguous) tiles: chunk ^ (row & 7), so the ds_read_b128 of 32
-// consecutive rows hits distinct banks. K-major tiles: chunk ^ (4 row mod CH),
-// so the transposed reads of 4 rows x 4 chunks per 16 lanes hit distinct banks.
+// Swizzle of the 16-byte chunks of one LDS row of a stage tile. The LDS
+// serves a ds_read_b128 16 lanes at a time from 64 four-byte banks (256
+// bytes), and the fragment reads give those 16 lanes 16 consecutive rows at
+// the same logical chunk. Row-major (K-contiguous) rows of 8 chunks (128 B,
+// two rows per 256 B): chunk ^ ((row >> 1) & 7) puts the 16 rows in 16
+// distinct bank slots; rows of 4 chunks (four per 256 B): chunk ^ ((row >> 2)
+// & 3). K-major tiles: chunk ^ (4 row mod CH) for the transposed reads of 4
+// rows x 4 chunks per 16 lanes.
 template <bool KMAJOR, int CH>
 __device__ __forceinline__ int stage_swizzle(int r) {
   if constexpr (KMAJOR) return (4 * r) & (CH - 1);
-  else return r & 7;
+  else if constexpr (CH == 4) return (r >> 2) & 3;
+  else return (r >> 1) & 7;
 }
 
 // Direct loads of one operand's stage tile: instruction i fills LDS slots
@@ -142,61 +150,87 @@ struct Frag {
   }
 };
 
-// One K step: MFMAs on stage (rs_a, rs_b) while the stage ST - 1 steps ahead
-// streams into (ds_a, ds_b), then wait for the next stage and synchronize.
-// All buffers arrive as __restrict__ pointers, so the compiler knows the reads
-// never touch the stage being filled and does not wait for the in-flight
-// loads before reading LDS.
+// The fragments of one 16-deep K slice of a stage: MB of op(A), NB of op(B).
+template <class S>
+struct FragSet {
+  bf16x8_t a[S::MB], b[S::NB];
+};
+
+template <class S>
+__device__ __forceinline__ void read_frags(FragSet<S>& f, const char* __restrict__ sa_, const char* __restrict__ sb_,
+                                           int k16, int lh, const Frag<S::kAT, S::ACH> (&af_)[S::MB],
+                                           const Frag<S::kBT, S::BCH> (&bf_)[S::NB]) {
+#pragma unroll
+  for (int mb = 0; mb < S::MB; ++mb) f.a[mb] = af_[mb].read(sa_, k16, lh);
+#pragma unroll
+  for (int nb = 0; nb < S::NB; ++nb) f.b[nb] = bf_[nb].read(sb_, k16, lh);
+}
+
+// One K step on stage (rs_a, rs_b), entered with the fragments of its first
+// 16-deep slice in `cur`. The loads of the stage ST - 1 steps ahead go into
+// (ds_a, ds_b) first. Each slice's MFMAs run while the next slice's fragments
+// are read: within the stage, or -- after waiting for the next stage
+// (nx_a, nx_b) to land and a barrier -- the next stage's first slice, so the
+// step leaves `cur` holding it. Scheduling fences keep the reads ahead of the
+// products they overlap (the compiler would otherwise sink each read to its
+// first use). All buffers arrive as __restrict__ pointers, so the compiler
+// knows the reads never touch the stage being filled.
 template <class S>
 __device__ __forceinline__ void gemm_step(const GemmArgs& g, const char* __restrict__ rs_a,
                                           const char* __restrict__ rs_b, char* __restrict__ ds_a,
-                                          char* __restrict__ ds_b, int kt, int nsteps, int kbase_elems, int k_end,
-                                          const char* abase, int arows, const char* bbase, int brows, int w,
-                                          int lane, const Frag<S::kAT, S::ACH> (&af_)[S::MB],
-                                          const Frag<S::kBT, S::BCH> (&bf_)[S::NB],
+                                          char* __restrict__ ds_b, const char* __restrict__ nx_a,
+                                          const char* __restrict__ nx_b, int kt, int nsteps, int kbase_elems,
+                                          int k_end, const char* abase, int arows, const char* bbase, int brows,
+                                          int w, int lane, const Frag<S::kAT, S::ACH> (&af_)[S::MB],
+                                          const Frag<S::kBT, S::BCH> (&bf_)[S::NB], FragSet<S>& cur,
                                           f32x16_t (&acc)[S::MB][S::NB]) {
   if (kt + S::kStagesAhead < nsteps) {
-    const int k0 = kbase_elems + (kt + S::kStagesAhead) * GBK;
+    const int k0 = kbase_elems + (kt + S::kStagesAhead) * S::kBK;
     issue_operand<S, S::kAT, S::ACH, S::kAPer>(operand_rsrc<S::kAT>(abase, g.lda, arows, arows, k0, k_end, g.K),
                                               g.lda, w, lane, ds_a);
     issue_operand<S, S::kBT, S::BCH, S::kBPer>(operand_rsrc<S::kBT>(bbase, g.ldb, brows, brows, k0, k_end, g.K),
                                               g.ldb, w, lane, ds_b);
   }
   const int lh = lane >> 5;
+  constexpr int KS = S::kBK / 16;
 #pragma unroll
-  for (int k16 = 0; k16 < 4; ++k16) {
-    bf16x8_t af[S::MB], bfr[S::NB];
-#pragma unroll
-    for (int mb = 0; mb < S::MB; ++mb) af[mb] = af_[mb].read(rs_a, k16, lh);
-#pragma unroll
-    for (int nb = 0; nb < S::NB; ++nb) bfr[nb] = bf_[nb].read(rs_b, k16, lh);
+  for (int k16 = 0; k16 < KS; ++k16) {
+    FragSet<S> nxt;
+    if (k16 + 1 < KS) {
+      read_frags<S>(nxt, rs_a, rs_b, k16 + 1, lh, af_, bf_);
+    } else {
+      // The next stage must have landed; the ones issued since may stay in flight.
+      asm volatile("" ::: "memory");
+      const int ahead = nsteps - 1 - (kt + 1);   // stages issued beyond the next one, capped below
+      if (ahead >= S::kStagesAhead - 1) {
+        if constexpr (S::kStagesAhead == 3) wait_vm_lgkm0<2 * S::kLoadsPerStage>();
+        else if constexpr (S::kStagesAhead == 2) wait_vm_lgkm0<S::kLoadsPerStage>();
+        else wait_vm_lgkm0<0>();
+      } else if (S::kStagesAhead == 3 && ahead == 1) {
+        wait_vm_lgkm0<S::kLoadsPerStage>();
+      } else {
+        wait_vm_lgkm0<0>();
+      }
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + 1 < nsteps) read_frags<S>(nxt, nx_a, nx_b, 0, lh, af_, bf_);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mb = 0; mb < S::MB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < S::NB; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[mb][nb], 0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[nb], cur.a[mb], acc[mb][nb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
   }
-  // The next stage must have landed; the ones issued since may stay in flight.
-  asm volatile("" ::: "memory");
-  const int ahead = nsteps - 1 - (kt + 1);   // stages issued beyond the next one, capped below
-  if (ahead >= S::kStagesAhead - 1) {
-    if constexpr (S::kStagesAhead == 3) wait_vm_lgkm0<2 * S::kLoadsPerStage>();
-    else if constexpr (S::kStagesAhead == 2) wait_vm_lgkm0<S::kLoadsPerStage>();
-    else wait_vm_lgkm0<0>();
-  } else if (S::kStagesAhead == 3 && ahead == 1) {
-    wait_vm_lgkm0<S::kLoadsPerStage>();
-  } else {
-    wait_vm_lgkm0<0>();
-  }
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
-template <int EPI, int BM, int BN, int WM, int WN, int ST, bool AT, bool BT>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_kernel(GemmArgs g) {
-  using S = GemmShape<BM, BN, WM, WN, ST, AT, BT>;
-  __shared__ __attribute__((aligned(16))) char sa[ST][BM * GBK * 2];
-  __shared__ __attribute__((aligned(16))) char sb[ST][BN * GBK * 2];
+template <int EPI, int BM, int BN, int WM, int WN, int ST, bool AT, bool BT, int BK>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 2) void gemm_kernel(GemmArgs g) {
+  using S = GemmShape<BM, BN, WM, WN, ST, AT, BT, BK>;
+  __shared__ __attribute__((aligned(16))) char sa[ST][BM * BK * 2];
+  __shared__ __attribute__((aligned(16))) char sb[ST][BN * BK * 2];
 
   // Workgroups are dealt to the 8 XCDs in turn (block b to XCD b % 8). Tile t
   // of the row-major tile order goes to a block on XCD t / ceil-share, so each
@@ -225,11 +259,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_kernel(Gem
   const int wm = w / S::kWavesN, wn = w % S::kWavesN;
 
   // K range of this split (blockIdx.y of gridDim.y); only K-major operands split K
-  const int ksteps_all = (g.K + GBK - 1) / GBK;
+  const int ksteps_all = (g.K + BK - 1) / BK;
   const int per = (ksteps_all + gridDim.y - 1) / gridDim.y;
   const int ks0 = blockIdx.y * per;
   const int nsteps = max(0, min(per, ksteps_all - ks0));
-  const int kbase_elems = ks0 * GBK, k_end = min(g.K, (ks0 + nsteps) * GBK);
+  const int kbase_elems = ks0 * BK, k_end = min(g.K, (ks0 + nsteps) * BK);
 
   // operand bases: row-major -> first row of the tile; K-major -> first column of the tile
   const char* abase = static_cast<const char*>(g.a) + (AT ? static_cast<int64_t>(m0) * 2 : static_cast<int64_t>(m0) * g.lda * 2);
@@ -253,21 +287,27 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_kernel(Gem
 #pragma unroll
   for (int s_ = 0; s_ < ST - 1; ++s_)
     if (s_ < nsteps) {
-      const int k0 = kbase_elems + s_ * GBK;
+      const int k0 = kbase_elems + s_ * BK;
       issue_operand<S, AT, S::ACH, S::kAPer>(operand_rsrc<AT>(abase, g.lda, arows, arows, k0, k_end, g.K), g.lda, w,
                                             lane, sa[s_]);
       issue_operand<S, BT, S::BCH, S::kBPer>(operand_rsrc<BT>(bbase, g.ldb, brows, brows, k0, k_end, g.K), g.ldb, w,
                                             lane, sb[s_]);
     }
-  wait_vm_lgkm0<0>();
+  // wait for stage 0 only; the later ones stay in flight
+  if (nsteps >= ST - 1) wait_vm_lgkm0<(ST - 2) * S::kLoadsPerStage>();
+  else wait_vm_lgkm0<0>();
   __syncthreads();
-  // stages rotate statically; step t reads stage t % ST and fills (t + ST - 1) % ST
+  // stages rotate statically; step t reads stage t % ST, fills (t + ST - 1) % ST
+  // and ends with the first fragments of stage (t + 1) % ST in registers
+  FragSet<S> cur;
+  if (nsteps > 0) read_frags<S>(cur, sa[0], sb[0], 0, lane >> 5, af_, bf_);
   for (int kt = 0; kt < nsteps; kt += ST) {
 #pragma unroll
     for (int u = 0; u < ST; ++u) {
       if (kt + u >= nsteps) break;
-      gemm_step<S>(g, sa[u], sb[u], sa[(u + ST - 1) % ST], sb[(u + ST - 1) % ST], kt + u, nsteps, kbase_elems,
-                   k_end, abase, arows, bbase, brows, w, lane, af_, bf_, acc);
+      gemm_step<S>(g, sa[u], sb[u], sa[(u + ST - 1) % ST], sb[(u + ST - 1) % ST], sa[(u + 1) % ST],
+                   sb[(u + 1) % ST], kt + u, nsteps, kbase_elems, k_end, abase, arows, bbase, brows, w, lane, af_,
+                   bf_, cur, acc);
     }
   }
 
@@ -408,10 +448,10 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(LnArgs a) {
 }  // namespace
 
 namespace {
-template <int EPI, int BM, int BN, int WM, int WN, int ST, bool AT, bool BT>
+template <int EPI, int BM, int BN, int WM, int WN, int ST, bool AT, bool BT, int BK = 64>
 hipError_t launch_gemm_shape(const GemmArgs& g, int splits, hipStream_t stream) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<EPI, BM, BN, WM, WN, ST, AT, BT>), dim3(tiles, splits),
+  hipLaunchKernelGGL((gemm_kernel<EPI, BM, BN, WM, WN, ST, AT, BT, BK>), dim3(tiles, splits),
                      dim3((BM / WM) * (BN / WN) * 64), 0, stream, g);
   return hipGetLastError();
 }
