@@ -330,10 +330,12 @@ def secondary_candidates(hstu, name: str, steps: int, warmup: int, dev):
     out = torch.empty_like(v)
     m = np.diff(c["offsets"])
     mmax = int(m.max())
+    ws = torch.empty(max(1, hstu.attn_cand_workspace_size(wl.num_heads, wl.dqk, wl.num_seqs, wl.total_tokens, mmax)),
+                     dtype=torch.uint8, device=dev)
 
     def step():
         hstu.attn_fwd_candidates(q, k, v, coff, kh, vh, hoff, timestamps=ts, cand_timestamps=cts,
-                                 pos_table=pt, time_table=tt, max_candidates=mmax, out=out)
+                                 pos_table=pt, time_table=tt, max_candidates=mmax, out=out, workspace=ws)
 
     stream = torch.cuda.current_stream(dev)
     ms_ev, ms_wall = time_steps(step, steps, warmup, stream)

@@ -10,6 +10,7 @@ or PyTorch fallback.
 from ._lib import HstuError, load  # noqa: F401
 from .ops import (  # noqa: F401
     attn_bwd,
+    attn_cand_workspace_size,
     attn_fwd,
     attn_fwd_candidates,
     attn_workspace_size,
@@ -24,6 +25,6 @@ from .ops import (  # noqa: F401
     timing_read,
 )
 
-__all__ = ["HstuError", "load", "attn_fwd", "attn_fwd_candidates", "attn_bwd", "attn_workspace_size", "layer_fwd",
+__all__ = ["HstuError", "load", "attn_fwd", "attn_fwd_candidates", "attn_cand_workspace_size", "attn_bwd", "attn_workspace_size", "layer_fwd",
            "layer_bwd", "head_fwd", "head_workspace_size",
            "stochastic_length", "gather_rows", "make_layer_params", "timing_enable", "timing_read"]

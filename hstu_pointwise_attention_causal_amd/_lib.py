@@ -22,7 +22,7 @@ STATUS_NAMES = {
 
 # Every function the header declares (checked against include/hstu.h by the CPU tests).
 EXPORTED = (
-    "hstu_attn_workspace_size", "hstu_attn_fwd", "hstu_attn_bwd", "hstu_attn_fwd_candidates",
+    "hstu_attn_workspace_size", "hstu_attn_fwd", "hstu_attn_bwd", "hstu_attn_fwd_candidates", "hstu_attn_cand_workspace_size",
     "hstu_layer_workspace_size", "hstu_layer_fwd",
     "hstu_layer_bwd_workspace_size", "hstu_layer_bwd",
     "hstu_head_workspace_size", "hstu_head_fwd",
@@ -110,7 +110,9 @@ def load() -> ctypes.CDLL:
                                   _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, _SZ, _P]
     lib.hstu_attn_bwd.restype = c
     lib.hstu_attn_fwd_candidates.argtypes = [_P, _P, _P, c, _P, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
-                                             _P, _I64, _P, _I64, _P]
+                                             _P, _I64, _P, _I64, _P, _SZ, _P]
+    lib.hstu_attn_cand_workspace_size.argtypes = [_P, _P, c, ctypes.POINTER(_SZ)]
+    lib.hstu_attn_cand_workspace_size.restype = c
     lib.hstu_attn_fwd_candidates.restype = c
     lib.hstu_layer_workspace_size.argtypes = [_P, _P, ctypes.POINTER(_SZ)]
     lib.hstu_layer_workspace_size.restype = c

@@ -279,11 +279,23 @@ hstu_status_t hstu_attn_bwd(const hstu_attn_desc_t* desc, const hstu_jagged_t* j
   return ok();
 }
 
+hstu_status_t hstu_attn_cand_workspace_size(const hstu_attn_desc_t* desc, const hstu_jagged_t* hist,
+                                            int32_t max_candidates, size_t* bytes) {
+  if (!bytes) return fail(HSTU_E_NULL, "bytes is NULL");
+  if (!desc || !hist) return fail(HSTU_E_NULL, "descriptor or history batch is NULL");
+  if (hist->num_seqs < 0 || hist->total_tokens < 0 || max_candidates < 0 || desc->num_heads < 1)
+    return fail(HSTU_E_SHAPE, "negative sizes or no heads");
+  *bytes = hstu::cand_workspace_bytes(hist->total_tokens, hist->num_seqs, max_candidates, desc->num_heads,
+                                      desc->dqk);
+  return ok();
+}
+
 hstu_status_t hstu_attn_fwd_candidates(const hstu_attn_desc_t* desc, const hstu_jagged_t* hist,
                                        const hstu_jagged_t* cand, int32_t max_candidates, const hstu_bias_t* bias,
                                        const void* k_hist, int64_t ldkh, const void* v_hist, int64_t ldvh,
                                        const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
-                                       int64_t ldv, void* o, int64_t ldo, void* hip_stream) {
+                                       int64_t ldv, void* o, int64_t ldo, void* workspace, size_t workspace_bytes,
+                                       void* hip_stream) {
   hstu_status_t st = check_attn_common(desc, hist, bias);
   if (st != HSTU_OK) return st;
   if (!cand) return fail(HSTU_E_NULL, "candidate batch is NULL");
@@ -311,7 +323,20 @@ hstu_status_t hstu_attn_fwd_candidates(const hstu_attn_desc_t* desc, const hstu_
   for (const Range& r : ins)
     if (overlaps(ro, r)) return fail(HSTU_E_ALIAS, "o overlaps an input");
   if (cand->num_seqs == 0 || Tc == 0 || max_candidates == 0) return ok();
+  const size_t need = hstu::cand_workspace_bytes(Th, cand->num_seqs, max_candidates, static_cast<int>(H),
+                                                 static_cast<int>(d));
+  if (workspace_bytes < need || !workspace)
+    return fail(HSTU_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(HSTU_E_ALIGN, "workspace must be 16-byte aligned");
+  const Range rw{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+  if (overlaps(rw, ro)) return fail(HSTU_E_ALIAS, "workspace overlaps o");
+  for (const Range& r : ins)
+    if (overlaps(rw, r)) return fail(HSTU_E_ALIAS, "workspace overlaps an input");
   hstu::CandArgs a{};
+  a.num_seqs = cand->num_seqs;
+  a.max_candidates = max_candidates;
+  a.chunk_base = static_cast<int64_t*>(workspace);
+  a.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + hstu::cand_partial_offset(cand->num_seqs));
   a.q_c = q; a.k_c = k; a.v_c = v; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv;
   a.k_h = k_hist; a.v_h = v_hist; a.ldkh = ldkh; a.ldvh = ldvh;
   a.o = o; a.ldo = ldo;
@@ -323,8 +348,7 @@ hstu_status_t hstu_attn_fwd_candidates(const hstu_attn_desc_t* desc, const hstu_
   a.time_table = has_time ? bias->time_table : nullptr;
   a.time_buckets = has_time ? bias->time_buckets : 0;
   a.alpha = desc->qk_scale; a.divisor = desc->divisor; a.num_heads = static_cast<int>(H);
-  hipError_t e = hstu::launch_attn_cand_bf16(a, static_cast<int>(d), cand->num_seqs, max_candidates,
-                                             static_cast<hipStream_t>(hip_stream));
+  hipError_t e = hstu::launch_attn_cand_bf16(a, static_cast<int>(d), Th, Tc, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "candidate scoring launch");
   return ok();
 }

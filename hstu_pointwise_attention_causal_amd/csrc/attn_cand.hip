@@ -10,7 +10,13 @@
 // Candidates never see each other, so one pass over the history's K and V
 // serves a whole micro-batch of candidates.
 //
-// A workgroup holds 128 candidates of one (sequence, head), 4 waves of 32.
+// Long histories are split into chunks of kCandChunk keys so that the
+// workgroups carry similar work whatever the history lengths: a workgroup
+// holds 128 candidates of one (sequence, head) against one chunk, 4 waves of
+// 32. A sequence with one chunk writes its output directly; otherwise each
+// chunk writes an fp32 partial (no softmax, so partials simply add) and
+// attn_cand_reduce_kernel sums them in chunk order and scales. The chunk-0
+// workgroup also takes the candidates' own keys.
 // History K / V / timestamp tiles of 64 keys go HBM -> LDS with direct loads,
 // double-buffered. Per 32-key block: S^T = K Q^T on v_mfma_f32_32x32x16_bf16
 // (Q in registers), P = SiLU(S + bias) in fp32, O += P V with P straight from
@@ -69,14 +75,62 @@ __device__ __forceinline__ float silu2(float x) {   // 2 g(x') with g(x') = log2
   return x * __builtin_amdgcn_rcpf(fmaf(__builtin_amdgcn_exp2f(-x), 0.5f, 0.5f));
 }
 
+// Sequence whose chunk range holds global chunk g: the last b with base[b] <= g.
+__device__ __forceinline__ int chunk_seq(const int64_t* base, int num_seqs, int64_t g) {
+  int lo = 0, hi = num_seqs;   // base[lo] <= g < base[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (base[mid] <= g) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// One workgroup: base[b] = sum over earlier sequences of max(1, ceil(n / kCandChunk)).
+__global__ __launch_bounds__(1024) void cand_chunk_scan_kernel(CandArgs a) {
+  __shared__ int64_t wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int64_t carry = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 1024) {
+    const int b = c0 + tid;
+    int64_t cnt = 0;
+    if (b < a.num_seqs) {
+      const int64_t n = max(a.hist_off[b + 1] - a.hist_off[b], int64_t(0));
+      cnt = max(int64_t(1), (n + kCandChunk - 1) / kCandChunk);
+    }
+    int64_t v = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t u = __shfl_up(v, o, 64);
+      if (lane >= o) v += u;
+    }
+    if (lane == 63) wsum[w] = v;
+    __syncthreads();
+    int64_t before = 0, total = 0;
+    for (int i = 0; i < 16; ++i) {
+      before += i < w ? wsum[i] : 0;
+      total += wsum[i];
+    }
+    if (b < a.num_seqs) a.chunk_base[b] = carry + before + v - cnt;
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) a.chunk_base[a.num_seqs] = carry;
+}
+
 template <int D>
 __global__ __launch_bounds__(kCWaves * 64, 2) void attn_cand_kernel(CandArgs a) {
   static_assert(D % 32 == 0, "head dim");
   constexpr int KB = D / 16, NB = D / 32, CH = D / 8;
-  const int b = blockIdx.z, h = blockIdx.y;
+  const int64_t g = blockIdx.x;
+  if (g >= a.chunk_base[a.num_seqs]) return;
+  const int b = chunk_seq(a.chunk_base, a.num_seqs, g), h = blockIdx.y;
+  const int chunk = static_cast<int>(g - a.chunk_base[b]);
+  const bool single = a.chunk_base[b + 1] - a.chunk_base[b] == 1;
   const int64_t h0 = a.hist_off[b], c0 = a.cand_off[b];
-  const int n = static_cast<int>(a.hist_off[b + 1] - h0), m = static_cast<int>(a.cand_off[b + 1] - c0);
-  const int ct0 = blockIdx.x * kCBM;
+  const int n = static_cast<int>(a.hist_off[b + 1] - h0);
+  const int m = min(static_cast<int>(a.cand_off[b + 1] - c0), a.max_candidates);
+  const int ct0 = blockIdx.z * kCBM;
   if (ct0 >= m) return;
 
   __shared__ CandSmem<D> sm;
@@ -171,9 +225,10 @@ __global__ __launch_bounds__(kCWaves * 64, 2) void attn_cand_kernel(CandArgs a) 
     }
   };
 
-  // ---- history: every key is visible to every candidate (all sit at position n)
-  const int ntiles = (n + kCBN - 1) / kCBN;
-  if (ntiles > 0) issue_hist(0, sm.k[0], sm.v[0], sm.t[0]);
+  // ---- history chunk: every key is visible to every candidate (all sit at position n)
+  const int t_begin = chunk * (kCandChunk / kCBN);
+  const int ntiles = min((n + kCBN - 1) / kCBN, t_begin + kCandChunk / kCBN);
+  if (t_begin < ntiles) issue_hist(t_begin, sm.k[0], sm.v[0], sm.t[0]);
   wait_vmcnt(0);
   __syncthreads();   // also publishes the staged bias tables
   auto tile_step = [&] __device__(const char* __restrict__ rk, const char* __restrict__ rv,
@@ -231,14 +286,15 @@ __global__ __launch_bounds__(kCWaves * 64, 2) void attn_cand_kernel(CandArgs a) 
     wait_vmcnt(0);
     tile_barrier();
   };
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1, nxt = buf ^ 1;
+  for (int t = t_begin; t < ntiles; ++t) {
+    const int buf = (t - t_begin) & 1, nxt = buf ^ 1;
     tile_step(sm.k[buf], sm.v[buf], sm.t[buf], sm.k[nxt], sm.v[nxt], sm.t[nxt], sm.pos, sm.time, t);
   }
 
-  // ---- each candidate's own key: the workgroup's 128 candidates as two
-  //      64-key tiles; wave w reads its 32 from tile w / 2, half w % 2
-  {
+  // ---- each candidate's own key (chunk 0 only): the workgroup's 128
+  //      candidates as two 64-key tiles; wave w reads its 32 from tile w / 2,
+  //      half w % 2
+  if (chunk == 0) {
     const char* kcb = static_cast<const char*>(a.k_c) + (c0 * a.ldk + h * D) * 2;
     const char* vcb = static_cast<const char*>(a.v_c) + (c0 * a.ldv + h * D) * 2;
 #pragma unroll
@@ -263,28 +319,86 @@ __global__ __launch_bounds__(kCWaves * 64, 2) void attn_cand_kernel(CandArgs a) 
   }
 
   // ---- epilogue: oacc[nb][j] = 2 log2(e) N O[cw + 8(j/4) + 4 lh + j%4][nb*32 + lr]
+  //      (this chunk's share of it when the history has several chunks)
+  if (single) {
+    const float scale = (a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n + 1)) / (2.0f * kLog2e);
+    __bf16* op = static_cast<__bf16*>(a.o) + (c0 + cw) * a.ldo + h * D + lr;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = 8 * (j >> 2) + 4 * lh + (j & 3);
+        if (cw + r < m) op[r * a.ldo + nb * 32] = static_cast<__bf16>(oacc[nb][j] * scale);
+      }
+  } else {
+    float* pp = a.partial + ((g * a.max_candidates + cw) * a.num_heads + h) * D + lr;
+    const int64_t rs = static_cast<int64_t>(a.num_heads) * D;   // floats per candidate row
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = 8 * (j >> 2) + 4 * lh + (j & 3);
+        if (cw + r < m) pp[r * rs + nb * 32] = oacc[nb][j];
+      }
+  }
+}
+
+// Candidate rows of sequences with several history chunks: the partials of
+// the sequence's chunks summed in chunk order, scaled, rounded to bf16. One
+// workgroup per candidate, four consecutive features per thread.
+__global__ __launch_bounds__(256) void attn_cand_reduce_kernel(CandArgs a, int d) {
+  const int64_t r = blockIdx.x;   // candidate token
+  const int b = chunk_seq(a.cand_off, a.num_seqs, r);
+  const int64_t c0 = a.cand_off[b];
+  const int64_t cl = r - c0;
+  const int64_t g0 = a.chunk_base[b], g1 = min(a.chunk_base[b + 1], a.chunk_limit);
+  if (a.chunk_base[b + 1] - g0 <= 1 || cl >= a.max_candidates) return;
+  const int n = static_cast<int>(a.hist_off[b + 1] - a.hist_off[b]);
   const float scale = (a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n + 1)) / (2.0f * kLog2e);
-  __bf16* op = static_cast<__bf16*>(a.o) + (c0 + cw) * a.ldo + h * D + lr;
+  const int width = a.num_heads * d;
+  __bf16* op = static_cast<__bf16*>(a.o) + r * a.ldo;
+  for (int i = threadIdx.x * 4; i < width; i += blockDim.x * 4) {
+    f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int64_t gg = g0; gg < g1; ++gg)
+      s += *reinterpret_cast<const f32x4_t*>(a.partial + (gg * a.max_candidates + cl) * width + i);
+    bf16x4_t o;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = 8 * (j >> 2) + 4 * lh + (j & 3);
-      if (cw + r < m) op[r * a.ldo + nb * 32] = static_cast<__bf16>(oacc[nb][j] * scale);
-    }
+    for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(s[e] * scale);
+    *reinterpret_cast<bf16x4_t*>(op + i) = o;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_attn_cand_bf16(const CandArgs& a, int d, int num_seqs, int max_candidates, hipStream_t stream) {
-  if (num_seqs <= 0 || max_candidates <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((max_candidates + kCBM - 1) / kCBM), static_cast<unsigned>(a.num_heads),
-                  static_cast<unsigned>(num_seqs));
+namespace {
+int64_t chunk_bound(int64_t hist_tokens, int num_seqs) {   // >= sum over sequences of max(1, ceil(n / C))
+  return (hist_tokens + kCandChunk - 1) / kCandChunk + num_seqs;
+}
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+}  // namespace
+
+size_t cand_partial_offset(int num_seqs) { return align256(static_cast<size_t>(num_seqs + 1) * 8); }
+
+size_t cand_workspace_bytes(int64_t hist_tokens, int num_seqs, int max_candidates, int num_heads, int d) {
+  if (num_seqs <= 0 || max_candidates <= 0) return 0;
+  return cand_partial_offset(num_seqs) +
+         static_cast<size_t>(chunk_bound(hist_tokens, num_seqs)) * max_candidates * num_heads * d * 4;
+}
+
+hipError_t launch_attn_cand_bf16(const CandArgs& a_in, int d, int64_t hist_tokens, int64_t cand_tokens,
+                                 hipStream_t stream) {
+  if (a_in.num_seqs <= 0 || a_in.max_candidates <= 0 || cand_tokens <= 0) return hipSuccess;
+  if (d != 128 && d != 64 && d != 32) return hipErrorInvalidValue;
+  CandArgs a = a_in;
+  a.chunk_limit = chunk_bound(hist_tokens, a.num_seqs);
+  const dim3 grid(static_cast<unsigned>(a.chunk_limit), static_cast<unsigned>(a.num_heads),
+                  static_cast<unsigned>((a.max_candidates + kCBM - 1) / kCBM));
   TimedScope timed(kTimedAttnCand, stream);
+  hipLaunchKernelGGL(cand_chunk_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
   if (d == 128) hipLaunchKernelGGL(attn_cand_kernel<128>, grid, dim3(kCWaves * 64), 0, stream, a);
   else if (d == 64) hipLaunchKernelGGL(attn_cand_kernel<64>, grid, dim3(kCWaves * 64), 0, stream, a);
-  else if (d == 32) hipLaunchKernelGGL(attn_cand_kernel<32>, grid, dim3(kCWaves * 64), 0, stream, a);
-  else return hipErrorInvalidValue;
+  else hipLaunchKernelGGL(attn_cand_kernel<32>, grid, dim3(kCWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL(attn_cand_reduce_kernel, dim3(static_cast<unsigned>(cand_tokens)), dim3(256), 0, stream, a, d);
   return hipGetLastError();
 }
 

@@ -87,8 +87,23 @@ struct CandArgs {
   float alpha;
   float divisor;
   int num_heads;
+  int num_seqs;
+  int max_candidates;      // candidates past it in a sequence are not scored
+  int64_t* chunk_base;     // workspace: [num_seqs + 1] first history chunk of each sequence
+  float* partial;          // workspace: fp32 [chunks][max_candidates][H][d] partial outputs
+  int64_t chunk_limit;     // chunks the partial buffer holds (set by the launcher)
 };
-hipError_t launch_attn_cand_bf16(const CandArgs& a, int d, int num_seqs, int max_candidates, hipStream_t stream);
+// History keys per chunk of candidate scoring: a sequence's history splits
+// into max(1, ceil(n / kCandChunk)) chunks, each one workgroup's key range.
+constexpr int kCandChunk = 2048;
+// Workspace of launch_attn_cand_bf16: chunk bases, then (at
+// cand_partial_offset) the partial outputs.
+size_t cand_partial_offset(int num_seqs);
+size_t cand_workspace_bytes(int64_t hist_tokens, int num_seqs, int max_candidates, int num_heads, int d);
+// Chunk bases, the chunked scoring, then the sum of the partials of
+// multi-chunk sequences, all on `stream`.
+hipError_t launch_attn_cand_bf16(const CandArgs& a, int d, int64_t hist_tokens, int64_t cand_tokens,
+                                 hipStream_t stream);
 
 hipError_t launch_attn_block_meta(const AttnArgs& a, int dqk, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, hipStream_t stream);

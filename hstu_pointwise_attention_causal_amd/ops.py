@@ -121,13 +121,25 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets: tor
     return out
 
 
+def attn_cand_workspace_size(num_heads: int, d: int, num_seqs: int, hist_tokens: int, max_candidates: int) -> int:
+    """hstu_attn_cand_workspace_size: workspace bytes of attn_fwd_candidates."""
+    desc = _desc(num_heads, d, d, torch.bfloat16, 1.0, 0.0)
+    j = _lib.Jagged()
+    j.num_seqs, j.total_tokens = int(num_seqs), int(hist_tokens)
+    need = _lib._SZ(0)
+    _lib.check(_lib.load().hstu_attn_cand_workspace_size(ctypes.byref(desc), ctypes.byref(j), int(max_candidates),
+                                                         ctypes.byref(need)))
+    return int(need.value)
+
+
 def attn_fwd_candidates(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cand_offsets: torch.Tensor,
                         k_hist: torch.Tensor, v_hist: torch.Tensor, hist_offsets: torch.Tensor, *,
                         timestamps: Optional[torch.Tensor] = None,
                         cand_timestamps: Optional[torch.Tensor] = None,
                         pos_table: Optional[torch.Tensor] = None, time_table: Optional[torch.Tensor] = None,
                         alpha: float = 1.0, divisor: float = 0.0, max_candidates: Optional[int] = None,
-                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                        out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """hstu_attn_fwd_candidates: candidates q, k, v [T_c, H, d] (offsets
     cand_offsets) scored against a history with cached k_hist, v_hist
     [T_h, H, d] (offsets hist_offsets). max_candidates defaults to the largest
@@ -149,10 +161,16 @@ def attn_fwd_candidates(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cand_
     jh = _jagged(hist_offsets, k_hist.shape[0], timestamps)
     jc = _jagged(cand_offsets, Tc, cand_timestamps)
     b = _bias(pos_table, time_table)
+    need = _lib._SZ(0)
+    _lib.check(lib.hstu_attn_cand_workspace_size(ctypes.byref(desc), ctypes.byref(jh), int(max_candidates),
+                                                 ctypes.byref(need)))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
     _lib.check(lib.hstu_attn_fwd_candidates(ctypes.byref(desc), ctypes.byref(jh), ctypes.byref(jc),
                                             int(max_candidates), ctypes.byref(b), _ptr(k_hist), ldkh,
                                             _ptr(v_hist), ldvh, _ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv,
-                                            _ptr(out), ldo, _stream_handle(q.device)))
+                                            _ptr(out), ldo, _ptr(workspace), workspace.numel(),
+                                            _stream_handle(q.device)))
     return out
 
 

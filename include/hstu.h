@@ -164,8 +164,11 @@ hstu_status_t hstu_attn_bwd(const hstu_attn_desc_t* desc, const hstu_jagged_t* j
  *     sizes the grid -- candidates past it in a sequence are not scored.
  *   k_hist, v_hist [T_h,H,d] (ldkh, ldvh): the history's cached keys / values.
  *   q, k, v [T_c,H,d]: the candidates' projections. o [T_c,H,d]: output.
- * bf16 only (dqk == dv in {32, 64, 128}); no workspace. Errors: as
- * hstu_attn_fwd.
+ *   workspace: at least hstu_attn_cand_workspace_size(...) bytes, 16-byte
+ *     aligned, not overlapping any argument (long histories are scored in
+ *     chunks whose fp32 partial outputs it holds; they are summed in a fixed
+ *     order, so results repeat bitwise).
+ * bf16 only (dqk == dv in {32, 64, 128}). Errors: as hstu_attn_fwd.
  * ------------------------------------------------------------------------- */
 hstu_status_t hstu_attn_fwd_candidates(const hstu_attn_desc_t* desc, const hstu_jagged_t* hist,
                                        const hstu_jagged_t* cand, int32_t max_candidates,
@@ -173,7 +176,15 @@ hstu_status_t hstu_attn_fwd_candidates(const hstu_attn_desc_t* desc, const hstu_
                                        const void* k_hist, int64_t ldkh, const void* v_hist, int64_t ldvh,
                                        const void* q, int64_t ldq, const void* k, int64_t ldk,
                                        const void* v, int64_t ldv, void* o, int64_t ldo,
-                                       void* hip_stream);
+                                       void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * hstu_attn_cand_workspace_size -- device workspace bytes for
+ * hstu_attn_fwd_candidates: about (T_h / 2048 + num_seqs) x max_candidates x
+ * H x d x 4 bytes. Host function; desc, hist and bytes are host pointers.
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_attn_cand_workspace_size(const hstu_attn_desc_t* desc, const hstu_jagged_t* hist,
+                                            int32_t max_candidates, size_t* bytes);
 
 /* Parameters of one HSTU layer (bf16 weights, fp32 norms and biases). Weight
  * matrices use the nn.Linear layout [out_features, in_features] of the

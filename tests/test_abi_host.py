@@ -190,3 +190,23 @@ def test_stochastic_length_and_gather_rejections(lib):
     assert g(IDX, CNT, 4, SRC + 2, 10, 1024, DST, 1024, 1024, None) == 4  # misaligned src
     assert g(IDX, CNT, 4, SRC, 10, 1024, SRC + 4096, 1024, 1024, None) == 7  # dst overlaps src
     assert g(IDX, CNT, 0, SRC, 10, 1024, DST, 1024, 1024, None) == 0   # nothing to copy
+
+
+def test_candidate_workspace_is_checked(lib):
+    c = lib.load()
+    d = _desc(lib, H=4, d=128)
+    hist = _jag(lib, B=2, T=5000)
+    cand = _jag(lib, B=2, T=300)
+    cand.seq_offsets = 0x30000
+    need = ctypes.c_size_t(0)
+    assert c.hstu_attn_cand_workspace_size(ctypes.byref(d), ctypes.byref(hist), 200, ctypes.byref(need)) == 0
+    # chunks: ceil(5000 / 2048) + 2 sequences = 5; 5 x 200 candidates x 4 heads x 128 x 4 bytes + offsets
+    assert need.value >= 5 * 200 * 4 * 128 * 4
+    b = lib.Bias()
+    G = 1 << 28   # fake device buffers 256 MB apart, never dereferenced
+    o = 6 * G
+    args = (ctypes.byref(d), ctypes.byref(hist), ctypes.byref(cand), 200, ctypes.byref(b),
+            1 * G, 512, 2 * G, 512, 3 * G, 512, 4 * G, 512, 5 * G, 512, o, 512)
+    assert c.hstu_attn_fwd_candidates(*args, 7 * G, need.value - 1, None) == 6      # workspace too small
+    assert c.hstu_attn_fwd_candidates(*args, 7 * G + 8, need.value, None) == 4      # misaligned workspace
+    assert c.hstu_attn_fwd_candidates(*args, o, need.value, None) == 7              # workspace overlaps o

@@ -55,6 +55,18 @@ def test_reduced_ragged_histories_all_candidates(hstu):
     assert err <= TOL_BF16
 
 
+def test_histories_across_the_chunk_size(hstu):
+    """Histories of 2047, 2048, 2049, 4100, 0 and 6000 tokens (one to three
+    history chunks of 2048 keys, partial outputs summed across chunks) with
+    3, 1, 130, 2, 5 and 64 candidates, both biases; every candidate."""
+    from workloads.generators import _cand_recipe
+    wl = _cand_recipe("chunks", 19, lengths=[2047, 2048, 2049, 4100, 0, 6000], cands=[3, 1, 130, 2, 5, 64],
+                      H=2, d=128)
+    err = rel_err(_gpu(hstu, wl), _ref(wl))
+    print(f"chunked histories err {err:.2e}")
+    assert err <= TOL_BF16
+
+
 @pytest.mark.parametrize("pos,time", [(False, False), (True, False), (False, True)])
 def test_bias_subsets_scale_and_divisor(hstu, pos, time):
     wl = make_workload("c6_small")
