@@ -44,16 +44,23 @@ METRIC = "HSTU attention causal-effective TFLOP/s + tokens/s/layer, jagged bf16,
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_c3_traffic.json")
 KERNEL_SRCS = [os.path.join(ROOT, "hstu_pointwise_attention_causal_amd", "csrc", f)
-               for f in ("attn_fwd.hip", "attn_common.h", "common.h", "launch.h")]
+               for f in ("attn_fwd.hip", "attn_common.h", "common.h")]
+LAUNCH_H = os.path.join(ROOT, "hstu_pointwise_attention_causal_amd", "csrc", "launch.h")
 COPY_BYTES = 1 << 30
 
 
 def kernel_hash() -> str:
-    """Hash of the sources the attention forward kernel is compiled from."""
+    """Hash of the sources the attention forward kernel is compiled from: its
+    own file and headers, and of the launch header only the argument struct
+    it reads (the header also declares every other kernel's launcher)."""
     h = hashlib.sha256()
     for p in KERNEL_SRCS:
         with open(p, "rb") as f:
             h.update(f.read())
+    with open(LAUNCH_H) as f:
+        text = f.read()
+    start = text.index("struct AttnArgs {")
+    h.update(text[start:text.index("};", start)].encode())
     return h.hexdigest()[:16]
 
 

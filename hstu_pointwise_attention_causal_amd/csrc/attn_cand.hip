@@ -71,10 +71,6 @@ __device__ __forceinline__ void issue_rows64(const char* base, int64_t ld, int r
   }
 }
 
-__device__ __forceinline__ float silu2(float x) {   // 2 g(x') with g(x') = log2(e) SiLU(x), x' = log2(e) x
-  return x * __builtin_amdgcn_rcpf(fmaf(__builtin_amdgcn_exp2f(-x), 0.5f, 0.5f));
-}
-
 // Sequence whose chunk range holds global chunk g: the last b with base[b] <= g.
 __device__ __forceinline__ int chunk_seq(const int64_t* base, int num_seqs, int64_t g) {
   int lo = 0, hi = num_seqs;   // base[lo] <= g < base[hi]
@@ -266,7 +262,7 @@ __global__ __launch_bounds__(kCWaves * 64, 2) void attn_cand_kernel(CandArgs a) 
       if (pos_const && time_const && !tail) {
         const float c = (has_pos ? pos_far : 0.f) + (has_time ? stime[tlo] : 0.f);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) p[j] = silu2(fmaf(s[j], alpha_l, c));
+        for (int j = 0; j < 16; ++j) p[j] = silu2_exact(fmaf(s[j], alpha_l, c));
       } else {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -278,7 +274,7 @@ __global__ __launch_bounds__(kCWaves * 64, 2) void attn_cand_kernel(CandArgs a) 
             c = pos_const ? pos_far : (pb < kCPosLds ? spos[pb] : kLog2e * a.pos_table[h * Bp + pb]);
           }
           if (has_time) c += time_const ? stime[tlo] : stime[time_bucket64(tc - rt[kl], Bt)];
-          p[j] = key < n ? silu2(fmaf(s[j], alpha_l, c)) : 0.f;
+          p[j] = key < n ? silu2_exact(fmaf(s[j], alpha_l, c)) : 0.f;
         }
       }
       pv(rv, kvb, p);
@@ -313,7 +309,7 @@ __global__ __launch_bounds__(kCWaves * 64, 2) void attn_cand_kernel(CandArgs a) 
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int kk = 8 * (j >> 2) + 4 * lh + (j & 3);   // candidate key within the wave's 32
-      p[j] = (kk == lr && crow < m) ? silu2(fmaf(s[j], alpha_l, pos_self + time_self)) : 0.f;
+      p[j] = (kk == lr && crow < m) ? silu2_exact(fmaf(s[j], alpha_l, pos_self + time_self)) : 0.f;
     }
     pv(vbuf, kvb, p);
   }

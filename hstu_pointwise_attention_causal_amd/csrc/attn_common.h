@@ -97,6 +97,29 @@ __device__ __forceinline__ int swz_dual(int r) {
   else return (r >> 2) & 3;
 }
 
+// SiLU in log2 units, shared by the attention kernels: with x' = log2(e) x,
+// g(x') = log2(e) SiLU(x) = x' / (1 + 2^-x'). Both forms return 2 g(x') (the
+// factor 2 is exact and removed in the output scale): exactly x' / (1/2 +
+// 2^-x' / 2) -- an exp2 and a reciprocal, both quarter rate -- or, when |x'|
+// is known to stay within kPolyBound, x' + y 2P(y) with y = x'^2 and a cubic P
+// fitted on |x| <= 2 (max error 2.8e-5 in x' units, two orders of magnitude
+// below the bf16 rounding of P; coefficients from gen_silu_poly.py): five
+// FMA-class operations.
+constexpr float kPolyC0 = 1.731778037e-01f, kPolyC1 = -6.804446619e-03f, kPolyC2 = 2.799578346e-04f,
+                kPolyC3 = -6.863766511e-06f;
+constexpr float kPolyBound = 1.95f * kLog2e;   // in x' units; fit range is 2 log2(e)
+
+__device__ __forceinline__ float silu2_exact(float x) {
+  return x * __builtin_amdgcn_rcpf(fmaf(__builtin_amdgcn_exp2f(-x), 0.5f, 0.5f));
+}
+__device__ __forceinline__ float silu2_poly(float x) {
+  const float y = x * x;
+  float p = fmaf(y, 2.0f * kPolyC3, 2.0f * kPolyC2);
+  p = fmaf(y, p, 2.0f * kPolyC1);
+  p = fmaf(y, p, 2.0f * kPolyC0);
+  return fmaf(y, p, x);
+}
+
 // Sum over the 16 lanes of each DPP row; every lane of the row gets the sum.
 __device__ __forceinline__ float row16_sum(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]

@@ -106,23 +106,6 @@ enum BlockPath { kUniform = 0, kTwoTime = 1, kGeneral = 2 };
 enum PolyMode { kPolyAll = 0, kPolyNone = 1, kPolyMixed = 2 };
 
 constexpr int kPosLdsFast = 1024;
-constexpr float kPolyC0 = 1.731778037e-01f, kPolyC1 = -6.804446619e-03f, kPolyC2 = 2.799578346e-04f,
-                kPolyC3 = -6.863766511e-06f;
-constexpr float kPolyBound = 1.95f * kLog2e;   // in x' units; fit range is 2 log2(e)
-
-// Both forms return 2 g(x') (the factor 2 is exact and removed in the output
-// scale): exactly x' / (1/2 + 2^-x' / 2), or x' + y 2P(y) with y = x'^2 -- five
-// FMA-class operations.
-__device__ __forceinline__ float silu2_exact(float x) {
-  return x * __builtin_amdgcn_rcpf(fmaf(__builtin_amdgcn_exp2f(-x), 0.5f, 0.5f));
-}
-__device__ __forceinline__ float silu2_poly(float x) {
-  const float y = x * x;
-  float p = fmaf(y, 2.0f * kPolyC3, 2.0f * kPolyC2);
-  p = fmaf(y, p, 2.0f * kPolyC1);
-  p = fmaf(y, p, 2.0f * kPolyC0);
-  return fmaf(y, p, x);
-}
 
 // Direct HBM -> LDS loads of one key tile (K, V and key timestamps). Kept out
 // of the kernel body as a device-only function (the LDS address-space
