@@ -366,6 +366,27 @@ def test_layer_matches_brute_force_loops():
     assert _rel(got, ref) < 1e-12
 
 
+def test_stack_matches_brute_force_layers_in_turn():
+    """A two-layer stack is the brute-force layer loops applied twice, the
+    second on the first's output."""
+    x, p1, off, ts = _tiny_layer(19, [5, 1, 3])
+    _, p2, _, _ = _tiny_layer(23, [5, 1, 3])
+    mid = B.layer_fwd(x, p1, off, 2, 3, 3, timestamps=ts)
+    ref = B.layer_fwd(np.array(mid), p2, off, 2, 3, 3, timestamps=ts)
+    got = O.stack_fwd(x, [p1, p2], off, num_heads=2, dqk=3, dv=3, timestamps=ts)
+    assert _rel(got, ref) < 1e-12
+
+
+def test_stack_with_zero_output_projections_is_identity():
+    x, p, off, ts = _tiny_layer(29, [4, 2])
+    p = dict(p)
+    p["w_out"] = np.zeros_like(p["w_out"])
+    if p.get("b_out") is not None:
+        p["b_out"] = np.zeros_like(p["b_out"])
+    got = O.stack_fwd(x, [p, p, p], off, num_heads=2, dqk=3, dv=3, timestamps=ts)
+    assert np.array_equal(got, x)
+
+
 def test_layer_rows_match_full_layer():
     x, p, off, ts = _tiny_layer(17, [6, 0, 9])
     full, _ = O.layer_fwd(x, p, off, num_heads=2, dqk=3, dv=3, timestamps=ts)
