@@ -114,3 +114,26 @@ def test_deterministic(hstu):
     a = _run(hstu, wl.x, h["table"], h["gamma"], h["eps"])
     b = _run(hstu, wl.x, h["table"], h["gamma"], h["eps"])
     assert torch.equal(a, b)
+
+
+def test_dim_1024_with_strided_rows_and_logits(hstu):
+    """dim 1024 (the other built width): x a column view of a wider buffer,
+    logits written into a buffer whose rows are padded past the vocabulary."""
+    import torch
+    rng = np.random.default_rng(79)
+    rows, dim, vocab = 130, 1024, 520
+    xw = (rng.standard_normal((rows, dim + 64)) * rng.uniform(0.1, 4.0, (rows, 1))).astype(np.float32)
+    table = (0.02 * rng.standard_normal((vocab, dim))).astype(np.float32)
+    gamma = (1.0 + 0.1 * rng.standard_normal(dim)).astype(np.float32)
+    xd = to_dev(xw, torch.bfloat16)[:, 32:32 + dim]
+    out_buf = torch.full((rows, vocab + 24), -5.0, dtype=torch.bfloat16, device="cuda:0")
+    out = out_buf[:, :vocab]
+    hstu.head_fwd(xd, to_dev(table, torch.bfloat16), gamma=to_dev(gamma, torch.float32), eps=1e-6, out=out)
+    torch.cuda.synchronize()
+    xr = xd.float().cpu().numpy()
+    tr = to_dev(table, torch.bfloat16).float().cpu().numpy()
+    ref = orc.head_fwd(xr, tr, gamma, 1e-6)
+    err = rel_err(out.float().cpu().numpy(), ref)
+    print(f"dim 1024 strided err {err:.2e}")
+    assert err <= TOL_BF16
+    assert bool((out_buf[:, vocab:] == -5.0).all())   # padding untouched

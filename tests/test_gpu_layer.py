@@ -152,3 +152,16 @@ def test_jagged_layer_full_size_sampled_rows(hstu):
     print(f"c2 sampled err {err:.2e} over {len(rows)} rows")
     assert err <= TOL_BF16
     assert np.all(np.isfinite(out))
+
+
+def test_wider_layer_d1024_h8(hstu):
+    """D = 1024 with 8 heads of 128 (H dv = 1024, G 4096 wide): the 1024-wide
+    LayerNorms and both GEMM shapes at another width, 5 ragged sequences."""
+    from workloads.generators import _layer_recipe
+    wl = _layer_recipe("wide", 31, lengths=[130, 1, 0, 257, 64], num_layers=1, D=1024, H=8, time=True)
+    got, _ = _run_stack(hstu, wl)
+    ref, _ = orc.layer_fwd(wl.x, wl.layers[0], wl.seq_offsets, num_heads=wl.num_heads, dqk=wl.dqk, dv=wl.dv,
+                           timestamps=wl.timestamps, eps=wl.ln_eps)
+    err = rel_err(got, ref)
+    print(f"D 1024 H 8 layer err {err:.2e}")
+    assert err <= TOL_BF16

@@ -123,3 +123,13 @@ def test_deterministic(hstu):
     assert np.array_equal(a[0], b[0])
     for k in a[1]:
         assert np.array_equal(a[1][k], b[1][k]), k
+
+
+def test_wider_layer_backward_d1024_h8(hstu):
+    """D = 1024 with 8 heads of 128: the 1024-wide LayerNorm backward and the
+    weight-gradient GEMMs at another width, 5 ragged sequences."""
+    from workloads.generators import _layer_recipe
+    wl = _layer_recipe("wide_bwd", 37, lengths=[130, 1, 0, 257, 64], num_layers=1, D=1024, H=8, time=True,
+                       backward=True)
+    p = wl.layers[0]
+    _compare("D 1024 H 8", _gpu_bwd(hstu, wl, p), _oracle(wl, p))
