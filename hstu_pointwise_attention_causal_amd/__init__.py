@@ -1,5 +1,7 @@
 """MI355X (gfx950) HSTU hot path: causal pointwise aggregated attention over
-jagged sequences, its backward, and one HSTU layer, behind the C ABI of
+jagged sequences and its backward, one HSTU layer forward and backward,
+candidate scoring against cached history keys and values, Stochastic Length,
+and the final RMSNorm with the tied retrieval head, behind the C ABI of
 ``libhstu.so`` (declared in ``include/hstu.h``).
 
 The Python functions below only marshal torch tensors into that ABI. The
@@ -25,6 +27,12 @@ from .ops import (  # noqa: F401
     timing_read,
 )
 
-__all__ = ["HstuError", "load", "attn_fwd", "attn_fwd_candidates", "attn_cand_workspace_size", "attn_bwd", "attn_workspace_size", "layer_fwd",
-           "layer_bwd", "head_fwd", "head_workspace_size",
-           "stochastic_length", "gather_rows", "make_layer_params", "timing_enable", "timing_read"]
+__all__ = [
+    "HstuError", "load",
+    "attn_fwd", "attn_bwd", "attn_workspace_size",
+    "attn_fwd_candidates", "attn_cand_workspace_size",
+    "layer_fwd", "layer_bwd", "make_layer_params",
+    "head_fwd", "head_workspace_size",
+    "stochastic_length", "gather_rows",
+    "timing_enable", "timing_read",
+]

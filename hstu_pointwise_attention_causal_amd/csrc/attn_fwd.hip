@@ -103,7 +103,6 @@ __device__ __forceinline__ float time_bias(const BiasLds& s, const AttnArgs& a, 
 // a bound over the whole bias table, so a row's result never depends on later
 // tokens.
 enum BlockPath { kUniform = 0, kTwoTime = 1, kGeneral = 2 };
-enum PolyMode { kPolyAll = 0, kPolyNone = 1, kPolyMixed = 2 };
 
 constexpr int kPosLdsFast = 1024;
 
