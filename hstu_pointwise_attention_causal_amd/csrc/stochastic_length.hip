@@ -10,7 +10,9 @@
 //                       three-pass radix select (11 + 11 + 10 bits, LDS
 //                       histograms), then a compaction pass in position order
 //                       that keeps keys below it and the first ones equal to
-//                       it, writing the kept tokens' input positions
+//                       it, writing the kept tokens' input positions; a
+//                       sequence of up to 16384 tokens works on an LDS copy
+//                       of its keys
 //   gather_rows_kernel  dst row r = src row index[r] (a wave per wide row, a
 //                       thread per narrow one)
 #include "stochastic_length.h"
@@ -90,27 +92,17 @@ __device__ __forceinline__ uint32_t block_excl(uint32_t v, uint32_t* wtot, uint3
   return before + incl - v;
 }
 
-__global__ __launch_bounds__(kSelThreads) void sl_select_kernel(SlArgs a) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t wtot[kSelThreads / 64];
-  __shared__ uint32_t sel[2];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  int64_t s, e;
-  seq_range(a, b, s, e);
-  const int64_t n = e - s, T = a.total_tokens;
-  const int64_t base = a.new_offsets[b];
-  int64_t* out = a.gather_index;
-  if (n <= a.max_len) {   // kept whole
-    for (int64_t i = tid; i < n; i += kSelThreads)
-      if (base + i < T) out[base + i] = s + i;
-    return;
-  }
-  if (a.max_len == 0) return;
-  const uint32_t* key = a.keys + s;
-  const int nn = static_cast<int>(n);   // n < T < 2^31
+constexpr int kSelLdsKeys = 16384;   // sequences up to this long are selected from a copy of their keys in LDS
 
-  // ---- the L-th smallest key: rank k among the keys that match the digits so far
-  uint32_t prefix = 0, mask = 0, k = static_cast<uint32_t>(a.max_len);
+// The cap-th smallest key of key[0, nn) and the compaction of the kept
+// positions into out[base ...]. `key` is a sequence's keys in global memory or
+// their LDS copy; each call site is inlined with its own address space.
+__device__ __forceinline__ void select_compact(const uint32_t* __restrict__ key, int nn, uint32_t cap,
+                                               int64_t s, int64_t base, int64_t T, int64_t* __restrict__ out,
+                                               uint32_t* hist, uint32_t* wtot, uint32_t* sel) {
+  const int tid = threadIdx.x;
+  // ---- the cap-th smallest key: rank k among the keys that match the digits so far
+  uint32_t prefix = 0, mask = 0, k = cap;
 #pragma unroll 1
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
@@ -147,21 +139,55 @@ __global__ __launch_bounds__(kSelThreads) void sl_select_kernel(SlArgs a) {
   // keys below `prefix` are kept; of the keys equal to it, the first k by position
   const uint32_t kstar = prefix, take_eq = k;
 
-  // ---- compaction in position order
-  uint32_t eq_carry = 0, keep_carry = 0;
+  // ---- compaction in position order. A kept token's output position is the
+  // number of keys below kstar before it plus min(equal keys before it,
+  // take_eq): one block scan of packed counts (below in the low 16 bits,
+  // equal in the high 16; a block holds at most 1024 of each) gives both.
+  uint32_t lt_carry = 0, eq_carry = 0;
   for (int c0 = 0; c0 < nn; c0 += kSelThreads) {
     const int i = c0 + tid;
     const bool valid = i < nn;
     const uint32_t kv = valid ? key[i] : 0u;
-    const bool eq = valid && kv == kstar;
-    uint32_t eq_total;
-    const uint32_t eq_rank = eq_carry + block_excl(eq ? 1u : 0u, wtot, eq_total);
-    const bool keep = valid && (kv < kstar || (eq && eq_rank < take_eq));
-    uint32_t keep_total;
-    const uint32_t pos = keep_carry + block_excl(keep ? 1u : 0u, wtot, keep_total);
-    if (keep && base + pos < T) out[base + pos] = s + i;
-    eq_carry += eq_total;
-    keep_carry += keep_total;
+    const bool lt = valid && kv < kstar, eq = valid && kv == kstar;
+    uint32_t total;
+    const uint32_t before = block_excl((lt ? 1u : 0u) | (eq ? 0x10000u : 0u), wtot, total);
+    const uint32_t lt_before = lt_carry + (before & 0xFFFFu), eq_before = eq_carry + (before >> 16);
+    if (lt || (eq && eq_before < take_eq)) {
+      const int64_t pos = static_cast<int64_t>(lt_before) + min(eq_before, take_eq);
+      if (base + pos < T) out[base + pos] = s + i;
+    }
+    lt_carry += total & 0xFFFFu;
+    eq_carry += total >> 16;
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void sl_select_kernel(SlArgs a) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t wtot[kSelThreads / 64];
+  __shared__ uint32_t sel[2];
+  __shared__ uint32_t skeys[kSelLdsKeys];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  int64_t s, e;
+  seq_range(a, b, s, e);
+  const int64_t n = e - s, T = a.total_tokens;
+  const int64_t base = a.new_offsets[b];
+  int64_t* out = a.gather_index;
+  if (n <= a.max_len) {   // kept whole
+    for (int64_t i = tid; i < n; i += kSelThreads)
+      if (base + i < T) out[base + i] = s + i;
+    return;
+  }
+  if (a.max_len == 0) return;
+  const uint32_t* key = a.keys + s;
+  const int nn = static_cast<int>(n);   // n < T < 2^31
+  const uint32_t cap = static_cast<uint32_t>(a.max_len);   // < n
+  if (nn <= kSelLdsKeys) {
+    // one read of the keys from memory; the four passes over them then run from LDS
+    for (int i = tid; i < nn; i += kSelThreads) skeys[i] = key[i];
+    __syncthreads();
+    select_compact(skeys, nn, cap, s, base, T, out, hist, wtot, sel);
+  } else {
+    select_compact(key, nn, cap, s, base, T, out, hist, wtot, sel);
   }
 }
 
