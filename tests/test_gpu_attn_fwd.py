@@ -89,6 +89,25 @@ def test_large_and_mixed_score_ranges(hstu):
     assert rel_err(_run(hstu, wl), _oracle(wl)) <= TOL_BF16
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_trailing_empty_sequences_leave_outputs_bitwise(hstu, d):
+    """Appending 600 empty sequences to a batch of long, ragged ones makes the
+    work-list bound ten times larger (every sequence reserves a query tile per
+    head) but adds no work: every output row is bitwise the same, and both
+    runs match the oracle. The 4100-token sequence walks key tiles past the
+    32-tile window of the per-block bias classification."""
+    import dataclasses
+    lengths = [1500, 700, 513, 512, 90, 4100, 641]
+    wl = _attn_recipe("pad", 300 + d, lengths, 2, d)
+    ref = _oracle(wl)
+    base = _run(hstu, wl)
+    off = np.asarray(wl.seq_offsets)
+    padded = dataclasses.replace(wl, seq_offsets=np.concatenate([off, np.full(600, off[-1], off.dtype)]))
+    out = _run(hstu, padded)
+    assert rel_err(base, ref) <= TOL_BF16
+    assert np.array_equal(base, out)
+
+
 def test_nan_in_neighbour_sequence_does_not_leak(hstu):
     import torch
     wl = _attn_recipe("nan", 10, [200, 150, 90], 2, 128)
