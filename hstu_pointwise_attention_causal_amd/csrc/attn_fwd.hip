@@ -178,6 +178,8 @@ struct FwdSmem {
 constexpr int kInfoPolyAll = 4;
 constexpr int kInfoMasked = 1 << 9;
 constexpr int kInfoExactAll = 1 << 10;   // no row of the wave qualifies for the polynomial
+constexpr int kInfoNarrowTime = 1 << 11; // every gap t_i - t_j of the block's pairs fits in int32
+constexpr int kInfoEmpty = 1 << 12;      // no pair of the block is causal and inside the sequence
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_kernel(AttnArgs a) {
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
   float rec_clo = 0.f, rec_chi = 0.f, rec_kmax = 0.f;
   auto classify_window = [&] __device__(int win, const float* stime) {
     const int ka = (win * 64 + lane) * 32;
-    int info = kGeneral | kInfoMasked;   // a block with no pair for this wave: everything masked
+    int info = kGeneral | kInfoMasked | kInfoEmpty;   // no pair for this wave: P is zero
     float clo = 0.f, chi = 0.f, km = 0.f;
     if (ka < n && ka <= qa + 31) {
       const BlockMeta m = meta_row[win * 64 + lane];
@@ -384,8 +386,12 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
       const bool polyall = !need_mask && fmaf(qbound_max, km, cmax) <= kPolyBound;
       // every row fails the bound when the smallest one does (fma is monotone in it)
       const bool exactall = !need_mask && fmaf(qbound_min, km, cmax) > kPolyBound;
+      // gaps of valid pairs lie in [wq_min - tmax, wq_max - tmin]; inside int32 the
+      // low words' wrapped difference is exact (and max(gap, 0) + 1 cannot overflow)
+      const bool narrow = has_time && qa < n && wq_max - m.tmin <= int64_t(INT32_MAX) - 1 &&
+                          wq_min - m.tmax >= int64_t(INT32_MIN);
       info = path | (polyall ? kInfoPolyAll : 0) | (exactall ? kInfoExactAll : 0) | (blo << 3) |
-             (need_mask ? kInfoMasked : 0);
+             (need_mask ? kInfoMasked : 0) | (narrow ? kInfoNarrowTime : 0);
     }
     rec_info = info;
     rec_clo = clo;
@@ -404,6 +410,11 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
   auto general_block = [&] __device__(const f32x16_t& sc, int l, int k0, int kvb, const int64_t* rt,
                                       const float* spos, const float* stime, bf16x8_t* pa) {
     const int info = __builtin_amdgcn_readlane(rec_info, l);
+    if (info & kInfoEmpty) {   // past the wave's last row or the sequence end
+      pa[0] = bf16x8_t{};
+      pa[1] = bf16x8_t{};
+      return;
+    }
     const int path = info & 3;
     float x[16];
     if (path == kUniform) {
@@ -418,17 +429,50 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
       for (int j = 0; j < 16; ++j)
         x[j] = fmaf(sc[j], alpha_l, rt[kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)] <= lim ? chi : clo);
     } else {
+      // Per-pair buckets. Every branch below is uniform over the wave and taken
+      // once per block, and each loop issues all 16 lookups before the first
+      // is used, so the LDS latencies overlap.
+      float c[16];
+      if (has_pos && pos_in_lds) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int kvl = kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
-        float c = 0.f;
-        if (has_pos) {
-          const int pb = min(max(qrow - (k0 + kvl), 0), Bp - 1);
-          c = pb < kPosLdsFast ? spos[pb] : kLog2e * a.pos_table[h * Bp + pb];
+        for (int j = 0; j < 16; ++j) {
+          const int kv = k0 + kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
+          c[j] = spos[min(max(qrow - kv, 0), Bp - 1)];
         }
-        if (has_time) c += stime[time_bucket64(tq - rt[kvl], Bt)];
-        x[j] = fmaf(sc[j], alpha_l, c);
+      } else if (has_pos) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int kv = k0 + kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
+          const int pb = min(max(qrow - kv, 0), Bp - 1);
+          c[j] = pb < kPosLdsFast ? spos[pb] : kLog2e * a.pos_table[h * Bp + pb];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) c[j] = 0.f;
       }
+      if (has_time) {
+        float tb[16];
+        if (info & kInfoNarrowTime) {
+          // floor(log2(1 + max(gap, 0))) of a gap that fits in int32
+          const int tq32 = static_cast<int>(tq);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int kvl = kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
+            const int gap = static_cast<int>(static_cast<unsigned>(tq32) - static_cast<unsigned>(rt[kvl]));
+            tb[j] = stime[min(31 - __builtin_clz(static_cast<unsigned>(max(gap, 0)) + 1u), Bt - 1)];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int kvl = kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
+            tb[j] = stime[time_bucket64(tq - rt[kvl], Bt)];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) c[j] += tb[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = fmaf(sc[j], alpha_l, c[j]);
     }
     float p[16];
     if (info & kInfoPolyAll) {
