@@ -100,6 +100,31 @@ __device__ __forceinline__ BlockClass classify_block(int qa, int ka, int n, bool
   return c;
 }
 
+// Time buckets of a block whose pairs need per-pair work (mask or varying
+// position buckets). Every valid pair's gap lies in [gmin, gmax] (from the
+// blocks' timestamp ranges), so its bucket lies in [lo, hi]; when that gap
+// range fits in int32 the wrapped difference of the timestamps' low words is
+// the gap itself.
+struct TimeSpan {
+  int lo, hi;
+  bool narrow;
+};
+
+__device__ __forceinline__ TimeSpan time_span(int64_t gmin, int64_t gmax, int Bt) {
+  TimeSpan t;
+  t.lo = time_bucket64(gmin, Bt);
+  t.hi = time_bucket64(gmax, Bt);
+  t.narrow = gmax <= int64_t(INT32_MAX) - 1 && gmin >= int64_t(INT32_MIN);
+  return t;
+}
+
+// floor(log2(1 + max(t_late - t_early, 0))), capped at Bt - 1, for a gap known
+// to fit in int32 (any other input still yields a bucket inside the table)
+__device__ __forceinline__ int time_bucket_narrow(int64_t t_late, int64_t t_early, int Bt) {
+  const int gap = static_cast<int>(static_cast<unsigned>(t_late) - static_cast<unsigned>(t_early));
+  return min(31 - __builtin_clz(static_cast<unsigned>(max(gap, 0)) + 1u), Bt - 1);
+}
+
 // Direct HBM -> LDS loads of one 64-row tile of two row-major matrices (A with
 // ACH, B with BCH 16-byte chunks per row), the rows' timestamps and the two
 // 32-row metadata records. Instruction i of a matrix is issued by wave i % kBW;
@@ -633,18 +658,54 @@ __global__ __launch_bounds__(kBThreads, 2) void attn_bwd_q_kernel(AttnBwdArgs g)
             ds[r] = da[r] * dsl;
           }
         } else {
+          // Per-pair buckets in two halves of 8 pairs, each issuing all its
+          // lookups before the first is used; one or two time buckets across
+          // the block's valid pairs take a compare-and-select instead (as in
+          // the key pass).
+          TimeSpan tsp{0, 0, false};
+          if (has_time) tsp = time_span(tq_min - tk_max, tq_max - tk_min, Bt);
+          const int64_t lim = tq - ((int64_t(1) << (tsp.lo + 1)) - 1);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kl = kvb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            const int kv = k0 + kl;
-            const bool valid = kv <= qrow && kv < n && qrow < n;
-            float cb = 0.f;
-            if (has_pos) cb = spos[min(max(qrow - kv, 0), Bp - 1)];
-            if (has_time) cb += stime[time_bucket64(tq - rt[kl], Bt)];
-            const float x = fmaf(s[r], alpha_l, cb);
-            float pl, dsl;
-            silu_and_grad(x, pl, dsl);
-            ds[r] = valid ? da[r] * dsl : 0.f;
+          for (int hf = 0; hf < 2; ++hf) {
+            float cb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * hf + e;
+              const int kv = k0 + kvb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+              cb[e] = has_pos ? spos[min(max(qrow - kv, 0), Bp - 1)] : 0.f;
+            }
+            if (has_time) {
+              if (tsp.hi - tsp.lo <= 1) {
+                const float vlo = stime[tsp.lo], vhi = stime[tsp.hi];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                  const int r = 8 * hf + e;
+                  cb[e] += tsp.hi > tsp.lo && rt[kvb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)] <= lim ? vhi : vlo;
+                }
+              } else if (tsp.narrow) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                  const int r = 8 * hf + e;
+                  cb[e] += stime[time_bucket_narrow(tq, rt[kvb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)], Bt)];
+                }
+              } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                  const int r = 8 * hf + e;
+                  cb[e] += stime[time_bucket64(tq - rt[kvb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)], Bt)];
+                }
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * hf + e;
+              const int kv = k0 + kvb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+              const bool valid = kv <= qrow && kv < n && qrow < n;
+              const float x = fmaf(s[r], alpha_l, cb[e]);
+              float pl, dsl;
+              silu_and_grad(x, pl, dsl);
+              ds[r] = valid ? da[r] * dsl : 0.f;
+            }
           }
         }
       }
