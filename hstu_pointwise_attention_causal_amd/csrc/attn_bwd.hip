@@ -118,13 +118,6 @@ __device__ __forceinline__ TimeSpan time_span(int64_t gmin, int64_t gmax, int Bt
   return t;
 }
 
-// floor(log2(1 + max(t_late - t_early, 0))), capped at Bt - 1, for a gap known
-// to fit in int32 (any other input still yields a bucket inside the table)
-__device__ __forceinline__ int time_bucket_narrow(int64_t t_late, int64_t t_early, int Bt) {
-  const int gap = static_cast<int>(static_cast<unsigned>(t_late) - static_cast<unsigned>(t_early));
-  return min(31 - __builtin_clz(static_cast<unsigned>(max(gap, 0)) + 1u), Bt - 1);
-}
-
 // Direct HBM -> LDS loads of one 64-row tile of two row-major matrices (A with
 // ACH, B with BCH 16-byte chunks per row), the rows' timestamps and the two
 // 32-row metadata records. Instruction i of a matrix is issued by wave i % kBW;

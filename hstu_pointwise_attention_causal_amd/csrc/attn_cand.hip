@@ -248,14 +248,15 @@ __global__ __launch_bounds__(kCWaves * 64, 2) void attn_cand_kernel(CandArgs a) 
       // position term: constant when every key of the block is >= Bp-1 back
       const bool pos_const = !has_pos || (n - (ka + 31) >= Bp - 1);
       // time term: constant when the block's bucket range is one bucket
-      int tlo = 0;
-      bool time_const = true;
+      int tlo = 0, thi = 0;
+      bool time_const = true, narrow = false;
       if (has_time) {
-        const int64_t bmin = __shfl(kmin, 32 * kvb, 64), bmax = __shfl(kmax, 32 * kvb, 64);
-        tlo = time_bucket64(uniform_i64(tc_min) - uniform_i64(bmax), Bt);
-        const int thi = time_bucket64(uniform_i64(tc_max) - uniform_i64(bmin), Bt);
-        time_const = __builtin_amdgcn_readfirstlane(tlo) == __builtin_amdgcn_readfirstlane(thi);
-        tlo = __builtin_amdgcn_readfirstlane(tlo);
+        const int64_t bmin = uniform_i64(__shfl(kmin, 32 * kvb, 64)), bmax = uniform_i64(__shfl(kmax, 32 * kvb, 64));
+        tlo = __builtin_amdgcn_readfirstlane(time_bucket64(tc_min - bmax, Bt));
+        thi = __builtin_amdgcn_readfirstlane(time_bucket64(tc_max - bmin, Bt));
+        time_const = tlo == thi;
+        // gaps of valid pairs lie in [tc_min - bmax, tc_max - bmin]
+        narrow = tc_max - bmin <= int64_t(INT32_MAX) - 1 && tc_min - bmax >= int64_t(INT32_MIN);
       }
       const bool tail = ka + 31 >= n;   // keys past the history: masked
       float p[16];
@@ -264,17 +265,49 @@ __global__ __launch_bounds__(kCWaves * 64, 2) void attn_cand_kernel(CandArgs a) 
 #pragma unroll
         for (int j = 0; j < 16; ++j) p[j] = silu2_exact(fmaf(s[j], alpha_l, c));
       } else {
+        // Per-pair terms. Each branch is uniform over the wave and taken once
+        // per block, and each loop issues all its lookups before the first is
+        // used. Keys j of this lane: t * kCBN + kvb * 32 + 8 (j / 4) + 4 lh + j % 4.
+        float c[16];
+        if (has_pos && !pos_const && Bp <= kCPosLds) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            c[j] = spos[min(max(n - (t * kCBN + kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)), 0), Bp - 1)];
+        } else if (has_pos && !pos_const) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int pb = min(max(n - (t * kCBN + kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)), 0), Bp - 1);
+            c[j] = pb < kCPosLds ? spos[pb] : kLog2e * a.pos_table[h * Bp + pb];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) c[j] = has_pos ? pos_far : 0.f;
+        }
+        if (has_time) {
+          if (time_const) {
+            const float v = stime[tlo];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) c[j] += v;
+          } else if (thi == tlo + 1) {
+            // bucket thi exactly when tc - t_j >= 2^(tlo+1) - 1
+            const int64_t lim = tc - ((int64_t(1) << (tlo + 1)) - 1);
+            const float vlo = stime[tlo], vhi = stime[thi];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) c[j] += rt[kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)] <= lim ? vhi : vlo;
+          } else if (narrow) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              c[j] += stime[time_bucket_narrow(tc, rt[kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)], Bt)];
+          } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              c[j] += stime[time_bucket64(tc - rt[kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)], Bt)];
+          }
+        }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int kl = kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);   // key within the tile
-          const int key = t * kCBN + kl;
-          float c = 0.f;
-          if (has_pos) {
-            const int pb = min(max(n - key, 0), Bp - 1);
-            c = pos_const ? pos_far : (pb < kCPosLds ? spos[pb] : kLog2e * a.pos_table[h * Bp + pb]);
-          }
-          if (has_time) c += time_const ? stime[tlo] : stime[time_bucket64(tc - rt[kl], Bt)];
-          p[j] = key < n ? silu2_exact(fmaf(s[j], alpha_l, c)) : 0.f;
+          const int key = t * kCBN + kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
+          p[j] = key < n ? silu2_exact(fmaf(s[j], alpha_l, c[j])) : 0.f;
         }
       }
       pv(rv, kvb, p);

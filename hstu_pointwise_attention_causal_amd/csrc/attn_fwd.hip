@@ -453,14 +453,9 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
       if (has_time) {
         float tb[16];
         if (info & kInfoNarrowTime) {
-          // floor(log2(1 + max(gap, 0))) of a gap that fits in int32
-          const int tq32 = static_cast<int>(tq);
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int kvl = kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
-            const int gap = static_cast<int>(static_cast<unsigned>(tq32) - static_cast<unsigned>(rt[kvl]));
-            tb[j] = stime[min(31 - __builtin_clz(static_cast<unsigned>(max(gap, 0)) + 1u), Bt - 1)];
-          }
+          for (int j = 0; j < 16; ++j)
+            tb[j] = stime[time_bucket_narrow(tq, rt[kvb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)], Bt)];
         } else {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {

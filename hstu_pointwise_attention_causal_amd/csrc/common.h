@@ -58,4 +58,12 @@ __device__ __forceinline__ int time_bucket64(int64_t dt, int nb) {
   return min(c, nb - 1);
 }
 
+// The same bucket of the gap t_late - t_early when that gap is known to fit
+// in int32: the wrapped difference of the low words is then the gap itself.
+// (Any other input still yields a bucket in [0, nb - 1].)
+__device__ __forceinline__ int time_bucket_narrow(int64_t t_late, int64_t t_early, int nb) {
+  const int gap = static_cast<int>(static_cast<unsigned>(t_late) - static_cast<unsigned>(t_early));
+  return min(31 - __builtin_clz(static_cast<unsigned>(max(gap, 0)) + 1u), nb - 1);
+}
+
 }  // namespace hstu
