@@ -129,4 +129,35 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Largest / smallest value over the wave as a wave-uniform (scalar) value: a
+// DPP reduction inside each row of 16 lanes, then the four row results read
+// back with v_readlane. fmaxf / fminf drop a NaN operand: a caller that must
+// see NaN tests for it separately.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max_uniform(float v) {
+  v = fmaxf(v, dpp_row<0xB1>(v));    // quad [1,0,3,2]
+  v = fmaxf(v, dpp_row<0x4E>(v));    // quad [2,3,0,1]
+  v = fmaxf(v, dpp_row<0x141>(v));   // half-row mirror
+  v = fmaxf(v, dpp_row<0x140>(v));   // row mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float wave_min_uniform(float v) {
+  v = fminf(v, dpp_row<0xB1>(v));
+  v = fminf(v, dpp_row<0x4E>(v));
+  v = fminf(v, dpp_row<0x141>(v));
+  v = fminf(v, dpp_row<0x140>(v));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fminf(fminf(r0, r1), fminf(r2, r3));
+}
+
 }  // namespace hstu

@@ -215,6 +215,26 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
   const BlockMeta* meta_row =
       static_cast<const BlockMeta*>(a.meta) + h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * a.tile_base[b];
 
+  // The loads of the prologue go out first, so that their latencies overlap
+  // with the table staging and the reductions below: key tile 0 and this
+  // lane's Q row.
+  const int kv_end = min(n, q0 + kAttnBM);
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+  const char* kbase = static_cast<const char*>(a.k) + (seq0 * a.ldk + h * DQK) * 2;
+  const char* vbase = static_cast<const char*>(a.v) + (seq0 * a.ldv + h * DV) * 2;
+  auto issue_tile = [&] __device__(int kt, char* dk, char* dv, int64_t* dt) {
+    issue_tile_loads<KCH, VCH>(kbase, vbase, has_time ? a.ts + seq0 : nullptr, a.ldk, a.ldv, n, kt * kBN, w, lane,
+                               dk, dv, dt);
+  };
+  if (ntiles > 0) issue_tile(0, sm.k[0], sm.v[0], sm.t[0]);
+
+  const __bf16* qp = static_cast<const __bf16*>(a.q);
+  bf16x8_t qf[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    qf[kb] = qrow < n ? *reinterpret_cast<const bf16x8_t*>(qp + (seq0 + qrow) * a.ldq + h * DQK + kb * 16 + lh * 8)
+                      : bf16x8_t{};
+
   if (has_pos) {
     for (int i = tid; i < min(Bp, kPosLdsFast); i += kThreads) sm.pos[i] = kLog2e * a.pos_table[h * Bp + i];
   }
@@ -238,35 +258,21 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
       tmax_ = fmaxf(tmax_, x);
       bad |= !(x == x);
     }
-  for (int o = 1; o < 64; o <<= 1) {
-    pmax = fmaxf(pmax, __shfl_xor(pmax, o, 64));
-    tmax_ = fmaxf(tmax_, __shfl_xor(tmax_, o, 64));
-  }
-  // wave-uniform values are moved to scalar registers
+  // wave-uniform values live in scalar registers
   const float cmax = __builtin_amdgcn_ballot_w64(bad) ? __builtin_nanf("")
-                                                      : __int_as_float(__builtin_amdgcn_readfirstlane(
-                                                            __float_as_int(pmax + tmax_)));
+                                                      : wave_max_uniform(pmax) + wave_max_uniform(tmax_);
 
-  const __bf16* qp = static_cast<const __bf16*>(a.q);
-  bf16x8_t qf[KB];
   float qsq = 0.f;
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    qf[kb] = qrow < n ? *reinterpret_cast<const bf16x8_t*>(qp + (seq0 + qrow) * a.ldq + h * DQK + kb * 16 + lh * 8)
-                      : bf16x8_t{};
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int i = 0; i < 8; ++i) qsq = fmaf(static_cast<float>(qf[kb][i]), static_cast<float>(qf[kb][i]), qsq);
-  }
   qsq += __shfl_xor(qsq, 32, 64);
   const float alpha_l = a.alpha * kLog2e;
   const float qbound = fabsf(alpha_l) * __builtin_sqrtf(qsq);   // |alpha| log2(e) |q_i|
-  float qbound_max = qbound;
-  for (int o = 1; o < 64; o <<= 1) qbound_max = fmaxf(qbound_max, __shfl_xor(qbound_max, o, 64));
-  if (__builtin_amdgcn_ballot_w64(qbound != qbound)) qbound_max = __builtin_nanf("");
-  qbound_max = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(qbound_max)));
-  float qbound_min = qrow < n ? qbound : __builtin_inff();   // smallest row bound of the wave
-  for (int o = 1; o < 64; o <<= 1) qbound_min = fminf(qbound_min, __shfl_xor(qbound_min, o, 64));
-  qbound_min = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(qbound_min)));
+  const float qbound_max =
+      __builtin_amdgcn_ballot_w64(qbound != qbound) ? __builtin_nanf("") : wave_max_uniform(qbound);
+  const float qbound_min = wave_min_uniform(qrow < n ? qbound : __builtin_inff());   // smallest row bound
   const int64_t tq = (has_time && qrow < n) ? a.ts[seq0 + qrow] : 0;
   int64_t wq_min = 0, wq_max = 0;   // timestamps of this wave's query rows (metadata of its block)
   if (has_time && qa < n) {
@@ -278,16 +284,6 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16_t{};
 
-  const int kv_end = min(n, q0 + kAttnBM);
-  const int ntiles = (kv_end + kBN - 1) / kBN;
-
-  const char* kbase = static_cast<const char*>(a.k) + (seq0 * a.ldk + h * DQK) * 2;
-  const char* vbase = static_cast<const char*>(a.v) + (seq0 * a.ldv + h * DV) * 2;
-
-  auto issue_tile = [&] __device__(int kt, char* dk, char* dv, int64_t* dt) {
-    issue_tile_loads<KCH, VCH>(kbase, vbase, has_time ? a.ts + seq0 : nullptr, a.ldk, a.ldv, n, kt * kBN, w, lane,
-                               dk, dv, dt);
-  };
   const int per_tile = loads_per_tile<KCH, VCH>(w);
 
   // ---- LDS byte offsets of this lane's operand fragments inside one buffer
@@ -559,8 +555,7 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
     tile_barrier();   // ... and every other wave's; tile kt's buffers are free
   };
 
-  // tile 0 in flight, then wait for it
-  if (ntiles > 0) issue_tile(0, sm.k[0], sm.v[0], sm.t[0]);
+  // tile 0 (in flight since the prologue) lands
   wait_vmcnt(0);
   __syncthreads();   // also publishes the bias tables staged with ordinary LDS stores
 
