@@ -40,6 +40,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBufs = 2;           // K/V tiles in flight (2 workgroups per CU fit in LDS)
 constexpr int kPosLds = 1024;      // position-table entries staged in LDS
 constexpr int kTimeLds = 64;       // time buckets reachable with int64 gaps: 0..62
+constexpr int64_t kFwdSplitItemBound = 512;   // work-list bound below which the key-range-split kernel runs
 
 struct BiasLds {
   float pos[kPosLds];
@@ -161,11 +162,12 @@ __device__ __forceinline__ int loads_per_tile(int w) {
   return c + (w == 0 ? 1 : 0);
 }
 
-template <int DQK, int DV>
+// HALVES: 2 for the key-range-split kernel (one tile pipeline per half)
+template <int DQK, int DV, int HALVES>
 struct FwdSmem {
-  __attribute__((aligned(16))) char k[kBufs][kBN * DQK * 2];
-  __attribute__((aligned(16))) char v[kBufs][kBN * DV * 2];
-  __attribute__((aligned(16))) int64_t t[kBufs][kBN];
+  __attribute__((aligned(16))) char k[HALVES][kBufs][kBN * DQK * 2];
+  __attribute__((aligned(16))) char v[HALVES][kBufs][kBN * DV * 2];
+  __attribute__((aligned(16))) int64_t t[HALVES][kBufs][kBN];
   float pos[kPosLdsFast];   // log2(e) * P[h][0 .. min(Bp, 1024))
   float time[kTimeLds];     // log2(e) * Tt[h][0 .. min(Bt, 64))
 };
@@ -181,8 +183,15 @@ constexpr int kInfoExactAll = 1 << 10;   // no row of the wave qualifies for the
 constexpr int kInfoNarrowTime = 1 << 11; // every gap t_i - t_j of the block's pairs fits in int32
 constexpr int kInfoEmpty = 1 << 12;      // no pair of the block is causal and inside the sequence
 
-template <int DQK, int DV>
-__global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_kernel(AttnArgs a) {
+// SPLIT: eight waves per workgroup. Waves 0-3 take key tiles [0, qt + 1) of
+// the item and waves 4-7 the rest up to the diagonal, each group with its own
+// double-buffered tiles; the groups run the same number of steps (the second
+// group's spare step, if any, lies past the diagonal and does no work), and
+// the second group's fp32 sums are added to the first group's through LDS, in
+// that order, before the store. For short work lists, where one workgroup per
+// compute unit would leave one wave per SIMD.
+template <int DQK, int DV, bool SPLIT>
+__global__ __launch_bounds__(SPLIT ? 2 * kThreads : kThreads, SPLIT ? 1 : 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims");
   constexpr int KB = DQK / 16;            // k-blocks of QK^T
   constexpr int NB = DV / 32;             // 32-wide column blocks of O
@@ -190,7 +199,8 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
   constexpr int VCH = DV / 8;             // 16-byte chunks per V row
   constexpr int KINST = (KCH + kWaves - 1) / kWaves;   // direct loads per wave per K tile (64 lanes x 16 B)
   constexpr int VINST = (VCH + kWaves - 1) / kWaves;
-  using Smem = FwdSmem<DQK, DV>;
+  using Smem = FwdSmem<DQK, DV, SPLIT ? 2 : 1>;
+  constexpr int kT = SPLIT ? 2 * kThreads : kThreads;
 
   const int item_idx = blockIdx.x;
   if (item_idx >= *a.item_count) return;
@@ -203,7 +213,8 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
   __shared__ Smem sm;
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(SPLIT ? (tid >> 6) & (kWaves - 1) : tid >> 6);   // query wave of its group
+  const int half = SPLIT ? __builtin_amdgcn_readfirstlane(tid >> 8) : 0;      // key-range group
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
   const int qa = q0 + 32 * w;                 // first query row of this wave
   const int qrow = qa + lr;                   // this lane's query column of S^T
@@ -220,13 +231,15 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
   // lane's Q row.
   const int kv_end = min(n, q0 + kAttnBM);
   const int ntiles = (kv_end + kBN - 1) / kBN;
+  const int kt_begin = SPLIT && half == 1 ? qt + 1 : 0;   // this group's first key tile
+  const int nsteps = SPLIT ? qt + 1 : ntiles;          // steps of every group
   const char* kbase = static_cast<const char*>(a.k) + (seq0 * a.ldk + h * DQK) * 2;
   const char* vbase = static_cast<const char*>(a.v) + (seq0 * a.ldv + h * DV) * 2;
   auto issue_tile = [&] __device__(int kt, char* dk, char* dv, int64_t* dt) {
     issue_tile_loads<KCH, VCH>(kbase, vbase, has_time ? a.ts + seq0 : nullptr, a.ldk, a.ldv, n, kt * kBN, w, lane,
                                dk, dv, dt);
   };
-  if (ntiles > 0) issue_tile(0, sm.k[0], sm.v[0], sm.t[0]);
+  if (ntiles > 0) issue_tile(kt_begin, sm.k[half][0], sm.v[half][0], sm.t[half][0]);
 
   const __bf16* qp = static_cast<const __bf16*>(a.q);
   bf16x8_t qf[KB];
@@ -236,10 +249,10 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
                       : bf16x8_t{};
 
   if (has_pos) {
-    for (int i = tid; i < min(Bp, kPosLdsFast); i += kThreads) sm.pos[i] = kLog2e * a.pos_table[h * Bp + i];
+    for (int i = tid; i < min(Bp, kPosLdsFast); i += kT) sm.pos[i] = kLog2e * a.pos_table[h * Bp + i];
   }
   if (has_time) {
-    for (int i = tid; i < min(Bt, kTimeLds); i += kThreads) sm.time[i] = kLog2e * a.time_table[h * Bt + i];
+    for (int i = tid; i < min(Bt, kTimeLds); i += kT) sm.time[i] = kLog2e * a.time_table[h * Bt + i];
   }
   const float pos_last = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(
       has_pos ? kLog2e * a.pos_table[h * Bp + Bp - 1] : 0.f)));   // bias of far pairs
@@ -284,7 +297,6 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16_t{};
 
-  const int per_tile = loads_per_tile<KCH, VCH>(w);
 
   // ---- LDS byte offsets of this lane's operand fragments inside one buffer
   uint32_t k_lds[KB];                       // K row (kvb*32 + lr): + kvb * 32 * KCH * 16
@@ -515,8 +527,8 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
     const int k0 = kt * kBN;
     // tile kt + 1 reuses the buffer of tile kt - 1, released by the last barrier
     issue_tile(kt + 1, dk, dv, dt);
-    if ((kt & 31) == 0) classify_window(kt >> 5, stime);
-    const bool active = qa < n && k0 <= qa + 31;
+    if ((SPLIT && kt == kt_begin) || (kt & 31) == 0) classify_window(kt >> 5, stime);
+    const bool active = qa < n && k0 <= qa + 31 && (!SPLIT || kt < ntiles);
     bf16x8_t kf[2 * KB];
     if (active) read_k(rk, kf);
     if (prev_active) pv_mfma(vf1, p1);
@@ -559,12 +571,40 @@ __global__ __launch_bounds__(kThreads, kWaves <= 4 ? 2 : 1) void attn_fwd_bf16_k
   wait_vmcnt(0);
   __syncthreads();   // also publishes the bias tables staged with ordinary LDS stores
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt % kBufs, nxt = (kt + 1) % kBufs;
-    tile_step(sm.k[buf], sm.v[buf], sm.t[buf], sm.k[nxt], sm.v[nxt], sm.t[nxt], sm.pos, sm.time, kt);
+  for (int kt = kt_begin; kt < kt_begin + nsteps; ++kt) {
+    const int buf = (kt - kt_begin) % kBufs, nxt = (kt - kt_begin + 1) % kBufs;
+    tile_step(sm.k[half][buf], sm.v[half][buf], sm.t[half][buf], sm.k[half][nxt], sm.v[half][nxt],
+              sm.t[half][nxt], sm.pos, sm.time, kt);
   }
   if (prev_active) pv_mfma(vf1, p1);
   wait_vmcnt(0);
+
+  if constexpr (SPLIT) {
+    // the second group's sums, through its own (now idle) tile buffers: 16
+    // floats x NB x 64 lanes per wave, two waves in the K buffers, two in V
+    __syncthreads();   // every wave's loads have landed; no wave reads a tile buffer any more
+    float* red = reinterpret_cast<float*>(w < 2 ? &sm.k[1][0][0] : &sm.v[1][0][0]) + (w & 1) * (NB * 16 * 64);
+    if (half == 1) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(red + ((nb * 4 + g) * 64 + lane) * 4) =
+              make_float4(oacc[nb][4 * g], oacc[nb][4 * g + 1], oacc[nb][4 * g + 2], oacc[nb][4 * g + 3]);
+    }
+    __syncthreads();
+    if (half == 1) return;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 x = *reinterpret_cast<const float4*>(red + ((nb * 4 + g) * 64 + lane) * 4);
+        oacc[nb][4 * g] += x.x;
+        oacc[nb][4 * g + 1] += x.y;
+        oacc[nb][4 * g + 2] += x.z;
+        oacc[nb][4 * g + 3] += x.w;
+      }
+  }
 
   // ---- epilogue: oacc[nb][j] = 2 log2(e) * N * O[qa + 8(j/4) + 4 lh + j%4][nb*32 + lr]
   const float scale = (a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n)) / (2.0f * kLog2e);
@@ -730,13 +770,22 @@ hipError_t launch_attn_block_meta(const AttnArgs& a, int dqk, hipStream_t stream
   return hipErrorInvalidValue;
 }
 
+template <int DQK, int DV>
+hipError_t launch_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
+  // A work list that fits the chip at one workgroup per compute unit (or
+  // little more) runs the key-range-split kernel: two waves per SIMD instead
+  // of one, and half the longest item's chain.
+  if (a.capacity < kFwdSplitItemBound) return launch_items(attn_fwd_bf16_kernel<DQK, DV, true>, a, 2 * kThreads, stream);
+  return launch_items(attn_fwd_bf16_kernel<DQK, DV, false>, a, kThreads, stream);
+}
+
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int dqk, int dv, hipStream_t stream) {
   hipError_t e = launch_attn_block_meta(a, dqk, stream);
   if (e != hipSuccess) return e;
   TimedScope timed(kTimedAttnFwd, stream);
-  if (dqk == 128 && dv == 128) return launch_items(attn_fwd_bf16_kernel<128, 128>, a, kThreads, stream);
-  if (dqk == 64 && dv == 64) return launch_items(attn_fwd_bf16_kernel<64, 64>, a, kThreads, stream);
-  if (dqk == 32 && dv == 32) return launch_items(attn_fwd_bf16_kernel<32, 32>, a, kThreads, stream);
+  if (dqk == 128 && dv == 128) return launch_fwd_bf16<128, 128>(a, stream);
+  if (dqk == 64 && dv == 64) return launch_fwd_bf16<64, 64>(a, stream);
+  if (dqk == 32 && dv == 32) return launch_fwd_bf16<32, 32>(a, stream);
   return hipErrorInvalidValue;
 }
 

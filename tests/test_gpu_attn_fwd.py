@@ -90,22 +90,33 @@ def test_large_and_mixed_score_ranges(hstu):
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
-def test_trailing_empty_sequences_leave_outputs_bitwise(hstu, d):
-    """Appending 600 empty sequences to a batch of long, ragged ones makes the
-    work-list bound ten times larger (every sequence reserves a query tile per
-    head) but adds no work: every output row is bitwise the same, and both
-    runs match the oracle. The 4100-token sequence walks key tiles past the
-    32-tile window of the per-block bias classification."""
+def test_short_and_long_work_lists(hstu, d):
+    """The same long, ragged sequences as a short work list (under 512 items:
+    the kernel whose workgroups split each item's key range between two wave
+    groups and add the halves' fp32 sums through LDS) and, padded with 600
+    empty sequences, as a long one (one wave group per item). Both match the
+    oracle and differ from each other by the order of one fp32 addition only.
+    The 4100-token sequence walks key tiles past the 32-tile window of the
+    per-block bias classification, in both halves."""
     import dataclasses
     lengths = [1500, 700, 513, 512, 90, 4100, 641]
     wl = _attn_recipe("pad", 300 + d, lengths, 2, d)
     ref = _oracle(wl)
-    base = _run(hstu, wl)
+    short = _run(hstu, wl)
     off = np.asarray(wl.seq_offsets)
     padded = dataclasses.replace(wl, seq_offsets=np.concatenate([off, np.full(600, off[-1], off.dtype)]))
-    out = _run(hstu, padded)
-    assert rel_err(base, ref) <= TOL_BF16
-    assert np.array_equal(base, out)
+    long_ = _run(hstu, padded)
+    assert rel_err(short, ref) <= TOL_BF16
+    assert rel_err(long_, ref) <= TOL_BF16
+    assert rel_err(short, long_) <= 2.0 ** -6   # two bf16 ulps of the largest output
+
+
+def test_split_kernel_edge_items(hstu):
+    """Short work list (key-range-split kernel) with items whose second half
+    has no tile (sequences of at most 64 tokens), a spare step (a last query
+    tile of 65..128 rows), exactly one tile each, and an empty sequence."""
+    wl = _attn_recipe("splitedge", 41, [64, 1, 65, 128, 129, 193, 0, 257, 320], 3, 64)
+    assert rel_err(_run(hstu, wl), _oracle(wl)) <= TOL_BF16
 
 
 def test_nan_in_neighbour_sequence_does_not_leak(hstu):
