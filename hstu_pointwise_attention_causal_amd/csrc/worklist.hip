@@ -49,10 +49,23 @@ __device__ int block_inclusive_scan(int v, int* total) {
   return x + prefix;
 }
 
+// Counters and scans of the builder live in LDS when the levels and the
+// sequences fit (LDS atomics and reads instead of global-memory round trips in
+// every phase); tile_base is also copied out, for the attention kernels.
+constexpr int kLdsLevels = 4096;   // num_levels + 1 entries per array
+constexpr int kLdsSeqs = 4096;     // B + 1 entries
+
+template <bool LDS>
 __global__ __launch_bounds__(kBuildThreads) void build_worklist_kernel(
     const int64_t* __restrict__ off, int B, int H, int BM, int num_levels,
-    int* __restrict__ hdr, int* __restrict__ hist, int* __restrict__ level_start,
-    int* __restrict__ fill, int* __restrict__ tile_base, WorkItem* __restrict__ items) {
+    int* __restrict__ hdr, int* __restrict__ hist_g, int* __restrict__ level_start_g,
+    int* __restrict__ fill_g, int* __restrict__ tile_base_g, WorkItem* __restrict__ items) {
+  __shared__ int lds_hist[LDS ? kLdsLevels : 1], lds_level_start[LDS ? kLdsLevels : 1],
+      lds_fill[LDS ? kLdsLevels : 1], lds_tile_base[LDS ? kLdsSeqs : 1];
+  int* hist = LDS ? lds_hist : hist_g;
+  int* level_start = LDS ? lds_level_start : level_start_g;
+  int* fill = LDS ? lds_fill : fill_g;
+  int* tile_base = LDS ? lds_tile_base : tile_base_g;
   const int tid = threadIdx.x;
   for (int i = tid; i <= num_levels; i += kBuildThreads) {
     hist[i] = 0;
@@ -90,7 +103,8 @@ __global__ __launch_bounds__(kBuildThreads) void build_worklist_kernel(
     int r = r0 + tid;
     int qt = num_levels - 1 - r;
     int h = (r < num_levels)
-                ? __hip_atomic_load(&hist[qt + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                ? __hip_atomic_load(&hist[qt + 1], __ATOMIC_RELAXED,
+                                    LDS ? __HIP_MEMORY_SCOPE_WORKGROUP : __HIP_MEMORY_SCOPE_AGENT)
                 : 0;
     int chunk_total;
     int incl = block_inclusive_scan(h, &chunk_total);
@@ -130,6 +144,8 @@ __global__ __launch_bounds__(kBuildThreads) void build_worklist_kernel(
       items[base + h] = w;
     }
   }
+  if (LDS)
+    for (int i = tid; i <= B; i += kBuildThreads) tile_base_g[i] = tile_base[i];
   if (tid == 0) {
     hdr[0] = total_tiles * H;
     hdr[1] = 0;
@@ -164,13 +180,18 @@ WorklistLayout worklist_layout(int B, int64_t T, int H, int BM) {
 
 hipError_t launch_build_worklist(const int64_t* off, int B, int H, int BM, const WorklistLayout& L,
                                  char* ws, hipStream_t stream) {
-  hipLaunchKernelGGL(build_worklist_kernel, dim3(1), dim3(kBuildThreads), 0, stream, off, B, H, BM,
-                     L.num_levels - 1, reinterpret_cast<int*>(ws + L.hdr_off),
-                     reinterpret_cast<int*>(ws + L.hist_off),
-                     reinterpret_cast<int*>(ws + L.level_start_off),
-                     reinterpret_cast<int*>(ws + L.fill_off),
-                     reinterpret_cast<int*>(ws + L.tile_base_off),
-                     reinterpret_cast<WorkItem*>(ws + L.items_off));
+  int* hdr = reinterpret_cast<int*>(ws + L.hdr_off);
+  int* hist = reinterpret_cast<int*>(ws + L.hist_off);
+  int* level_start = reinterpret_cast<int*>(ws + L.level_start_off);
+  int* fill = reinterpret_cast<int*>(ws + L.fill_off);
+  int* tile_base = reinterpret_cast<int*>(ws + L.tile_base_off);
+  WorkItem* items = reinterpret_cast<WorkItem*>(ws + L.items_off);
+  if (L.num_levels + 1 <= kLdsLevels && B + 1 <= kLdsSeqs)
+    hipLaunchKernelGGL(build_worklist_kernel<true>, dim3(1), dim3(kBuildThreads), 0, stream, off, B, H, BM,
+                       L.num_levels - 1, hdr, hist, level_start, fill, tile_base, items);
+  else
+    hipLaunchKernelGGL(build_worklist_kernel<false>, dim3(1), dim3(kBuildThreads), 0, stream, off, B, H, BM,
+                       L.num_levels - 1, hdr, hist, level_start, fill, tile_base, items);
   return hipGetLastError();
 }
 

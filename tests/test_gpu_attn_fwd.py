@@ -119,6 +119,15 @@ def test_split_kernel_edge_items(hstu):
     assert rel_err(_run(hstu, wl), _oracle(wl)) <= TOL_BF16
 
 
+def test_many_short_sequences(hstu):
+    """5000 sequences of 0..9 tokens: more sequences than the work-list
+    builder keeps in LDS, so its counters and scans go through global memory;
+    a long list (one wave group per item)."""
+    lengths = np.random.default_rng(77).integers(0, 10, size=5000).tolist()
+    wl = _attn_recipe("many", 78, lengths, 2, 32)
+    assert rel_err(_run(hstu, wl), _oracle(wl)) <= TOL_BF16
+
+
 def test_nan_in_neighbour_sequence_does_not_leak(hstu):
     import torch
     wl = _attn_recipe("nan", 10, [200, 150, 90], 2, 128)
