@@ -113,6 +113,11 @@ hstu_status_t hstu_attn_workspace_size(const hstu_attn_desc_t* desc, const hstu_
  *   bf16 output; HSTU_F32: fp32 throughout). bias may be NULL (no bias).
  *   workspace: device scratch of at least hstu_attn_workspace_size(...,0,...)
  *   bytes (holds the per-tile work list); contents on entry are ignored.
+ * Results are deterministic run to run. A row's bf16 output does not depend on
+ * later tokens of its sequence. With fewer than 512 work items in the bound
+ * (H times the query tiles the batch can hold), the bf16 path sums each
+ * query tile's two key-range halves separately and adds them, so the same
+ * sequence in a batch of a different size may differ in the last bit.
  * Errors: HSTU_E_NULL, HSTU_E_SHAPE, HSTU_E_DTYPE, HSTU_E_ALIGN,
  *   HSTU_E_UNSUPPORTED, HSTU_E_WORKSPACE, HSTU_E_ALIAS, HSTU_E_HIP.
  * ------------------------------------------------------------------------- */
