@@ -412,6 +412,22 @@ constexpr int kColSumRows = 16;
 // resident on an XCD share that band in L2 and read each table tile together.
 constexpr int kHeadGroupRows = 8;
 
+// Workgroups of the head GEMM: one per compute unit of the current device (its
+// 256 x 256 tiles take a unit's LDS), rounded down to a multiple of 8, each
+// looping over tiles so that one tile's logit stores drain while the next
+// tile's products run. 0 (one workgroup per tile) if the count is unknown.
+int head_gemm_blocks() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const int blocks = cus / 8 * 8;
+  if (dev >= 0 && dev < 64) cached[dev] = blocks;
+  return blocks;
+}
+
 int weight_grad_splits(int64_t M, int64_t N, int64_t T) {
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   const int64_t ksteps = (T + 63) / 64;
@@ -780,6 +796,7 @@ hstu_status_t hstu_head_fwd(int64_t rows, int32_t dim, int64_t vocab, float eps,
   g.a = workspace; g.lda = dim; g.b = table; g.ldb = ldt; g.c = logits; g.ldc = ldl;
   g.M = static_cast<int>(rows); g.N = static_cast<int>(vocab); g.K = dim;
   g.group_m = kHeadGroupRows;
+  g.blocks = head_gemm_blocks();
   if ((e = hstu::launch_head_gemm(g, stream)) != hipSuccess) return hip_fail(e, "head GEMM launch");
   return ok();
 }

@@ -35,6 +35,7 @@ struct GemmArgs {
   int64_t split_stride;   // elements between split partials (kEpiF32)
   int M, N, K;
   int group_m;         // > 1: tile order in bands of group_m tile rows, column by column
+  int blocks;          // > 0: that many workgroups (a multiple of 8), each looping over tiles; 0: one per tile
 };
 
 // y = LN(x) * gamma + beta (optionally * gate), rows of `width` features, bf16 in/out.

@@ -238,9 +238,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 2) void gemm_kernel(Gem
   // With group_m > 1 the order walks bands of group_m tile rows column by
   // column instead, so the workgroups resident on one XCD share a short band
   // of A rows and a few B tiles (for outputs far wider than tall).
+  // A grid smaller than the tile count (a multiple of 8 workgroups) loops:
+  // workgroup b takes virtual blocks b, b + grid, ..., each mapped as above, so
+  // a tile's stores drain while the next tile's products run.
   const int tiles_n = (g.N + BN - 1) / BN;
-  const int tiles = gridDim.x, xcd = blockIdx.x % 8, q = tiles / 8, r = tiles % 8;
-  const int t = xcd * q + min(xcd, r) + blockIdx.x / 8;
+  const int tiles = ((g.M + BM - 1) / BM) * tiles_n, q = tiles / 8, r = tiles % 8;
+  for (int vb = blockIdx.x; vb < tiles; vb += gridDim.x) {
+  const int xcd = vb % 8;
+  const int t = xcd * q + min(xcd, r) + vb / 8;
   int tm, tn;
   if (g.group_m > 1) {
     const int tiles_m = (g.M + BM - 1) / BM;
@@ -386,6 +391,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 2) void gemm_kernel(Gem
       *reinterpret_cast<bf16x8_t*>(cp + (static_cast<int64_t>(m) * g.ldc + n) * 2) = out;
     }
   }
+  // the staging area (A stage buffers) is read back before the next tile's loads refill it
+  if (vb + static_cast<int>(gridDim.x) < tiles) __syncthreads();
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -451,7 +459,8 @@ namespace {
 template <int EPI, int BM, int BN, int WM, int WN, int ST, bool AT, bool BT, int BK = 64>
 hipError_t launch_gemm_shape(const GemmArgs& g, int splits, hipStream_t stream) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<EPI, BM, BN, WM, WN, ST, AT, BT, BK>), dim3(tiles, splits),
+  const int grid = g.blocks > 0 && g.blocks < tiles ? g.blocks : tiles;
+  hipLaunchKernelGGL((gemm_kernel<EPI, BM, BN, WM, WN, ST, AT, BT, BK>), dim3(grid, splits),
                      dim3((BM / WM) * (BN / WN) * 64), 0, stream, g);
   return hipGetLastError();
 }
@@ -478,7 +487,7 @@ hipError_t check_gemm(const GemmArgs& g, int epi, bool a_kmajor, bool b_kmajor, 
   }
   if (epi == kEpiResidual && (g.ldr % 8 != 0 || !aligned(g.r, 16))) return hipErrorInvalidValue;
   if (epi == kEpiSiluPair && (g.ldc2 % 8 != 0 || !aligned(g.c2, 16))) return hipErrorInvalidValue;
-  if (g.group_m < 0) return hipErrorInvalidValue;
+  if (g.group_m < 0 || g.blocks < 0 || g.blocks % 8 != 0) return hipErrorInvalidValue;
   return hipSuccess;
 }
 }  // namespace
