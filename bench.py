@@ -30,6 +30,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -49,18 +50,27 @@ LAUNCH_H = os.path.join(ROOT, "hstu_pointwise_attention_causal_amd", "csrc", "la
 COPY_BYTES = 1 << 30
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments, trailing blanks or empty lines (the
+    kernel files hold no string literal with a comment marker)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_hash() -> str:
-    """Hash of the sources the attention forward kernel is compiled from: its
-    own file and headers, and of the launch header only the argument struct
-    it reads (the header also declares every other kernel's launcher)."""
+    """Hash of the code the attention forward kernel is compiled from: its own
+    file and headers, and of the launch header only the argument struct it
+    reads (the header also declares every other kernel's launcher). Comments
+    are left out, so editing one keeps a counter measurement valid."""
     h = hashlib.sha256()
     for p in KERNEL_SRCS:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            h.update(_code_only(f.read()).encode())
     with open(LAUNCH_H) as f:
         text = f.read()
     start = text.index("struct AttnArgs {")
-    h.update(text[start:text.index("};", start)].encode())
+    h.update(_code_only(text[start:text.index("};", start)]).encode())
     return h.hexdigest()[:16]
 
 

@@ -18,8 +18,12 @@
 // key rows of the 32x32 block, which is the A-operand layout of the P.V
 // product once the 16 keys of a k-block are read in the permuted order
 // {4h..4h+3, 8+4h..8+4h+3} (h = lane / 32); V^T is read from LDS in the same
-// order, so no LDS round trip or cross-lane shuffle is needed between the two
-// products. V is transposed once per tile while it is staged into LDS.
+// order with transposing reads (ds_read_b64_tr_b16), so no LDS round trip or
+// cross-lane shuffle is needed between the two products.
+//
+// Short work lists (fewer items than two per compute unit) run the same code
+// with eight waves per workgroup: two groups of four split each item's key
+// range and add their sums through LDS (see attn_fwd_bf16_kernel).
 //
 // fp32 kernel (VALU): one thread per query row, fp32 throughout, for the
 // fp32 workload and as a precision reference path.
