@@ -128,6 +128,34 @@ def test_many_short_sequences(hstu):
     assert rel_err(_run(hstu, wl), _oracle(wl)) <= TOL_BF16
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_batches(hstu, seed):
+    """Seeded random batches: 1-12 sequences of 0-1500 tokens, 1-4 heads, head
+    dims 32/64/128, position and time biases on or off with random bucket
+    counts (beyond the 1024 position buckets staged in LDS for one seed in
+    four), score scale alpha and divisor. Odd seeds append 600 empty sequences,
+    so the long-list kernel runs; even seeds take the short-list kernel."""
+    import dataclasses
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 13))
+    lengths = np.floor(np.exp(rng.uniform(0.0, np.log(1501.0), size=B))).astype(int) - 1
+    H = int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([32, 64, 128]))
+    pos, time = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    Bp = int(rng.choice([16, 128, 1500])) if seed % 4 == 3 else int(rng.choice([16, 128]))
+    Bt = int(rng.choice([8, 32, 64]))
+    wl = _attn_recipe(f"rand{seed}", 2000 + seed, lengths.tolist(), H, d, pos=pos, time=time, Bp=Bp, Bt=Bt,
+                      table_std=float(rng.choice([0.02, 0.5])))
+    wl.alpha = float(rng.choice([1.0, 0.5]))
+    wl.divisor = float(rng.choice([0.0, 300.0]))
+    if seed % 2 == 1:
+        off = np.asarray(wl.seq_offsets)
+        wl = dataclasses.replace(wl, seq_offsets=np.concatenate([off, np.full(600, off[-1], off.dtype)]))
+    err = rel_err(_run(hstu, wl), _oracle(wl))
+    print(f"seed {seed}: B {B} H {H} d {d} pos {pos} time {time} Bp {Bp} Bt {Bt} err {err:.2e}")
+    assert err <= TOL_BF16
+
+
 def test_nan_in_neighbour_sequence_does_not_leak(hstu):
     import torch
     wl = _attn_recipe("nan", 10, [200, 150, 90], 2, 128)
