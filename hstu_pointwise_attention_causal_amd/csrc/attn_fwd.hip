@@ -157,15 +157,6 @@ __device__ __forceinline__ void issue_tile_loads(const char* kbase, const char* 
   }
 }
 
-// Direct loads this wave issues per tile (see issue_tile_loads).
-template <int KCH, int VCH>
-__device__ __forceinline__ int loads_per_tile(int w) {
-  int c = 0;
-  for (int i = w; i < KCH; i += kWaves) ++c;
-  for (int i = w; i < VCH; i += kWaves) ++c;
-  return c + (w == 0 ? 1 : 0);
-}
-
 // HALVES: 2 for the key-range-split kernel (one tile pipeline per half)
 template <int DQK, int DV, int HALVES>
 struct FwdSmem {
@@ -201,8 +192,6 @@ __global__ __launch_bounds__(SPLIT ? 2 * kThreads : kThreads, SPLIT ? 1 : 2) voi
   constexpr int NB = DV / 32;             // 32-wide column blocks of O
   constexpr int KCH = DQK / 8;            // 16-byte chunks per K row
   constexpr int VCH = DV / 8;             // 16-byte chunks per V row
-  constexpr int KINST = (KCH + kWaves - 1) / kWaves;   // direct loads per wave per K tile (64 lanes x 16 B)
-  constexpr int VINST = (VCH + kWaves - 1) / kWaves;
   using Smem = FwdSmem<DQK, DV, SPLIT ? 2 : 1>;
   constexpr int kT = SPLIT ? 2 * kThreads : kThreads;
 
