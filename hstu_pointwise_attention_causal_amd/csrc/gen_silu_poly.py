@@ -4,12 +4,14 @@ With x' = log2(e) * x, the kernel needs g(x') = log2(e) * SiLU(x) =
 x' / (1 + 2^-x'). Its odd part is x'/2 and its even part is a smooth function
 of y = x'^2, so on |x| <= R
 
-    g(x') ~= 0.5 x' + y * (c0 + c1 y + c2 y^2 + c3 y^3).
+    g(x') ~= 0.5 x' + y * (c0 + c1 y + c2 y^2).
 
 The coefficients are a y-weighted least-squares fit on Chebyshev nodes of
-y in [0, (R log2 e)^2] (R = 2). Running this script prints them and the
-maximum absolute error of g on a dense grid (about 2.8e-5, i.e. 1e-5 of
-max|g|, two orders of magnitude below the bf16 rounding of the scores' SiLU).
+y in [0, (R log2 e)^2] (R = 2). Running this script prints them, the
+maximum absolute error of g on a dense grid (about 3.3e-4) and the largest
+relative error where |g| > 0.05 (about 1.1e-3, below the bf16 half-ulp of
+2^-9 that the kernel rounds the result to). A cubic (deg=3) reaches 2.8e-5
+for one more FMA per score.
 """
 import numpy as np
 
@@ -21,7 +23,7 @@ def g_exact(xp):
     return xp / (1.0 + np.exp2(-xp))
 
 
-def fit(deg=3, R=R):
+def fit(deg=2, R=R):
     Rp = R * L
     yc = (np.cos(np.linspace(0.0, np.pi, 400)) + 1.0) / 2.0 * Rp * Rp
     xc = np.sqrt(yc)
@@ -36,5 +38,8 @@ if __name__ == "__main__":
     xs = np.linspace(-R * L, R * L, 200001)
     y = xs * xs
     g = 0.5 * xs + y * np.polynomial.polynomial.polyval(y, c)
-    print("coefficients c0..c3:", ", ".join(f"{v:.9e}f" for v in c))
-    print("max |g - g_exact| on |x| <= R:", np.max(np.abs(g - g_exact(xs))))
+    print("coefficients c0..c%d:" % (len(c) - 1), ", ".join(f"{v:.9e}f" for v in c))
+    err = np.abs(g - g_exact(xs))
+    big = np.abs(g_exact(xs)) > 0.05
+    print("max |g - g_exact| on |x| <= R:", err.max())
+    print("max relative error where |g| > 0.05:", (err[big] / np.abs(g_exact(xs))[big]).max())
