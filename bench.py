@@ -134,13 +134,29 @@ def cpu_baseline(wl, target_s: float):
                       f"elementwise steps single-threaded"}
 
 
-def time_steps(step, steps: int, warmup: int, stream):
-    """Warm up, then time exactly `steps` calls between two synchronizations;
+# Shortest warm-up by time: the shader clock ramps up over the first ~40 ms of
+# sustained load, so warm-up continues past `--warmup` calls until this much
+# wall time has passed.
+MIN_WARMUP_MS = 200.0
+WARMUP_DONE = {}   # label -> (calls, ms) of the warm-up actually run
+
+
+def time_steps(step, steps: int, warmup: int, stream, label: str = "secondary"):
+    """Warm up (at least `warmup` calls and at least MIN_WARMUP_MS of wall
+    time), then time exactly `steps` calls between two synchronizations;
     returns (ms per step from HIP events on `stream`, ms per step of wall time)."""
     import torch
+    t0 = time.perf_counter()
+    calls = 0
     for _ in range(warmup):
         step()
+        calls += 1
     torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < MIN_WARMUP_MS:
+        step()
+        calls += 1
+        torch.cuda.synchronize()
+    WARMUP_DONE[label] = (calls, round((time.perf_counter() - t0) * 1e3, 1))
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
@@ -491,7 +507,7 @@ def main():
                       time_table=a["tt"], alpha=wl.alpha, divisor=wl.divisor, out=out, workspace=ws)
 
     stream = torch.cuda.current_stream(dev)   # the stream every kernel is launched on
-    ms_events, ms_wall = time_steps(step, args.steps, args.warmup, stream)
+    ms_events, ms_wall = time_steps(step, args.steps, args.warmup, stream, label="headline")
     ms_step = max(ms_events, ms_wall)
     kern = kernel_ms(hstu, step, args.steps, ["attn_fwd"])["attn_fwd"]
 
@@ -506,6 +522,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": {"calls": WARMUP_DONE["headline"][0], "ms": WARMUP_DONE["headline"][1],
+                       "min_ms": MIN_WARMUP_MS},
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

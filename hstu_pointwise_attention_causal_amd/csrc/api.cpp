@@ -11,6 +11,7 @@
 #include <string>
 
 #include "../../include/hstu.h"
+#include "api_internal.h"
 #include "launch.h"
 #include "layer.h"
 #include "stochastic_length.h"
@@ -30,6 +31,20 @@ hstu_status_t fail(hstu_status_t st, const char* fmt, ...) {
 }
 
 hstu_status_t ok() { return HSTU_OK; }
+
+}  // namespace
+
+hstu_status_t hstu::api_fail(hstu_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+namespace {
 
 hstu_status_t hip_fail(hipError_t e, const char* what) {
   return fail(HSTU_E_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -97,7 +112,7 @@ hstu::AttnArgs make_args(const hstu_attn_desc_t* d, const hstu_jagged_t* j, cons
   a.ldq = ldq;
   a.ldk = ldk;
   a.ldv = ldv;
-  a.off = j->seq_offsets;
+  a.off = nullptr;   // set by bind_worklist: the kernels read the clamped copy
   a.ts = j->timestamps;
   a.pos_table = bias ? bias->pos_table : nullptr;
   a.pos_buckets = bias && bias->pos_table ? bias->pos_buckets : 0;
@@ -107,6 +122,18 @@ hstu::AttnArgs make_args(const hstu_attn_desc_t* d, const hstu_jagged_t* j, cons
   a.divisor = d->divisor;
   a.num_heads = d->num_heads;
   return a;
+}
+
+// Points the kernels at the work list, the block metadata and the clamped
+// offsets that the builder writes into the workspace ws (laid out by L).
+void bind_worklist(hstu::AttnArgs& a, const hstu::WorklistLayout& L, char* ws) {
+  a.off = reinterpret_cast<const int64_t*>(ws + L.offc_off);
+  a.items = ws + L.items_off;
+  a.item_count = reinterpret_cast<const int*>(ws + L.hdr_off);
+  a.capacity = L.capacity;
+  a.tile_base = reinterpret_cast<const int*>(ws + L.tile_base_off);
+  a.meta = ws + L.meta_off;
+  a.meta_blocks = L.meta_blocks;
 }
 
 
@@ -183,17 +210,12 @@ hstu_status_t hstu_attn_fwd(const hstu_attn_desc_t* desc, const hstu_jagged_t* j
 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   char* ws = static_cast<char*>(workspace);
-  hipError_t e = hstu::launch_build_worklist(jag->seq_offsets, jag->num_seqs, (int)H, hstu::kAttnBM, L, ws, stream);
+  hipError_t e = hstu::launch_build_worklist(jag->seq_offsets, T, jag->num_seqs, (int)H, hstu::kAttnBM, L, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "work-list launch");
   hstu::AttnArgs a = make_args(desc, jag, bias, q, ldq, k, ldk, v, ldv);
+  bind_worklist(a, L, ws);
   a.o = o;
   a.ldo = ldo;
-  a.items = ws + L.items_off;
-  a.item_count = reinterpret_cast<const int*>(ws + L.hdr_off);
-  a.capacity = L.capacity;
-  a.tile_base = reinterpret_cast<const int*>(ws + L.tile_base_off);
-  a.meta = ws + L.meta_off;
-  a.meta_blocks = L.meta_blocks;
   e = dt == HSTU_BF16 ? hstu::launch_attn_fwd_bf16(a, desc->dqk, desc->dv, stream)
                       : hstu::launch_attn_fwd_f32(a, desc->dqk, desc->dv, stream);
   if (e != hipSuccess) return hip_fail(e, "attention forward launch");
@@ -250,16 +272,11 @@ hstu_status_t hstu_attn_bwd(const hstu_attn_desc_t* desc, const hstu_jagged_t* j
   if (!aligned16(workspace)) return fail(HSTU_E_ALIGN, "workspace must be 16-byte aligned");
 
   char* ws = static_cast<char*>(workspace);
-  hipError_t e = hstu::launch_build_worklist(jag->seq_offsets, jag->num_seqs, (int)H, hstu::kAttnBM, L, ws, stream);
+  hipError_t e = hstu::launch_build_worklist(jag->seq_offsets, T, jag->num_seqs, (int)H, hstu::kAttnBM, L, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "work-list launch");
   hstu::AttnBwdArgs g{};
   g.f = make_args(desc, jag, bias, q, ldq, k, ldk, v, ldv);
-  g.f.items = ws + L.items_off;
-  g.f.item_count = reinterpret_cast<const int*>(ws + L.hdr_off);
-  g.f.capacity = L.capacity;
-  g.f.tile_base = reinterpret_cast<const int*>(ws + L.tile_base_off);
-  g.f.meta = ws + L.meta_off;
-  g.f.meta_blocks = L.meta_blocks;
+  bind_worklist(g.f, L, ws);
   g.d_o = d_o;
   g.lddo = lddo;
   g.dq = dq;
@@ -340,7 +357,7 @@ hstu_status_t hstu_attn_fwd_candidates(const hstu_attn_desc_t* desc, const hstu_
   a.q_c = q; a.k_c = k; a.v_c = v; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv;
   a.k_h = k_hist; a.v_h = v_hist; a.ldkh = ldkh; a.ldvh = ldvh;
   a.o = o; a.ldo = ldo;
-  a.hist_off = hist->seq_offsets; a.cand_off = cand->seq_offsets;
+  a.hist_off_in = hist->seq_offsets; a.cand_off_in = cand->seq_offsets;
   a.ts_h = has_time ? hist->timestamps : nullptr;
   a.ts_c = has_time ? cand->timestamps : nullptr;
   a.pos_table = bias ? bias->pos_table : nullptr;
@@ -555,18 +572,13 @@ hstu_status_t hstu_layer_fwd(const hstu_layer_params_t* p, const hstu_jagged_t* 
   // 3. O = attention(q, k, v) on column views of G
   const __bf16* gb = static_cast<const __bf16*>(g);
   hstu::WorklistLayout WL = L.attn;
-  if ((e = hstu::launch_build_worklist(jag->seq_offsets, jag->num_seqs, static_cast<int>(H), hstu::kAttnBM, WL, ws,
-                                       stream)) != hipSuccess)
+  if ((e = hstu::launch_build_worklist(jag->seq_offsets, T, jag->num_seqs, static_cast<int>(H), hstu::kAttnBM, WL,
+                                       ws, stream)) != hipSuccess)
     return hip_fail(e, "work-list launch");
   hstu::AttnArgs a = make_args(&p->attn, jag, &p->bias, gb + 2 * hv, n1, gb + 2 * hv + H * dqk, n1, gb + hv, n1);
+  bind_worklist(a, WL, ws);
   a.o = o;
   a.ldo = hv;
-  a.items = ws + WL.items_off;
-  a.item_count = reinterpret_cast<const int*>(ws + WL.hdr_off);
-  a.capacity = WL.capacity;
-  a.tile_base = reinterpret_cast<const int*>(ws + WL.tile_base_off);
-  a.meta = ws + WL.meta_off;
-  a.meta_blocks = WL.meta_blocks;
   if ((e = hstu::launch_attn_fwd_bf16(a, static_cast<int>(dqk), static_cast<int>(dv), stream)) != hipSuccess)
     return hip_fail(e, "attention forward launch");
 
@@ -646,18 +658,13 @@ hstu_status_t hstu_layer_bwd(const hstu_layer_params_t* p, const hstu_jagged_t* 
   g1.c2 = z; g1.ldc2 = n1; g1.M = static_cast<int>(T); g1.N = static_cast<int>(n1); g1.K = static_cast<int>(D);
   if ((e = hstu::launch_gemm(g1, hstu::kEpiSiluPair, false, false, 1, stream)) != hipSuccess)
     return hip_fail(e, "UVQK projection");
-  if ((e = hstu::launch_build_worklist(jag->seq_offsets, jag->num_seqs, static_cast<int>(H), hstu::kAttnBM, L.attn, ws,
-                                       stream)) != hipSuccess)
+  if ((e = hstu::launch_build_worklist(jag->seq_offsets, T, jag->num_seqs, static_cast<int>(H), hstu::kAttnBM,
+                                       L.attn, ws, stream)) != hipSuccess)
     return hip_fail(e, "work-list launch");
   const __bf16* gb = static_cast<const __bf16*>(g);
   const void *uq = gb + 2 * hv, *uk = gb + 2 * hv + H * dqk, *uv = gb + hv;
   hstu::AttnArgs a = make_args(&p->attn, jag, &p->bias, uq, n1, uk, n1, uv, n1);
-  a.items = ws + L.attn.items_off;
-  a.item_count = reinterpret_cast<const int*>(ws + L.attn.hdr_off);
-  a.capacity = L.attn.capacity;
-  a.tile_base = reinterpret_cast<const int*>(ws + L.attn.tile_base_off);
-  a.meta = ws + L.attn.meta_off;
-  a.meta_blocks = L.attn.meta_blocks;
+  bind_worklist(a, L.attn, ws);
   a.o = o;
   a.ldo = hv;
   if ((e = hstu::launch_attn_fwd_bf16(a, static_cast<int>(dqk), static_cast<int>(dv), stream)) != hipSuccess)

@@ -29,6 +29,7 @@
 #include "attn_common.h"
 #include "common.h"
 #include "launch.h"
+#include "offsets.h"
 #include "timing.h"
 
 namespace hstu {
@@ -82,34 +83,62 @@ __device__ __forceinline__ int chunk_seq(const int64_t* base, int num_seqs, int6
   return lo;
 }
 
-// One workgroup: base[b] = sum over earlier sequences of max(1, ceil(n / kCandChunk)).
-__global__ __launch_bounds__(1024) void cand_chunk_scan_kernel(CandArgs a) {
+// Block-wide scans of the one-workgroup kernel below (1024 threads, 16 waves):
+// inclusive sum and inclusive max of int64 values; *total gets the block's
+// sum / maximum.
+__device__ int64_t block_scan_i64(int64_t v, bool is_max, int64_t* total) {
   __shared__ int64_t wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t u = __shfl_up(v, o, 64);
+    if (lane >= o) v = is_max ? (u > v ? u : v) : v + u;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  int64_t before = is_max ? INT64_MIN : 0, all = is_max ? INT64_MIN : 0;
+  for (int i = 0; i < 16; ++i) {
+    const int64_t x = wsum[i];
+    if (i < w) before = is_max ? (x > before ? x : before) : before + x;
+    all = is_max ? (x > all ? x : all) : all + x;
+  }
+  *total = all;
+  __syncthreads();
+  return is_max ? (before > v ? before : v) : before + v;
+}
+
+// Clamped copy of a batch's offsets (offsets.h): out[b] = min(max(0, in[0..b]), T).
+__device__ void clamp_offsets(const int64_t* in, int num_seqs, int64_t T, int64_t* out) {
+  int64_t run = 0;
+  for (int c0 = 0; c0 <= num_seqs; c0 += 1024) {
+    const int b = c0 + static_cast<int>(threadIdx.x);
+    int64_t chunk_max;
+    const int64_t m = block_scan_i64(b <= num_seqs ? in[b] : INT64_MIN, true, &chunk_max);
+    if (b <= num_seqs) out[b] = clamp_offset(m, run, T);
+    run = chunk_max > run ? chunk_max : run;
+  }
+}
+
+// One workgroup: the clamped history and candidate offsets, which every later
+// kernel of the call reads, then base[b] = sum over earlier sequences of
+// max(1, ceil(n / kCandChunk)).
+__global__ __launch_bounds__(1024) void cand_chunk_scan_kernel(CandArgs a) {
+  const int tid = threadIdx.x;
+  clamp_offsets(a.hist_off_in, a.num_seqs, a.hist_tokens, a.hist_off);
+  clamp_offsets(a.cand_off_in, a.num_seqs, a.cand_tokens, a.cand_off);
+  __syncthreads();
   int64_t carry = 0;
   for (int c0 = 0; c0 < a.num_seqs; c0 += 1024) {
     const int b = c0 + tid;
     int64_t cnt = 0;
     if (b < a.num_seqs) {
-      const int64_t n = max(a.hist_off[b + 1] - a.hist_off[b], int64_t(0));
+      const int64_t n = a.hist_off[b + 1] - a.hist_off[b];   // >= 0, sum over b <= hist_tokens
       cnt = max(int64_t(1), (n + kCandChunk - 1) / kCandChunk);
     }
-    int64_t v = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t u = __shfl_up(v, o, 64);
-      if (lane >= o) v += u;
-    }
-    if (lane == 63) wsum[w] = v;
-    __syncthreads();
-    int64_t before = 0, total = 0;
-    for (int i = 0; i < 16; ++i) {
-      before += i < w ? wsum[i] : 0;
-      total += wsum[i];
-    }
-    if (b < a.num_seqs) a.chunk_base[b] = carry + before + v - cnt;
+    int64_t total;
+    const int64_t incl = block_scan_i64(cnt, false, &total);
+    if (b < a.num_seqs) a.chunk_base[b] = carry + incl - cnt;
     carry += total;
-    __syncthreads();
   }
   if (tid == 0) a.chunk_base[a.num_seqs] = carry;
 }
@@ -381,7 +410,9 @@ __global__ __launch_bounds__(256) void attn_cand_reduce_kernel(CandArgs a, int d
   const int64_t c0 = a.cand_off[b];
   const int64_t cl = r - c0;
   const int64_t g0 = a.chunk_base[b], g1 = min(a.chunk_base[b + 1], a.chunk_limit);
-  if (a.chunk_base[b + 1] - g0 <= 1 || cl >= a.max_candidates) return;
+  // past the last sequence (clamped offsets may end before cand_tokens), a
+  // single-chunk sequence, or a candidate past max_candidates: nothing to sum
+  if (r >= a.cand_off[b + 1] || a.chunk_base[b + 1] - g0 <= 1 || cl >= a.max_candidates) return;
   const int n = static_cast<int>(a.hist_off[b + 1] - a.hist_off[b]);
   const float scale = (a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n + 1)) / (2.0f * kLog2e);
   const int width = a.num_heads * d;
@@ -406,7 +437,9 @@ int64_t chunk_bound(int64_t hist_tokens, int num_seqs) {   // >= sum over sequen
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
-size_t cand_partial_offset(int num_seqs) { return align256(static_cast<size_t>(num_seqs + 1) * 8); }
+// Workspace: chunk bases, the clamped history offsets and the clamped
+// candidate offsets (int64 [num_seqs + 1] each), then the partial outputs.
+size_t cand_partial_offset(int num_seqs) { return align256(3 * static_cast<size_t>(num_seqs + 1) * 8); }
 
 size_t cand_workspace_bytes(int64_t hist_tokens, int num_seqs, int max_candidates, int num_heads, int d) {
   if (num_seqs <= 0 || max_candidates <= 0) return 0;
@@ -420,6 +453,10 @@ hipError_t launch_attn_cand_bf16(const CandArgs& a_in, int d, int64_t hist_token
   if (d != 128 && d != 64 && d != 32) return hipErrorInvalidValue;
   CandArgs a = a_in;
   a.chunk_limit = chunk_bound(hist_tokens, a.num_seqs);
+  a.hist_tokens = hist_tokens;
+  a.cand_tokens = cand_tokens;
+  a.hist_off = a.chunk_base + (a.num_seqs + 1);
+  a.cand_off = a.hist_off + (a.num_seqs + 1);
   const dim3 grid(static_cast<unsigned>(a.chunk_limit), static_cast<unsigned>(a.num_heads),
                   static_cast<unsigned>((a.max_candidates + kCBM - 1) / kCBM));
   TimedScope timed(kTimedAttnCand, stream);

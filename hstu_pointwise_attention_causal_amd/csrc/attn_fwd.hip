@@ -100,13 +100,13 @@ __device__ __forceinline__ float time_bias(const BiasLds& s, const AttnArgs& a, 
 // the kernel needs g(x') = log2(e) SiLU(x) = x' / (1 + 2^-x'). Exactly, that
 // is one exp2 and one reciprocal (both quarter-rate on gfx950). When a row's
 // scores in an unmasked block are provably small -- |alpha| |q_i| max_j |k_j|
-// + max |bias table| <= 1.95 (Cauchy-Schwarz) -- g is evaluated as 0.5 x' + y P(y), y = x'^2,
-// with a cubic P fitted on |x| <= 2 (max error 2.8e-5 in x' units, two orders
-// of magnitude below the bf16 rounding of P); six full-rate FMA-class
-// operations instead. The choice is
-// made per query row from that row's own norm, the norms of keys before it and
-// a bound over the whole bias table, so a row's result never depends on later
-// tokens.
+// + max |bias table| <= 1.95 (Cauchy-Schwarz) -- the kernel evaluates
+// 2 g = x' + y 2P(y), y = x'^2, with a quadratic P fitted on |x| <= 2 (max
+// error 3.3e-4 in x' units; where |g| > 0.05 the relative error is at most
+// 1.1e-3, below the bf16 half-ulp that P is rounded to): four FMA-class
+// operations instead (silu2_poly in attn_common.h). The choice is made per
+// query row from that row's own norm, the norms of keys before it and a bound
+// over the whole bias table, so a row's result never depends on later tokens.
 enum BlockPath { kUniform = 0, kTwoTime = 1, kGeneral = 2 };
 
 constexpr int kPosLdsFast = 1024;

@@ -41,9 +41,10 @@ __device__ __forceinline__ float silu_f32(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// Accurate variant for the fp32 path: IEEE division.
+// Variant for the fp32 path: the device library's expf (not the fast
+// __expf) and an IEEE division.
 __device__ __forceinline__ float silu_f32_accurate(float x) {
-  return x / (1.0f + __expf(-x));
+  return x / (1.0f + expf(-x));
 }
 
 // Relative position bucket: min(i - j, nb - 1) for i - j >= 0.

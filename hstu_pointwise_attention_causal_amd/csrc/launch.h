@@ -11,6 +11,7 @@ namespace hstu {
 struct WorklistLayout {
   int num_levels = 0;   // ceil(T/BM) + 1
   int64_t capacity = 0; // upper bound on the number of items
+  size_t offc_off = 0;  // int64 [B+1]: the clamped offsets (offsets.h) every kernel reads
   size_t hdr_off = 0, hist_off = 0, level_start_off = 0, fill_off = 0, tile_base_off = 0,
          items_off = 0;
   // per-(head, 32-key block) metadata of the bf16 forward: 4 blocks per query tile
@@ -20,7 +21,8 @@ struct WorklistLayout {
 };
 
 WorklistLayout worklist_layout(int B, int64_t T, int H, int BM);
-hipError_t launch_build_worklist(const int64_t* off, int B, int H, int BM, const WorklistLayout& L,
+// Writes the clamped offsets and the work list into ws (laid out by L).
+hipError_t launch_build_worklist(const int64_t* off, int64_t T, int B, int H, int BM, const WorklistLayout& L,
                                  char* ws, hipStream_t stream);
 
 // Query-tile height shared by every attention kernel and the work list.
@@ -36,7 +38,7 @@ struct AttnArgs {
   int64_t ldq, ldk, ldv;
   void* o;         // forward output
   int64_t ldo;
-  const int64_t* off;
+  const int64_t* off;       // the clamped copy written by the work-list builder
   const int64_t* ts;        // may be NULL
   const float* pos_table;   // may be NULL
   int pos_buckets;
@@ -76,8 +78,11 @@ struct CandArgs {
   int64_t ldkh, ldvh;
   void* o;
   int64_t ldo;
-  const int64_t* hist_off;
-  const int64_t* cand_off;
+  const int64_t* hist_off_in;   // the caller's offsets, read once by the chunk-scan kernel
+  const int64_t* cand_off_in;
+  int64_t* hist_off;        // workspace: their clamped copies (offsets.h), read by every other kernel
+  int64_t* cand_off;
+  int64_t hist_tokens, cand_tokens;
   const int64_t* ts_h;      // history timestamps, NULL without a time table
   const int64_t* ts_c;      // candidate timestamps, NULL without a time table
   const float* pos_table;

@@ -10,9 +10,12 @@
 // schedule over a dynamic pool of compute units.
 //
 // The builder runs as ONE workgroup, on the stream of the attention call,
-// entirely on device: the host never reads the offsets.
+// entirely on device: the host never reads the offsets. It also writes the
+// clamped copy of the offsets (offsets.h) that every later kernel of the call
+// reads instead of the caller's array.
 #include "common.h"
 #include "launch.h"
+#include "offsets.h"
 
 namespace hstu {
 
@@ -49,6 +52,30 @@ __device__ int block_inclusive_scan(int v, int* total) {
   return x + prefix;
 }
 
+// Inclusive max-scan of int64 values over the block; writes the block's
+// maximum to *total.
+__device__ int64_t block_inclusive_max(int64_t v, int64_t* total) {
+  __shared__ int64_t wave_max[kBuildThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x = y > x ? y : x;
+  }
+  if (lane == 63) wave_max[wave] = x;
+  __syncthreads();
+  int64_t before = INT64_MIN, all = INT64_MIN;
+  for (int i = 0; i < kBuildThreads / 64; ++i) {
+    const int64_t m = wave_max[i];
+    if (i < wave) before = m > before ? m : before;
+    all = m > all ? m : all;
+  }
+  *total = all;
+  __syncthreads();
+  return before > x ? before : x;
+}
+
 // Counters and scans of the builder live in LDS when the levels and the
 // sequences fit (LDS atomics and reads instead of global-memory round trips in
 // every phase); tile_base is also copied out, for the attention kernels.
@@ -57,8 +84,8 @@ constexpr int kLdsSeqs = 4096;     // B + 1 entries
 
 template <bool LDS>
 __global__ __launch_bounds__(kBuildThreads) void build_worklist_kernel(
-    const int64_t* __restrict__ off, int B, int H, int BM, int num_levels,
-    int* __restrict__ hdr, int* __restrict__ hist_g, int* __restrict__ level_start_g,
+    const int64_t* __restrict__ off_in, int64_t T, int B, int H, int BM, int num_levels,
+    int64_t* __restrict__ off, int* __restrict__ hdr, int* __restrict__ hist_g, int* __restrict__ level_start_g,
     int* __restrict__ fill_g, int* __restrict__ tile_base_g, WorkItem* __restrict__ items) {
   __shared__ int lds_hist[LDS ? kLdsLevels : 1], lds_level_start[LDS ? kLdsLevels : 1],
       lds_fill[LDS ? kLdsLevels : 1], lds_tile_base[LDS ? kLdsSeqs : 1];
@@ -71,6 +98,16 @@ __global__ __launch_bounds__(kBuildThreads) void build_worklist_kernel(
     hist[i] = 0;
     fill[i] = 0;
   }
+
+  // 0. the clamped offsets: c(b) = min(max(0, off[0..b]), T)
+  int64_t run = 0;   // max(0, off[0 .. b0 - 1])
+  for (int b0 = 0; b0 <= B; b0 += kBuildThreads) {
+    const int b = b0 + tid;
+    int64_t chunk_max;
+    const int64_t m = block_inclusive_max(b <= B ? off_in[b] : INT64_MIN, &chunk_max);
+    if (b <= B) off[b] = clamp_offset(m, run, T);
+    run = chunk_max > run ? chunk_max : run;
+  }
   __syncthreads();
 
   // 1. tiles per sequence, histogram of tile counts, and the exclusive scan of
@@ -80,7 +117,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_worklist_kernel(
     int b = b0 + tid;
     int nt = 0;
     if (b < B) {
-      int64_t n = off[b + 1] - off[b];
+      const int64_t n = off[b + 1] - off[b];   // >= 0, sum over b <= T
       nt = n <= 0 ? 0 : static_cast<int>((n + BM - 1) / BM);
       nt = min(nt, num_levels);
       atomicAdd(&hist[nt], 1);
@@ -167,6 +204,7 @@ WorklistLayout worklist_layout(int B, int64_t T, int H, int BM) {
     return o;
   };
   L.hdr_off = take(16);
+  L.offc_off = take(sizeof(int64_t) * (static_cast<size_t>(B) + 1));
   L.hist_off = take(sizeof(int) * (levels + 1));
   L.level_start_off = take(sizeof(int) * (levels + 1));
   L.fill_off = take(sizeof(int) * (levels + 1));
@@ -178,8 +216,9 @@ WorklistLayout worklist_layout(int B, int64_t T, int H, int BM) {
   return L;
 }
 
-hipError_t launch_build_worklist(const int64_t* off, int B, int H, int BM, const WorklistLayout& L,
+hipError_t launch_build_worklist(const int64_t* off, int64_t T, int B, int H, int BM, const WorklistLayout& L,
                                  char* ws, hipStream_t stream) {
+  int64_t* offc = reinterpret_cast<int64_t*>(ws + L.offc_off);
   int* hdr = reinterpret_cast<int*>(ws + L.hdr_off);
   int* hist = reinterpret_cast<int*>(ws + L.hist_off);
   int* level_start = reinterpret_cast<int*>(ws + L.level_start_off);
@@ -187,11 +226,11 @@ hipError_t launch_build_worklist(const int64_t* off, int B, int H, int BM, const
   int* tile_base = reinterpret_cast<int*>(ws + L.tile_base_off);
   WorkItem* items = reinterpret_cast<WorkItem*>(ws + L.items_off);
   if (L.num_levels + 1 <= kLdsLevels && B + 1 <= kLdsSeqs)
-    hipLaunchKernelGGL(build_worklist_kernel<true>, dim3(1), dim3(kBuildThreads), 0, stream, off, B, H, BM,
-                       L.num_levels - 1, hdr, hist, level_start, fill, tile_base, items);
+    hipLaunchKernelGGL(build_worklist_kernel<true>, dim3(1), dim3(kBuildThreads), 0, stream, off, T, B, H, BM,
+                       L.num_levels - 1, offc, hdr, hist, level_start, fill, tile_base, items);
   else
-    hipLaunchKernelGGL(build_worklist_kernel<false>, dim3(1), dim3(kBuildThreads), 0, stream, off, B, H, BM,
-                       L.num_levels - 1, hdr, hist, level_start, fill, tile_base, items);
+    hipLaunchKernelGGL(build_worklist_kernel<false>, dim3(1), dim3(kBuildThreads), 0, stream, off, T, B, H, BM,
+                       L.num_levels - 1, offc, hdr, hist, level_start, fill, tile_base, items);
   return hipGetLastError();
 }
 

@@ -65,11 +65,21 @@ typedef enum {
 
 typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype_t;
 
-/* A jagged batch of B sequences packed along the token axis. */
+/* A jagged batch of B sequences packed along the token axis.
+ *
+ * seq_offsets lives in device memory and the host never reads it. Each call's
+ * first kernel writes a clamped copy, c(b) = min(max(0, off[0], ..., off[b]),
+ * T), and every later kernel of the call reads only that copy. A well-formed
+ * array (off[0] = 0, non-decreasing, off[B] = T) is unchanged by it. A
+ * malformed one cannot make a kernel read or write outside the T tokens: it
+ * is computed as the batch of the clamped offsets. Offsets past T are cut to
+ * T, a decreasing step becomes an empty sequence, and tokens past c(B) belong
+ * to no sequence and their outputs are not written. (hstu_stochastic_length
+ * clamps its offsets per sequence instead; see there.) */
 typedef struct {
   int32_t num_seqs;           /* B >= 0 */
-  int64_t total_tokens;       /* T; must equal seq_offsets[B] (not checked on the host) */
-  const int64_t* seq_offsets; /* device [B+1]: off[0] = 0, non-decreasing; empty sequences allowed */
+  int64_t total_tokens;       /* T: the tokens every [T, ...] tensor holds */
+  const int64_t* seq_offsets; /* device [B+1]: off[0] = 0, non-decreasing, off[B] = T; empty sequences allowed */
   const int64_t* timestamps;  /* device [T] int64 seconds, or NULL (then no time bias);
                                  pairwise gaps must fit in int64 */
 } hstu_jagged_t;

@@ -160,3 +160,15 @@ def test_query_gradient_ignores_later_tokens(hstu):
     inp2 = dict(inp, k=to_dev(round_to_bf16(k2), torch.bfloat16), v=to_dev(round_to_bf16(v2), torch.bfloat16))
     b = _gpu_bwd(hstu, inp2)
     assert np.array_equal(a[0][:300], b[0][:300])
+
+
+def test_malformed_offsets_are_clamped(hstu):
+    """Offsets [0, 250, 120, 900] over 300 tokens read as their clamped copy
+    [0, 250, 250, 300] (include/hstu.h): every gradient equals the oracle's on
+    the clamped batch."""
+    q, k, v, d_o, _, ts, pt, tt = _synthetic([300], 2, 128, seed=23)
+    raw = np.array([0, 250, 120, 900], np.int64)
+    clamped = np.array([0, 250, 250, 300], np.int64)
+    got = _gpu_bwd(hstu, _dev(q, k, v, d_o, raw, ts, pt, tt))
+    ref = _oracle_bwd(q, k, v, d_o, clamped, ts, pt, tt)
+    _compare(got, ref, "malformed offsets")

@@ -144,3 +144,19 @@ def test_single_candidate_equals_forward_last_row(hstu):
 def test_deterministic(hstu):
     wl = make_workload("c6_small")
     assert np.array_equal(_gpu(hstu, wl), _gpu(hstu, wl))
+
+
+def test_malformed_offsets_are_clamped(hstu):
+    """History offsets [0, 150, 60, 10**9] over 300 tokens and candidate
+    offsets [0, 3, 1, 12] over 10 candidates read as their clamped copies
+    [0, 150, 150, 300] and [0, 3, 3, 10] (include/hstu.h): every candidate
+    equals the oracle's score on the clamped batch."""
+    import dataclasses
+    from workloads.generators import _cand_recipe
+    wl = _cand_recipe("malformed", 29, lengths=[150, 0, 150], cands=[3, 0, 7], H=2, d=64)
+    ref = _ref(wl)
+    c = dict(wl.cand, offsets=np.array([0, 3, 1, 12], np.int64))
+    got = _gpu(hstu, dataclasses.replace(wl, seq_offsets=np.array([0, 150, 60, 10 ** 9], np.int64)), c=c)
+    err = rel_err(got, ref)
+    print(f"malformed offsets err {err:.2e}")
+    assert err <= TOL_BF16

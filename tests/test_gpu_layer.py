@@ -102,14 +102,21 @@ def test_nonzero_biases_and_affine_norms(hstu):
 
 
 def test_four_layer_stack_full_size(hstu):
-    """The 4-layer, 8 x 1024-token stack at full size. Each layer is checked
-    against the oracle layer applied to the same input (the previous GPU
-    layer's bf16 output) to the bf16 tolerance. Against the all-fp64 stack the
-    deviation compounds over layers, because every activation between steps
-    is stored in bf16 (unit roundoff 2^-9): rounding a fp64 pipeline at the
-    same points on the CPU gives 1.7e-2 after 4 layers, so the end-to-end
-    check uses 2e-2."""
+    """The 4-layer, 8 x 1024-token stack at full size.
+
+    - Each layer against the oracle layer applied to the same input (the
+      previous GPU layer's bf16 output), at the bf16 tolerance.
+    - The whole stack against the all-fp64 stack. The workload stores every
+      activation in bf16 between steps, and that storage alone moves the
+      oracle's own stack e_s = 1.7e-2 from fp64 after four layers (the oracle
+      evaluated with LN(X), G, O, Y, X' rounded where they are stored,
+      tests/bf16_storage.py; pinned on the CPU by tests/test_stack_precision.py).
+      The bound is that storage error plus the bf16 tolerance that each layer's
+      kernels are held to: e_s + 1e-2, computed here from the emulation, not
+      picked by hand.
+    """
     import torch
+    from tests.bf16_storage import stack_errors
     wl = make_workload("c1")
     x_gpu = to_dev(wl.x, torch.bfloat16)
     off = to_dev(wl.seq_offsets)
@@ -124,34 +131,26 @@ def test_four_layer_stack_full_size(hstu):
         err = rel_err(x_gpu.float().cpu().numpy(), ref)
         print(f"c1 layer {li}: err {err:.2e} (same input)")
         assert err <= TOL_BF16
-    ref = orc.stack_fwd(wl.x, wl.layers, wl.seq_offsets, num_heads=wl.num_heads, dqk=wl.dqk,
-                        dv=wl.dv, timestamps=wl.timestamps, eps=wl.ln_eps)
-    err = rel_err(x_gpu.float().cpu().numpy(), ref)
-    print(f"c1 4-layer end-to-end err {err:.2e}")
-    assert err <= 2e-2
+    got = x_gpu.float().cpu().numpy()
+    emu, ref64, e_s = stack_errors(wl)[-1]
+    bound = e_s + TOL_BF16
+    err = rel_err(got, ref64)
+    print(f"c1 4-layer end-to-end vs fp64: {err:.2e}; bound {bound:.2e} = bf16-storage error {e_s:.2e} + "
+          f"{TOL_BF16:.0e}; vs the bf16-storage stack: {rel_err(got, emu):.2e}")
+    assert err <= bound
 
 
-def test_jagged_layer_full_size_sampled_rows(hstu):
-    """One layer over the 64-sequence jagged batch at full size; sampled rows
-    (first, last, tile edges and random rows of several sequences) recomputed
-    by the row-wise oracle."""
+def test_jagged_layer_full_size_every_row(hstu):
+    """One layer over the 64-sequence jagged batch at full size (49 404 tokens,
+    lengths log-uniform in [32, 4096]): every output row against the oracle."""
     wl = make_workload("c2")
     out, _ = _run_stack(hstu, wl)
-    rng = np.random.default_rng(3)
-    off = wl.seq_offsets
-    rows = []
-    for b in rng.choice(wl.num_seqs, 10, replace=False):
-        n = int(off[b + 1] - off[b])
-        for r in (0, 1, 127, 128, n - 1, int(rng.integers(0, n))):
-            if 0 <= r < n:
-                rows.append(int(off[b] + r))
-    rows = sorted(set(rows))
-    ref = orc.layer_fwd_rows(wl.x, wl.layers[0], off, rows, num_heads=wl.num_heads, dqk=wl.dqk,
-                             dv=wl.dv, timestamps=wl.timestamps, eps=wl.ln_eps)
-    err = rel_err(out[rows], ref)
-    print(f"c2 sampled err {err:.2e} over {len(rows)} rows")
-    assert err <= TOL_BF16
     assert np.all(np.isfinite(out))
+    ref, _ = orc.layer_fwd(wl.x, wl.layers[0], wl.seq_offsets, num_heads=wl.num_heads, dqk=wl.dqk, dv=wl.dv,
+                           timestamps=wl.timestamps, eps=wl.ln_eps)
+    err = rel_err(out, ref)
+    print(f"c2 every row: err {err:.2e} over {out.shape[0]} rows")
+    assert err <= TOL_BF16
 
 
 def test_wider_layer_d1024_h8(hstu):
