@@ -15,6 +15,7 @@ from .ops import (  # noqa: F401
     attn_cand_workspace_size,
     attn_fwd,
     attn_fwd_candidates,
+    attn_fwd_noalloc,
     attn_workspace_size,
     head_fwd,
     gather_rows,
@@ -29,7 +30,7 @@ from .ops import (  # noqa: F401
 
 __all__ = [
     "HstuError", "load",
-    "attn_fwd", "attn_bwd", "attn_workspace_size",
+    "attn_fwd", "attn_fwd_noalloc", "attn_bwd", "attn_workspace_size",
     "attn_fwd_candidates", "attn_cand_workspace_size",
     "layer_fwd", "layer_bwd", "make_layer_params",
     "head_fwd", "head_workspace_size",

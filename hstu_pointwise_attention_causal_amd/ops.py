@@ -148,12 +148,8 @@ def attn_workspace_size(num_heads: int, dqk: int, dv: int, dtype: torch.dtype, n
     return out.value
 
 
-def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets: torch.Tensor, *,
-             timestamps: Optional[torch.Tensor] = None, pos_table: Optional[torch.Tensor] = None,
-             time_table: Optional[torch.Tensor] = None, alpha: float = 1.0, divisor: float = 0.0,
-             out: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """hstu_attn_fwd on [T, H, d] tensors (bf16 or fp32) of one jagged batch."""
+def _attn_fwd_args(q, k, v, seq_offsets, timestamps, pos_table, time_table, alpha, divisor, out, workspace):
+    """Checks and marshals the arguments shared by attn_fwd and attn_fwd_noalloc."""
     if q.dtype not in _DT:
         raise ValueError(f"q must be bf16 or fp32, got {q.dtype}")
     if q.dim() != 3:
@@ -179,6 +175,17 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets: tor
     d = _desc(H, dqk, dv, q.dtype, alpha, divisor)
     j = _jagged(seq_offsets, T, timestamps)
     b = _bias(pos_table, time_table)
+    return lib, T, H, ldq, ldk, ldv, out, ldo, d, j, b
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets: torch.Tensor, *,
+             timestamps: Optional[torch.Tensor] = None, pos_table: Optional[torch.Tensor] = None,
+             time_table: Optional[torch.Tensor] = None, alpha: float = 1.0, divisor: float = 0.0,
+             out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """hstu_attn_fwd on [T, H, d] tensors (bf16 or fp32) of one jagged batch."""
+    lib, T, H, ldq, ldk, ldv, out, ldo, d, j, b = _attn_fwd_args(
+        q, k, v, seq_offsets, timestamps, pos_table, time_table, alpha, divisor, out, workspace)
     need = ctypes.c_size_t(0)
     _lib.check(lib.hstu_attn_workspace_size(ctypes.byref(d), ctypes.byref(j), ctypes.byref(b), 0,
                                             ctypes.byref(need)))
@@ -187,6 +194,21 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets: tor
     _lib.check(lib.hstu_attn_fwd(ctypes.byref(d), ctypes.byref(j), ctypes.byref(b),
                                  _ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv, _ptr(out), ldo,
                                  _ptr(workspace), workspace.numel(), _stream_handle(q.device)))
+    return out
+
+
+def attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets: torch.Tensor, *,
+                     timestamps: Optional[torch.Tensor] = None, pos_table: Optional[torch.Tensor] = None,
+                     time_table: Optional[torch.Tensor] = None, alpha: float = 1.0, divisor: float = 0.0,
+                     out: torch.Tensor) -> torch.Tensor:
+    """hstu_attn_fwd_noalloc: attn_fwd without a workspace (the library's own
+    fixed device array holds it). `out` must be passed: the call allocates
+    nothing, and calls that overlap in time on one GPU race on the array."""
+    lib, T, H, ldq, ldk, ldv, out, ldo, d, j, b = _attn_fwd_args(
+        q, k, v, seq_offsets, timestamps, pos_table, time_table, alpha, divisor, out, None)
+    _lib.check(lib.hstu_attn_fwd_noalloc(ctypes.byref(d), ctypes.byref(j), ctypes.byref(b),
+                                         _ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv, _ptr(out), ldo,
+                                         _stream_handle(q.device)))
     return out
 
 

@@ -138,6 +138,27 @@ hstu_status_t hstu_attn_fwd(const hstu_attn_desc_t* desc, const hstu_jagged_t* j
                             void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * hstu_attn_fwd_noalloc -- hstu_attn_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation, arguments and errors as
+ * hstu_attn_fwd, without the workspace. Its workspace lives in a fixed 16 MiB
+ * array of device memory that the library holds on each GPU it runs on until
+ * the process ends; the first call on a device looks up that device's copy.
+ * The call allocates nothing (no hipMalloc, no allocating library routine).
+ * A batch whose hstu_attn_workspace_size(..., 0, ...) exceeds 16 MiB
+ * (T x H above about 15 million token-heads) returns HSTU_E_UNSUPPORTED; use
+ * hstu_attn_fwd with a workspace for it. Every call on a GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (other streams, other
+ * host threads) race on it and may corrupt each other's outputs. Nothing in
+ * the array needs clearing between calls (the first kernel of a call
+ * initialises what the later ones read).
+ * ------------------------------------------------------------------------- */
+hstu_status_t hstu_attn_fwd_noalloc(const hstu_attn_desc_t* desc, const hstu_jagged_t* jag,
+                                    const hstu_bias_t* bias,
+                                    const void* q, int64_t ldq, const void* k, int64_t ldk,
+                                    const void* v, int64_t ldv, void* o, int64_t ldo, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * hstu_attn_bwd -- gradients of sum(O * dO) for hstu_attn_fwd with the same
  * inputs: with sig = 1/(1+e^-S), SiLU'(S) = sig (1 + S (1 - sig)), over pairs
  * j <= i: dA_ij = dO_i.v_j, dS_ij = dA_ij SiLU'(S_ij)/N, dv_j = sum_i A_ij dO_i,
