@@ -87,6 +87,78 @@ def _traffic():
     return t.get("bytes_per_launch")
 
 
+# Kernels the counter summary reports, by a substring of their symbol name.
+COUNTER_KERNELS = {
+    "attn_fwd": ("attn_fwd_bf16_kernel", "attn_fwd_pp_kernel"),
+    "attn_bwd_kv": "attn_bwd_kv_kernel",
+    "attn_bwd_q": "attn_bwd_q_kernel",
+    "attn_cand": "attn_cand_kernel",
+    "head_gemm": "gemm_kernel",
+    "copy": "copyBuffer",
+}
+SIMDS, CUS, XCDS = 1024, 256, 8      # MI355X: 256 compute units of 4 SIMDs in 8 XCDs
+
+
+def summarize_counters(csv_paths, kernels):
+    """Per-dispatch averages of the counters in rocprofv3 --pmc CSV files
+    (p_counter_collection.csv), for each named kernel, and the figures derived
+    from them. Counters summed over the whole device per dispatch; the later
+    half of each kernel's dispatches is used (after warm-up)."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))   # kernel -> counter -> [per dispatch]
+    meta = {}
+    for path in csv_paths:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                name = row["Kernel_Name"]
+                for kname, subs in kernels.items():
+                    if any(sub in name for sub in ((subs,) if isinstance(subs, str) else subs)):
+                        # one entry per (kernel, grid size): a workload's launches of that kernel
+                        key = f"{kname} grid {int(row['Grid_Size']) // int(row['Workgroup_Size'])}"
+                        vals[key][row["Counter_Name"]].append((int(row["Dispatch_Id"]), float(row["Counter_Value"]),
+                                                              int(row["End_Timestamp"]) - int(row["Start_Timestamp"])))
+                        meta[key] = dict(vgpr=int(row["VGPR_Count"]), agpr=int(row["Accum_VGPR_Count"]),
+                                         lds=int(row["LDS_Block_Size"]), wg=int(row["Workgroup_Size"]))
+    out = {}
+    for key, cs in vals.items():
+        avg, ns = {}, []
+        for cname, lst in cs.items():
+            lst.sort()
+            later = lst[len(lst) // 2:]
+            avg[cname] = sum(v for _, v, _ in later) / len(later)
+            ns += [d for _, _, d in later]
+        r = {"dispatches": max(len(v) for v in cs.values()), "counters": {k: round(v, 1) for k, v in avg.items()},
+             **meta.get(key, {})}
+        g = avg.get("GRBM_GUI_ACTIVE")
+        if g:
+            # GRBM_GUI_ACTIVE is the sum over the XCDs: one XCD's busy cycles is that over XCDS
+            g /= XCDS
+            r["gui_active_cycles_per_xcd"] = round(g, 1)
+            if ns:
+                r["avg_clock_ghz"] = round(g / (sum(ns) / len(ns)), 3)
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                r["mfma_busy_frac"] = round(avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * SIMDS), 4)
+            if "SQ_LDS_IDX_ACTIVE" in avg:
+                r["lds_active_frac"] = round(avg["SQ_LDS_IDX_ACTIVE"] / (g * CUS), 4)
+        if avg.get("SQ_INSTS_MFMA"):
+            m = avg["SQ_INSTS_MFMA"]
+            for c, label in (("SQ_INSTS_VALU", "valu_per_mfma"), ("SQ_INSTS_SALU", "salu_per_mfma"),
+                             ("SQ_INSTS_LDS", "lds_per_mfma")):
+                if c in avg:
+                    r[label] = round((avg[c] - (m if c == "SQ_INSTS_VALU" else 0)) / m, 3)
+        if avg.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+            r["coexec_frac_of_mfma_busy"] = round(avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / avg["SQ_VALU_MFMA_BUSY_CYCLES"], 4)
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg and ns:
+            # 512 flops per MOP (the rocprofv3 derived-metric definition)
+            r["mfma_bf16_tflops_from_counters"] = round(avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 /
+                                                        (sum(ns) / len(ns) * 1e-9) / 1e12, 1)
+        if ns:
+            r["avg_dispatch_ns_under_profiler"] = round(sum(ns) / len(ns), 1)
+        out[key] = r
+    return out
+
+
 def copy_calib():
     import torch
     dev = torch.device("cuda:0")
@@ -479,7 +551,12 @@ def main():
                     help="comma-separated secondary figures to run (default: all)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="print per-kernel averages and derived figures of rocprofv3 --pmc CSV files and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters, COUNTER_KERNELS), indent=1))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
