@@ -213,6 +213,38 @@ struct BwdGradSmem {
   float gtime[kBW][kBwdTimeSlots][64];
 };
 
+// LDS float add without a return value; lanes that hit one address are all
+// applied. Written as asm: the compiler's atomic carries no alias scope, so
+// it would first wait for every tile load in flight. The compiler does not
+// count it among the outstanding LDS operations: a reader on another wave
+// waits for it explicitly (lgkmcnt(0) before the barrier), see below.
+__device__ __forceinline__ void lds_add_f32(float* p, float v) {
+  const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(to_lds(p)));
+  asm volatile("ds_add_f32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// Diagonal sums of a 32 x 32 block held as an MFMA accumulator: lane
+// (lr, lh), element r holds row i' = 8(r/4) + 4 lh + r%4, column lr, on
+// diagonal i' - lr. Element r of lane m of each half is rotated to the column
+// (i' - m) mod 32 of the same row, whose diagonal is m (no wrap) or m - 32.
+// On return lanes lr of both halves hold dpos = the sum of diagonal lr and
+// dneg = the sum of diagonal lr - 32 (zero for lr = 0), each over the whole
+// block; the order of the additions is fixed.
+__device__ __forceinline__ void diagonal_sums(const float* v, int lr, int lh, float& dpos, float& dneg) {
+  float sp = 0.f, sn = 0.f;
+  const int t0 = 4 * lh - lr, hbase = lh << 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int d = 8 * (r >> 2) + (r & 3) + t0;   // i' - lr
+    const int src = hbase | (d & 31);
+    const float y = __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v[r])));
+    sp += d >= 0 ? y : 0.f;
+    sn += d < 0 ? y : 0.f;
+  }
+  dpos = sp + __shfl_xor(sp, 32, 64);
+  dneg = sn + __shfl_xor(sn, 32, 64);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   v = row16_sum(v);
   v += __shfl_xor(v, 16, 64);
@@ -244,8 +276,17 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
   const int kt = ntl - 1 - item_qtile(item);
   const int k0 = kt * kAttnBM;
 
-  __shared__ BwdSmem<DQK, DV> sm;
-  __shared__ BwdGradSmem gs;
+  // One LDS object: with two, the module's LDS lowering gives every access
+  // the scope of its object, so reads of a tile could no longer be told apart
+  // from the direct loads filling the other tile of the same object, and
+  // every step would wait for the next tile's loads.
+  struct KvSmem {
+    BwdSmem<DQK, DV> t;
+    BwdGradSmem g;
+  };
+  __shared__ KvSmem lds;
+  BwdSmem<DQK, DV>& sm = lds.t;
+  BwdGradSmem& gs = lds.g;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -343,7 +384,8 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
                              const int64_t* __restrict__ rt, const BlockMeta* __restrict__ rm,
                              char* __restrict__ nq, char* __restrict__ nd, int64_t* __restrict__ nt,
                              BlockMeta* __restrict__ nm, const float* __restrict__ spos,
-                             const float* __restrict__ stime, int t) __attribute__((always_inline)) {
+                             const float* __restrict__ stime, float* __restrict__ gpos,
+                             float* __restrict__ gtime, int t) __attribute__((always_inline)) {
     const int i0 = (tq0 + t) * kBBN;
     if (t + 1 < ntq)
       issue_rows_tile<QCH, DCH>(qbase, dbase, a.ldq, g.lddo, tsbase, meta_row, n, i0 + kBBN, w, lane, qoff, doff, nq,
@@ -434,13 +476,26 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
             silu_and_grad(x, pl, dsl);
             p[r] = valid ? pl : 0.f;
             ds[r] = valid ? da[r] * dsl : 0.f;
-            // masked pairs add nothing; pairs in the last position bucket go
-            // to the register sum of the far pairs
-            if (has_pos && valid) {
-              if (pb < Bp - 1) atomicAdd(&gpos[pb], ds[r]);
-              else far_acc += ds[r];
-            }
             if (has_time) gtime[64 * tb] += ds[r];
+          }
+          // position buckets: a valid pair of the block reads bucket
+          // min(i - key, Bp - 1) = min(qa - kw + d, Bp - 1) with d = i' - lr
+          // its diagonal (masked pairs hold dS = 0)
+          if (has_pos) {
+            if (qa - (kw + 31) >= Bp - 1) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) far_acc += ds[r];
+            } else {
+              float dpos, dneg;
+              diagonal_sums(ds, lr, lh, dpos, dneg);
+              if (lh == 0) {
+                const int bpos = qa - kw + lr, bneg = bpos - 32;
+                if (bpos < Bp - 1) gpos[bpos] += dpos;
+                else far_acc += dpos;
+                if (bneg >= Bp - 1) far_acc += dneg;
+                else if (bneg >= 0) gpos[bneg] += dneg;
+              }
+            }
           }
         }
       }
@@ -463,7 +518,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
   for (int t = 0; t < ntq; ++t) {
     const int buf = t & 1;
     step(sm.a[buf], sm.b[buf], sm.t[buf], sm.m[buf], sm.a[buf ^ 1], sm.b[buf ^ 1], sm.t[buf ^ 1], sm.m[buf ^ 1],
-         sm.pos, sm.time, t);
+         sm.pos, sm.time, gpos, gtime, t);
     wait_vmcnt(0);
     tile_barrier();
   }
@@ -492,6 +547,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
       const float f = wave_sum(far_acc);
       if (lane == 0) gpos[Bp - 1] += f;
     }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the asm adds above have landed
     __syncthreads();
     float* prow = g.partial + (static_cast<int64_t>(h) * g.tile_rows + a.tile_base[b] + kt) * g.grad_stride;
     if (has_pos)
