@@ -202,17 +202,6 @@ struct BwdSmem {
   float time[kBwdTimeSlots];    // log2(e) Tt[h][.]
 };
 
-// Bias-table gradients of one key tile, summed in LDS. Position buckets: one
-// table per wave (its lanes' pairs rarely share a bucket within one add).
-// Time buckets: one column per lane of each wave ([wave][bucket][lane]) --
-// near the diagonal most pairs of a block share a bucket, and lane-private
-// columns keep those adds free of same-address serialization (and of atomics:
-// plain read-modify-write measured faster than conflict-free LDS atomics).
-struct BwdGradSmem {
-  float gpos[kBW][kBwdPosMax];
-  float gtime[kBW][kBwdTimeSlots][64];
-};
-
 // LDS float add without a return value; lanes that hit one address are all
 // applied. Written as asm: the compiler's atomic carries no alias scope, so
 // it would first wait for every tile load in flight. The compiler does not
@@ -254,15 +243,105 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // ============================================================================
 // key pass: dK, dV and the bias-table gradients
+//
+// A work item owns 128 keys and walks the 32-row query blocks from the
+// diagonal to the end of the sequence. Waves w and w + 4 of the workgroup run
+// on one SIMD and share a group of 32 keys (kw = k0 + 32 (w & 3), one key per
+// lane as the column of S), in two roles:
+//   score wave (w < 4)      S = Q K^T, the bias, P = SiLU(x) and SiLU'(x) of
+//                           every pair (masked pairs: 0), dV += P^T dO;
+//   gradient wave (w >= 4)  one block behind: dA = dO V^T, dS = dA SiLU'(x),
+//                           the bias-table gradients, dK += dS^T Q.
+// SiLU'(x) (fp32) and each pair's time bucket reach the gradient wave through
+// LDS. Each role's registers fit two waves per SIMD; the per-pair arithmetic
+// of the score wave overlaps the gradient wave's products and its
+// read-modify-write chains on the gradient tables. K (score) and V (gradient)
+// of the lane's key stay in registers as MFMA B operands; Q and dO blocks
+// stream through a ring of three LDS slots (block t + 1 loads while t and
+// t - 1 are read), with one barrier per block.
 // ============================================================================
+constexpr int kKW = 8;                // waves of a key-pass workgroup
+constexpr int kKThreads = kKW * 64;
+constexpr int kKRing = 3;             // 32-row Q and dO slots
+constexpr int kGFast = 32;            // time buckets summed in lane-private columns
+
 template <int DQK, int DV>
-__global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g) {
+struct KvLds {
+  __attribute__((aligned(16))) char q[kKRing][32 * DQK * 2];
+  __attribute__((aligned(16))) char d[kKRing][32 * DV * 2];
+  __attribute__((aligned(16))) int64_t t[kKRing][32];
+  __attribute__((aligned(16))) BlockMeta m[kKRing];
+  f32x4_t xg[2][4][4][64];      // SiLU'(x) of a block: [buffer][key group][r / 4][lane]
+  u32x4_t xb[2][4][64];         // time bucket of pair r in byte r % 4 of word r / 4: [buffer][key group][lane]
+  int xinfo[2][4];              // block class of a block: [buffer][key group]
+  // Bias-table gradients, one table per gradient wave. Position buckets:
+  // plain adds of diagonal sums. Time buckets below kGFast: one column per
+  // lane ([wave][bucket][lane]), as most pairs of a block near the diagonal
+  // share a bucket; larger buckets (gaps of 2^32 - 1 and more): per-wave sums.
+  float gpos[4][kBwdPosMax];
+  float gtime[4][kGFast][64];
+  float gslow[4][kBwdTimeSlots];
+  float pos[kBwdPosMax];        // log2(e) P[h][.] (one 0 without the table)
+  float time[kBwdTimeSlots];    // log2(e) Tt[h][.] (one 0 without the table)
+};
+
+// Direct loads of one 32-row block of a row-major matrix with CH 16-byte
+// chunks per row, stored with the dual-read swizzle: instruction i fills LDS
+// slots [64 i, 64 i + 64) and is issued by wave i % kKW. Rows past the
+// sequence arrive as zeros.
+template <int CH>
+__device__ __forceinline__ void block_load_offsets(int w, int lane, int64_t ld, uint32_t* off) {
+  constexpr int NI = CH / 2;
+#pragma unroll
+  for (int j = 0; j < (NI + kKW - 1) / kKW; ++j) {
+    const int s = (w + j * kKW) * 64 + lane;
+    const int r = s / CH, c = (s % CH) ^ swz_dual<CH>(r);
+    off[j] = static_cast<uint32_t>(r * ld * 2 + c * 16);
+  }
+}
+
+template <int CH>
+__device__ __forceinline__ void issue_block(const char* base, int64_t ld, int n, int r0, int w, const uint32_t* off,
+                                            char* dst) {
+  constexpr int NI = CH / 2;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + static_cast<int64_t>(r0) * ld * 2,
+                                              static_cast<int64_t>(n - r0) * ld * 2);
+#pragma unroll
+  for (int j = 0; j < (NI + kKW - 1) / kKW; ++j) {
+    const int i = w + j * kKW;
+    if (i < NI) load_lds16(rs, dst + i * 1024, off[j]);
+  }
+}
+
+// The 32 timestamps (wave kKW - 2; zeros without timestamps) and the
+// metadata record (wave kKW - 1) of the query block at row r0.
+__device__ __forceinline__ void issue_block_extras(const int64_t* tsbase, const BlockMeta* mbase, int n, int r0,
+                                                   int w, int lane, int64_t* st, BlockMeta* sm) {
+  if (w == kKW - 2 && lane < 16) {
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(tsbase ? tsbase + r0 : nullptr,
+                                                tsbase ? static_cast<int64_t>(n - r0) * 8 : 0);
+    load_lds16(rt, reinterpret_cast<char*>(st), lane * 16);
+  }
+  if (w == kKW - 1 && lane < 2) {
+    const int blk = r0 / 32, nblk = (n + 31) / 32;
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(mbase + blk, static_cast<int64_t>(nblk - blk) * 32);
+    load_lds16(rm, reinterpret_cast<char*>(sm), lane * 16);
+  }
+}
+
+// xinfo word: bits 0-1 the path, bits 8-15 the low time bucket of a uniform
+// or two-bucket block, bit 16 set when every time bucket of the block is
+// below kGFast.
+constexpr int kInfoFastTime = 1 << 16;
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g) {
   static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims");
   const AttnArgs& a = g.f;
   constexpr int KB = DQK / 16, VB = DV / 16;       // k-steps of S and dA
   constexpr int NQ = DQK / 32, NV = DV / 32;       // 32-column groups of dK and dV
   constexpr int QCH = DQK / 8, DCH = DV / 8;       // 16-byte chunks per Q / dO row
-  constexpr int QI = (QCH + kBW - 1) / kBW, DI = (DCH + kBW - 1) / kBW;
+  constexpr int QI = (QCH / 2 + kKW - 1) / kKW, DI = (DCH / 2 + kKW - 1) / kKW;
 
   const int item_idx = blockIdx.x;
   if (item_idx >= *a.item_count) return;
@@ -276,207 +355,261 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
   const int kt = ntl - 1 - item_qtile(item);
   const int k0 = kt * kAttnBM;
 
-  // One LDS object: with two, the module's LDS lowering gives every access
-  // the scope of its object, so reads of a tile could no longer be told apart
-  // from the direct loads filling the other tile of the same object, and
-  // every step would wait for the next tile's loads.
-  struct KvSmem {
-    BwdSmem<DQK, DV> t;
-    BwdGradSmem g;
-  };
-  __shared__ KvSmem lds;
-  BwdSmem<DQK, DV>& sm = lds.t;
-  BwdGradSmem& gs = lds.g;
+  __shared__ KvLds<DQK, DV> lds;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
-  const int kw = k0 + 32 * w;     // first key of this wave
+  const int grp = w & 3;
+  const int kw = k0 + 32 * grp;   // first key of this wave's group
   const int key = kw + lr;        // this lane's key (column of S)
   const bool has_time = a.time_table != nullptr, has_pos = a.pos_table != nullptr;
   const int Bp = a.pos_buckets, Bt = a.time_buckets;
+  // index bounds of the staged tables (a missing table is one zero entry)
+  const int pos_hi = has_pos ? Bp - 1 : 0, time_nb = has_time ? min(Bt, kBwdTimeSlots) : 1;
   const BlockMeta* meta_row =
       static_cast<const BlockMeta*>(a.meta) + h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * a.tile_base[b];
 
-  if (has_pos)
-    for (int i = tid; i < Bp; i += kBThreads) sm.pos[i] = kLog2e * a.pos_table[h * Bp + i];
-  if (has_time)
-    for (int i = tid; i < min(Bt, kBwdTimeSlots); i += kBThreads) sm.time[i] = kLog2e * a.time_table[h * Bt + i];
-  for (int i = tid; i < kBW * kBwdPosMax; i += kBThreads) (&gs.gpos[0][0])[i] = 0.f;
-  for (int i = tid; i < kBW * kBwdTimeSlots * 64; i += kBThreads) (&gs.gtime[0][0][0])[i] = 0.f;
-  const float pos_last = has_pos ? kLog2e * a.pos_table[h * Bp + Bp - 1] : 0.f;
-
-  // K and V rows of this lane's key: B operands of S = Q K^T and dA = dO V^T
-  const __bf16* kp = static_cast<const __bf16*>(a.k);
-  const __bf16* vp = static_cast<const __bf16*>(a.v);
-  bf16x8_t kf[KB], vf[VB];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-    kf[kb] = key < n ? *reinterpret_cast<const bf16x8_t*>(kp + (seq0 + key) * a.ldk + h * DQK + kb * 16 + lh * 8)
-                     : bf16x8_t{};
-#pragma unroll
-  for (int vb = 0; vb < VB; ++vb)
-    vf[vb] = key < n ? *reinterpret_cast<const bf16x8_t*>(vp + (seq0 + key) * a.ldv + h * DV + vb * 16 + lh * 8)
-                     : bf16x8_t{};
-  const int64_t tk = (has_time && key < n) ? a.ts[seq0 + key] : 0;
-  int64_t tk_min = 0, tk_max = 0;
-  if (has_time && kw < n) {
-    tk_min = uniform_i64(meta_row[kw / 32].tmin);
-    tk_max = uniform_i64(meta_row[kw / 32].tmax);
-  }
-  const float alpha_l = a.alpha * kLog2e;
-
-  f32x16_t dva[NV], dka[NQ];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) dva[i] = f32x16_t{};
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) dka[i] = f32x16_t{};
-  float far_acc = 0.f;   // dS' of the blocks whose pairs all read position bucket Bp - 1
+  for (int i = tid; i <= pos_hi; i += kKThreads) lds.pos[i] = has_pos ? kLog2e * a.pos_table[h * Bp + i] : 0.f;
+  for (int i = tid; i < time_nb; i += kKThreads) lds.time[i] = has_time ? kLog2e * a.time_table[h * Bt + i] : 0.f;
+  for (int i = tid; i < 4 * kBwdPosMax; i += kKThreads) (&lds.gpos[0][0])[i] = 0.f;
+  for (int i = tid; i < 4 * kGFast * 64; i += kKThreads) (&lds.gtime[0][0][0])[i] = 0.f;
+  for (int i = tid; i < 4 * kBwdTimeSlots; i += kKThreads) (&lds.gslow[0][0])[i] = 0.f;
 
   uint32_t qoff[QI], doff[DI];
-  tile_load_offsets<QCH>(w, lane, a.ldq, qoff);
-  tile_load_offsets<DCH>(w, lane, g.lddo, doff);
+  block_load_offsets<QCH>(w, lane, a.ldq, qoff);
+  block_load_offsets<DCH>(w, lane, g.lddo, doff);
   const char* qbase = static_cast<const char*>(a.q) + (seq0 * a.ldq + h * DQK) * 2;
   const char* dbase = static_cast<const char*>(g.d_o) + (seq0 * g.lddo + h * DV) * 2;
   const int64_t* tsbase = has_time ? a.ts + seq0 : nullptr;
-  uint32_t q_row[KB], d_row[VB];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) q_row[kb] = row_read_offset<QCH>(lr, lh, kb);
-#pragma unroll
-  for (int vb = 0; vb < VB; ++vb) d_row[vb] = row_read_offset<DCH>(lr, lh, vb);
-  uint32_t q_tr0[NQ], q_tr1[NQ], d_tr0[NV], d_tr1[NV];
-#pragma unroll
-  for (int nb = 0; nb < NQ; ++nb) tr_read_offsets<QCH>(lane, nb, q_tr0[nb], q_tr1[nb]);
-#pragma unroll
-  for (int nb = 0; nb < NV; ++nb) tr_read_offsets<DCH>(lane, nb, d_tr0[nb], d_tr1[nb]);
 
-  const int tq0 = k0 / kBBN;                       // first query tile: holds the diagonal
-  const int ntq = (n + kBBN - 1) / kBBN - tq0;     // >= 1
-  float* gpos = gs.gpos[w];
-  float* gtime = &gs.gtime[w][0][lane];   // bucket b of this lane: gtime[64 b]
-
-  // dV += P^T dO and dK += dS^T Q of a block run one block late: they are
-  // issued right after the next block's S and dA products, so they execute
-  // while that block's P and dS are computed. Carried between blocks: the
-  // packed P and dS and the block's transposed dO and Q fragments (read before
-  // the barrier that may recycle their tile). Zero-initialized, the first
-  // block's late products add nothing.
-  bf16x8_t pa_prev[2], sa_prev[2], ob_prev[2 * NV], qt_prev[2 * NQ];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) pa_prev[kk] = sa_prev[kk] = bf16x8_t{};
-#pragma unroll
-  for (int i = 0; i < 2 * NV; ++i) ob_prev[i] = bf16x8_t{};
-#pragma unroll
-  for (int i = 0; i < 2 * NQ; ++i) qt_prev[i] = bf16x8_t{};
-  auto late_products = [&] __device__() __attribute__((always_inline)) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int nb = 0; nb < NV; ++nb)
-        dva[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_prev[kk], ob_prev[kk * NV + nb], dva[nb], 0, 0, 0);
-#pragma unroll
-      for (int nb = 0; nb < NQ; ++nb)
-        dka[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa_prev[kk], qt_prev[kk * NQ + nb], dka[nb], 0, 0, 0);
+  const int qb0 = k0 / 32;                   // first query block: key group 0's diagonal
+  const int nqb = (n + 31) / 32 - qb0;       // >= 1
+  // a block's pairs are all masked when its last row precedes the group's first key
+  auto block_active = [&](int t) __attribute__((always_inline)) { return kw < n && (qb0 + t) * 32 + 31 >= kw; };
+  // Q, dO, timestamps and metadata of block t + 1 (their slot was released
+  // by the barrier that ended block t - 1)
+  auto issue = [&](int t, char* nq, char* nd, int64_t* nt, BlockMeta* nm) __attribute__((always_inline)) {
+    if (t + 1 < nqb) {
+      const int r0 = (qb0 + t + 1) * 32;
+      issue_block<QCH>(qbase, a.ldq, n, r0, w, qoff, nq);
+      issue_block<DCH>(dbase, g.lddo, n, r0, w, doff, nd);
+      issue_block_extras(tsbase, meta_row, n, r0, w, lane, nt, nm);
     }
   };
 
-  auto step = [&] __device__(const char* __restrict__ rq, const char* __restrict__ rd,
-                             const int64_t* __restrict__ rt, const BlockMeta* __restrict__ rm,
-                             char* __restrict__ nq, char* __restrict__ nd, int64_t* __restrict__ nt,
-                             BlockMeta* __restrict__ nm, const float* __restrict__ spos,
-                             const float* __restrict__ stime, float* __restrict__ gpos,
-                             float* __restrict__ gtime, int t) __attribute__((always_inline)) {
-    const int i0 = (tq0 + t) * kBBN;
-    if (t + 1 < ntq)
-      issue_rows_tile<QCH, DCH>(qbase, dbase, a.ldq, g.lddo, tsbase, meta_row, n, i0 + kBBN, w, lane, qoff, doff, nq,
-                                nd, nt, nm);
+  issue_block<QCH>(qbase, a.ldq, n, qb0 * 32, w, qoff, lds.q[0]);
+  issue_block<DCH>(dbase, g.lddo, n, qb0 * 32, w, doff, lds.d[0]);
+  issue_block_extras(tsbase, meta_row, n, qb0 * 32, w, lane, lds.t[0], &lds.m[0]);
+  wait_vmcnt(0);
+  __syncthreads();   // also publishes the staged tables and the zeroed gradient tables
+
+  const float inv_n = a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n);
+
+  if (w < 4) {
+    // ======================= score wave =======================
+    const __bf16* kp = static_cast<const __bf16*>(a.k);
+    bf16x8_t kf[KB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int qa = i0 + 32 * qb;
-      const bool active = kw < n && qa < n && qa + 31 >= kw;
-      f32x16_t s = f32x16_t{}, da = f32x16_t{};
-      const char* qblk = rq + qb * 32 * QCH * 16;
-      const char* dblk = rd + qb * 32 * DCH * 16;
-      // all A fragments first (their reads overlap), then the two chains
-      bf16x8_t qfr[KB], dfr[VB];
+    for (int kb = 0; kb < KB; ++kb)
+      kf[kb] = key < n ? *reinterpret_cast<const bf16x8_t*>(kp + (seq0 + key) * a.ldk + h * DQK + kb * 16 + lh * 8)
+                       : bf16x8_t{};
+    const int64_t tk = (has_time && key < n) ? a.ts[seq0 + key] : 0;
+    int64_t tk_min = 0, tk_max = 0;
+    if (has_time && kw < n) {
+      tk_min = uniform_i64(meta_row[kw / 32].tmin);
+      tk_max = uniform_i64(meta_row[kw / 32].tmax);
+    }
+    const float alpha_l = a.alpha * kLog2e;
+    const float pos_last = has_pos ? kLog2e * a.pos_table[h * Bp + Bp - 1] : 0.f;
+    uint32_t q_row[KB], d_tr0[NV], d_tr1[NV];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) qfr[kb] = *reinterpret_cast<const bf16x8_t*>(qblk + q_row[kb]);
+    for (int kb = 0; kb < KB; ++kb) q_row[kb] = row_read_offset<QCH>(lr, lh, kb);
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb) dfr[vb] = *reinterpret_cast<const bf16x8_t*>(dblk + d_row[vb]);
+    for (int nb = 0; nb < NV; ++nb) tr_read_offsets<DCH>(lane, nb, d_tr0[nb], d_tr1[nb]);
+    f32x16_t dva[NV];
 #pragma unroll
-      for (int kb = 0; kb < (KB > VB ? KB : VB); ++kb) {
-        if (kb < KB) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[kb], kf[kb], s, 0, 0, 0);
-        if (kb < VB) da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr[kb], vf[kb], da, 0, 0, 0);
+    for (int i = 0; i < NV; ++i) dva[i] = f32x16_t{};
+
+    // Every LDS buffer comes in through a __restrict__ parameter: the step
+    // reads block t's slots and fills block t + 1's, so the compiler does not
+    // wait for the loads in flight before reading LDS.
+    auto step = [&](const char* __restrict__ rq, const char* __restrict__ rd, const int64_t* __restrict__ rt,
+                    const BlockMeta* __restrict__ rm, f32x4_t* __restrict__ xg, u32x4_t* __restrict__ xb,
+                    int* __restrict__ xinfo, char* __restrict__ nq, char* __restrict__ nd, int64_t* __restrict__ nt,
+                    BlockMeta* __restrict__ nm, const float* __restrict__ spos, const float* __restrict__ stime,
+                    int t) __attribute__((always_inline)) {
+      issue(t, nq, nd, nt, nm);
+      if (!block_active(t)) return;
+      const int qa = (qb0 + t) * 32;
+      bf16x8_t qfr[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) qfr[kb] = *reinterpret_cast<const bf16x8_t*>(rq + q_row[kb]);
+      f32x16_t s = f32x16_t{};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[kb], kf[kb], s, 0, 0, 0);
+      // s[4g+e]: query row qa + 8g + 4lh + e, key `key`
+      int64_t tq_min = 0, tq_max = 0;
+      if (has_time) {
+        tq_min = uniform_i64(rm->tmin);
+        tq_max = uniform_i64(rm->tmax);
       }
-      // the previous block's dV, dK products, then this block's transposed
-      // fragments for its own (one block later)
-      late_products();
+      const BlockClass c =
+          classify_block(qa, kw, n, has_pos, Bp, has_time, Bt, tq_min, tq_max, tk_min, tk_max, pos_last, stime);
+      float p[16], dsl[16];
+      int tb[16];
+      int info = c.path | (c.tlo << 8);
+      if (c.path != kBGeneral) {
+        const int64_t lim = tk + ((int64_t(1) << (c.tlo + 1)) - 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int il = 8 * (r >> 2) + 4 * lh + (r & 3);
+          const bool hi = c.path == kBTwoTime && rt[il] >= lim;
+          silu_and_grad(fmaf(s[r], alpha_l, hi ? c.chi : c.clo), p[r], dsl[r]);
+          tb[r] = c.tlo + (hi ? 1 : 0);
+        }
+      } else {
+        // straight-line per pair: both table lookups (zero tables stand in
+        // for missing ones), the causal / sequence-end mask as selects
+        if (!has_time || time_bucket64(tq_max - tk_min, Bt) < kGFast) info |= kInfoFastTime;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int il = 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int i = qa + il;
+          const bool valid = i >= key && i < n && key < n;
+          const int pb = min(max(i - key, 0), pos_hi);
+          const int tbr = time_bucket64(rt[il] - tk, time_nb);
+          float pl, dl;
+          silu_and_grad(fmaf(s[r], alpha_l, spos[pb] + stime[tbr]), pl, dl);
+          p[r] = valid ? pl : 0.f;
+          dsl[r] = valid ? dl : 0.f;
+          // a masked pair adds 0 to bucket 0: a key past the sequence end
+          // reads timestamp 0, and its bucket is not bounded by the block's
+          tb[r] = valid ? tbr : 0;
+        }
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        xg[q4 * 64 + lane] = f32x4_t{dsl[4 * q4], dsl[4 * q4 + 1], dsl[4 * q4 + 2], dsl[4 * q4 + 3]};
+      }
+      u32x4_t tw;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        tw[q4] = static_cast<uint32_t>(tb[4 * q4]) | (static_cast<uint32_t>(tb[4 * q4 + 1]) << 8) |
+                 (static_cast<uint32_t>(tb[4 * q4 + 2]) << 16) | (static_cast<uint32_t>(tb[4 * q4 + 3]) << 24);
+      xb[lane] = tw;
+      if (lane == 0) *xinfo = info;
+      // dV += P^T dO over the block's 32 query rows (two 16-row steps)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const char* dst = dblk + kk * 16 * DCH * 16;
-        const char* qst = qblk + kk * 16 * QCH * 16;
+        bf16x8_t pa;
 #pragma unroll
-        for (int nb = 0; nb < NV; ++nb)
-          ob_prev[kk * NV + nb] =
+        for (int i = 0; i < 8; ++i) pa[i] = static_cast<__bf16>(p[kk * 8 + i]);
+        const char* dst = rd + kk * 16 * DCH * 16;
+#pragma unroll
+        for (int nb = 0; nb < NV; ++nb) {
+          const bf16x8_t ob =
               __builtin_shufflevector(tr_read(dst + d_tr0[nb]), tr_read(dst + d_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int nb = 0; nb < NQ; ++nb)
-          qt_prev[kk * NQ + nb] =
-              __builtin_shufflevector(tr_read(qst + q_tr0[nb]), tr_read(qst + q_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-      __builtin_amdgcn_sched_barrier(0);   // the products above go out before the P / dS arithmetic
-      // s[4g+e], da[4g+e]: query row qa + 8g + 4lh + e, key `key`
-      float p[16], ds[16];
-      if (!active) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = ds[r] = 0.f;
-      } else {
-        int64_t tq_min = 0, tq_max = 0;
-        if (has_time) {
-          tq_min = uniform_i64(rm[qb].tmin);
-          tq_max = uniform_i64(rm[qb].tmax);
+          dva[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, ob, dva[nb], 0, 0, 0);
         }
-        const BlockClass c =
-            classify_block(qa, kw, n, has_pos, Bp, has_time, Bt, tq_min, tq_max, tk_min, tk_max, pos_last, stime);
-        if (c.path != kBGeneral) {
-          const int64_t lim = tk + ((int64_t(1) << (c.tlo + 1)) - 1);
+      }
+    };
+
+    for (int t = 0; t < nqb; ++t) {
+      const int sl = t % kKRing, nx = (t + 1) % kKRing;
+      step(lds.q[sl], lds.d[sl], lds.t[sl], &lds.m[sl], &lds.xg[t & 1][grp][0][0], &lds.xb[t & 1][grp][0],
+           &lds.xinfo[t & 1][grp], lds.q[nx], lds.d[nx], lds.t[nx], &lds.m[nx], lds.pos, lds.time, t);
+      wait_vmcnt(0);
+      tile_barrier();
+    }
+
+    // ---- dV: accumulator [i][r] holds key kw + 8(r/4) + 4 lh + r%4, column 32 i + lr
+    const float sv = inv_n / kLog2e;
+    __bf16* dvp = static_cast<__bf16*>(g.dv) + (seq0 + kw) * g.lddv + h * DV + lr;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (kw + kr < n) {
+#pragma unroll
+        for (int nb = 0; nb < NV; ++nb) dvp[kr * g.lddv + nb * 32] = static_cast<__bf16>(dva[nb][r] * sv);
+      }
+    }
+  } else {
+    // ====================== gradient wave ======================
+    const __bf16* vp = static_cast<const __bf16*>(a.v);
+    bf16x8_t vf[VB];
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+      vf[vb] = key < n ? *reinterpret_cast<const bf16x8_t*>(vp + (seq0 + key) * a.ldv + h * DV + vb * 16 + lh * 8)
+                       : bf16x8_t{};
+    uint32_t d_row[VB], q_tr0[NQ], q_tr1[NQ];
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) d_row[vb] = row_read_offset<DCH>(lr, lh, vb);
+#pragma unroll
+    for (int nb = 0; nb < NQ; ++nb) tr_read_offsets<QCH>(lane, nb, q_tr0[nb], q_tr1[nb]);
+    f32x16_t dka[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) dka[i] = f32x16_t{};
+    float far_acc = 0.f;   // dS' of the pairs that read position bucket Bp - 1
+
+    // Block t: dA, dS, the gradient-table updates and dK. Its buffers come in
+    // through __restrict__ parameters (as in the score wave's step).
+    auto grad_block = [&](const char* __restrict__ rd, const char* __restrict__ rq, const f32x4_t* __restrict__ xg,
+                          const u32x4_t* __restrict__ xb, const int* __restrict__ xinfo, float* __restrict__ gpos,
+                          float* __restrict__ gtime, float* __restrict__ gslow, int t) __attribute__((always_inline)) {
+      const int qa = (qb0 + t) * 32;
+      bf16x8_t dfr[VB];
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) dfr[vb] = *reinterpret_cast<const bf16x8_t*>(rd + d_row[vb]);
+      f32x16_t da = f32x16_t{};
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr[vb], vf[vb], da, 0, 0, 0);
+      const int info = __builtin_amdgcn_readfirstlane(*xinfo);
+      const int path = info & 3, tlo = (info >> 8) & 255;
+      const u32x4_t tw = xb[lane];
+      float ds[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4_t v = xg[q4 * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ds[4 * q4 + e] = da[4 * q4 + e] * v[e];
+      }
+      if (g.grad_stride > 0) {
+        if (path != kBGeneral) {
+          // every pair reads position bucket Bp - 1 and time bucket tlo or tlo + 1
           float slo = 0.f, shi = 0.f;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int il = qb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            const bool hi = c.path == kBTwoTime && rt[il] >= lim;
-            const float x = fmaf(s[r], alpha_l, hi ? c.chi : c.clo);
-            float dsl;
-            silu_and_grad(x, p[r], dsl);
-            ds[r] = da[r] * dsl;
-            if (hi) shi += ds[r];
-            else slo += ds[r];
+            const bool hi = ((tw[r >> 2] >> (8 * (r & 3))) & 255) != static_cast<uint32_t>(tlo);
+            slo += hi ? 0.f : ds[r];
+            shi += hi ? ds[r] : 0.f;
           }
           if (has_pos) far_acc += slo + shi;
           if (has_time) {
-            gtime[64 * c.tlo] += slo;
-            if (c.path == kBTwoTime) gtime[64 * (c.tlo + 1)] += shi;
+            if (tlo + 1 < kGFast) {
+              gtime[64 * tlo] += slo;
+              if (path == kBTwoTime) gtime[64 * (tlo + 1)] += shi;
+            } else {
+              const float s0 = wave_sum(slo), s1 = wave_sum(shi);
+              if (lane == 0) {
+                gslow[tlo] += s0;
+                if (path == kBTwoTime) gslow[tlo + 1] += s1;
+              }
+            }
           }
         } else {
+          if (has_time) {
+            if (info & kInfoFastTime) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int il = qb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            const int i = i0 + il;
-            const bool valid = i >= key && i < n && key < n;
-            const int pb = min(max(i - key, 0), Bp - 1);
-            float cb = 0.f;
-            if (has_pos) cb = spos[pb];
-            int tb = 0;
-            if (has_time) {
-              tb = time_bucket64(rt[il] - tk, Bt);
-              cb += stime[tb];
+              for (int r = 0; r < 16; ++r) gtime[64 * ((tw[r >> 2] >> (8 * (r & 3))) & 255)] += ds[r];
+            } else {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int tbr = (tw[r >> 2] >> (8 * (r & 3))) & 255;
+                if (tbr < kGFast) gtime[64 * tbr] += ds[r];
+                else lds_add_f32(&gslow[tbr], ds[r]);
+              }
             }
-            const float x = fmaf(s[r], alpha_l, cb);
-            float pl, dsl;
-            silu_and_grad(x, pl, dsl);
-            p[r] = valid ? pl : 0.f;
-            ds[r] = valid ? da[r] * dsl : 0.f;
-            if (has_time) gtime[64 * tb] += ds[r];
           }
           // position buckets: a valid pair of the block reads bucket
           // min(i - key, Bp - 1) = min(qa - kw + d, Bp - 1) with d = i' - lr
@@ -499,80 +632,92 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
           }
         }
       }
-      // P and dS of this block's 32 query rows (two 16-row steps), for the
-      // late products
+      // dK += dS^T Q over the block's 32 query rows (two 16-row steps)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8_t sa;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pa_prev[kk][i] = static_cast<__bf16>(p[kk * 8 + i]);
-          sa_prev[kk][i] = static_cast<__bf16>(ds[kk * 8 + i]);
+        for (int i = 0; i < 8; ++i) sa[i] = static_cast<__bf16>(ds[kk * 8 + i]);
+        const char* qst = rq + kk * 16 * QCH * 16;
+#pragma unroll
+        for (int nb = 0; nb < NQ; ++nb) {
+          const bf16x8_t qt =
+              __builtin_shufflevector(tr_read(qst + q_tr0[nb]), tr_read(qst + q_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
+          dka[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, qt, dka[nb], 0, 0, 0);
         }
+      }
+    };
+
+    // step t: block t - 1 (its SiLU' was written before the last barrier),
+    // then the loads of block t + 1 (the compiler would otherwise wait for
+    // them before the block's LDS reads)
+    for (int t = 0; t < nqb; ++t) {
+      if (t >= 1 && block_active(t - 1)) {
+        const int pv = (t - 1) % kKRing;
+        grad_block(lds.d[pv], lds.q[pv], &lds.xg[(t - 1) & 1][grp][0][0], &lds.xb[(t - 1) & 1][grp][0],
+                   &lds.xinfo[(t - 1) & 1][grp], lds.gpos[grp], &lds.gtime[grp][0][lane], lds.gslow[grp], t - 1);
+      }
+      const int nx = (t + 1) % kKRing;
+      issue(t, lds.q[nx], lds.d[nx], lds.t[nx], &lds.m[nx]);
+      wait_vmcnt(0);
+      tile_barrier();
     }
-  };
+    if (block_active(nqb - 1)) {
+      const int pv = (nqb - 1) % kKRing;
+      grad_block(lds.d[pv], lds.q[pv], &lds.xg[(nqb - 1) & 1][grp][0][0], &lds.xb[(nqb - 1) & 1][grp][0],
+                 &lds.xinfo[(nqb - 1) & 1][grp], lds.gpos[grp], &lds.gtime[grp][0][lane], lds.gslow[grp], nqb - 1);
+    }
 
-  issue_rows_tile<QCH, DCH>(qbase, dbase, a.ldq, g.lddo, tsbase, meta_row, n, tq0 * kBBN, w, lane, qoff, doff,
-                            sm.a[0], sm.b[0], sm.t[0], sm.m[0]);
-  wait_vmcnt(0);
-  __syncthreads();   // also publishes the staged tables and the zeroed gradient tables
-  for (int t = 0; t < ntq; ++t) {
-    const int buf = t & 1;
-    step(sm.a[buf], sm.b[buf], sm.t[buf], sm.m[buf], sm.a[buf ^ 1], sm.b[buf ^ 1], sm.t[buf ^ 1], sm.m[buf ^ 1],
-         sm.pos, sm.time, gpos, gtime, t);
-    wait_vmcnt(0);
-    tile_barrier();
-  }
-
-  late_products();   // the last block's
-
-  // ---- dK, dV: accumulator [i][r] holds key kw + 8(r/4) + 4 lh + r%4, column 32 i + lr
-  const float inv_n = a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n);
-  const float sv = inv_n / kLog2e, sk = a.alpha * inv_n;
-  __bf16* dvp = static_cast<__bf16*>(g.dv) + (seq0 + kw) * g.lddv + h * DV + lr;
-  __bf16* dkp = static_cast<__bf16*>(g.dk) + (seq0 + kw) * g.lddk + h * DQK + lr;
+    // ---- dK: accumulator [i][r] holds key kw + 8(r/4) + 4 lh + r%4, column 32 i + lr
+    const float sk = a.alpha * inv_n;
+    __bf16* dkp = static_cast<__bf16*>(g.dk) + (seq0 + kw) * g.lddk + h * DQK + lr;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int kr = 8 * (r >> 2) + 4 * lh + (r & 3);
-    if (kw + kr < n) {
+    for (int r = 0; r < 16; ++r) {
+      const int kr = 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (kw + kr < n) {
 #pragma unroll
-      for (int nb = 0; nb < NV; ++nb) dvp[kr * g.lddv + nb * 32] = static_cast<__bf16>(dva[nb][r] * sv);
-#pragma unroll
-      for (int nb = 0; nb < NQ; ++nb) dkp[kr * g.lddk + nb * 32] = static_cast<__bf16>(dka[nb][r] * sk);
+        for (int nb = 0; nb < NQ; ++nb) dkp[kr * g.lddk + nb * 32] = static_cast<__bf16>(dka[nb][r] * sk);
+      }
+    }
+    if (g.grad_stride > 0 && has_pos) {
+      const float f = wave_sum(far_acc);
+      if (lane == 0) lds.gpos[grp][Bp - 1] += f;
     }
   }
 
   // ---- bias-table gradients of this key tile
   if (g.grad_stride > 0) {
-    if (has_pos) {
-      const float f = wave_sum(far_acc);
-      if (lane == 0) gpos[Bp - 1] += f;
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the asm adds above have landed
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the asm adds have landed
     __syncthreads();
     float* prow = g.partial + (static_cast<int64_t>(h) * g.tile_rows + a.tile_base[b] + kt) * g.grad_stride;
     if (has_pos)
-      for (int i = tid; i < Bp; i += kBThreads) {
+      for (int i = tid; i < Bp; i += kKThreads) {
         float s = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < kBW; ++ww) s += gs.gpos[ww][i];
+        for (int ww = 0; ww < 4; ++ww) s += lds.gpos[ww][i];
         prow[i] = s * inv_n;
       }
     if (has_time) {
-      // bucket tid / 4: thread (tid & 3) sums wave (tid & 3)'s 64 lane columns,
-      // then the 4 threads (adjacent lanes) combine, in a fixed order
-      static_assert(kBThreads == 4 * kBwdTimeSlots && kBW == 4, "one bucket per 4 threads");
+      // bucket tid / 8: thread part = tid % 8 sums half part % 2 of gradient
+      // wave part / 2's lane columns, then the 8 threads (adjacent lanes)
+      // combine in a fixed order
+      static_assert(kKThreads == 8 * kBwdTimeSlots, "one bucket per 8 threads");
       float* trow = prow + (has_pos ? Bp : 0);
-      const int tb = tid >> 2, ww = tid & 3;
-      const f32x4_t* col = reinterpret_cast<const f32x4_t*>(&gs.gtime[ww][tb][0]);
+      const int tb = tid >> 3, part = tid & 7, ww = part >> 1, half = part & 1;
       float s = 0.f;
+      if (tb < kGFast) {
+        const f32x4_t* col = reinterpret_cast<const f32x4_t*>(&lds.gtime[ww][tb][half * 32]);
 #pragma unroll
-      for (int c4 = 0; c4 < 16; ++c4) {
-        const f32x4_t v4 = col[c4];
-        s += (v4[0] + v4[1]) + (v4[2] + v4[3]);
+        for (int c4 = 0; c4 < 8; ++c4) {
+          const f32x4_t v4 = col[c4];
+          s += (v4[0] + v4[1]) + (v4[2] + v4[3]);
+        }
       }
+      if (half == 0) s += lds.gslow[ww][tb];
       s += __shfl_xor(s, 1, 64);
       s += __shfl_xor(s, 2, 64);
-      if (ww == 0) trow[tb] = s * inv_n;
+      s += __shfl_xor(s, 4, 64);
+      if (part == 0) trow[tb] = s * inv_n;
     }
   }
 }
@@ -851,9 +996,9 @@ __global__ __launch_bounds__(kReduceGroups * 64) void attn_bwd_bias_reduce_kerne
 }
 
 template <typename K>
-hipError_t launch_bwd_items(K kernel, const AttnBwdArgs& g, hipStream_t stream) {
+hipError_t launch_bwd_items(K kernel, int threads, const AttnBwdArgs& g, hipStream_t stream) {
   if (g.f.capacity <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(g.f.capacity)), dim3(kBThreads), 0, stream, g);
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(g.f.capacity)), dim3(threads), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -862,12 +1007,12 @@ hipError_t launch_bwd_dims(const AttnBwdArgs& g, hipStream_t stream) {
   hipError_t e;
   {
     TimedScope timed(kTimedAttnBwdKv, stream);
-    e = launch_bwd_items(attn_bwd_kv_kernel<D, D>, g, stream);
+    e = launch_bwd_items(attn_bwd_kv_kernel<D, D>, kKThreads, g, stream);
   }
   if (e != hipSuccess) return e;
   {
     TimedScope timed(kTimedAttnBwdQ, stream);
-    e = launch_bwd_items(attn_bwd_q_kernel<D, D>, g, stream);
+    e = launch_bwd_items(attn_bwd_q_kernel<D, D>, kBThreads, g, stream);
   }
   if (e != hipSuccess) return e;
   if (g.grad_stride > 0) {
