@@ -248,26 +248,31 @@ __device__ __forceinline__ float wave_sum(float v) {
 // diagonal to the end of the sequence. Waves w and w + 4 of the workgroup run
 // on one SIMD and share a group of 32 keys (kw = k0 + 32 (w & 3), one key per
 // lane as the column of S), in two roles:
-//   score wave (w < 4)      S = Q K^T, the bias, P = SiLU(x) and SiLU'(x) of
-//                           every pair (masked pairs: 0), dV += P^T dO;
+//   score wave (w < 4)      S = Q K^T one block ahead (its products run under
+//                           the current block's arithmetic), the bias,
+//                           P = SiLU(x) and SiLU'(x) of every pair (masked
+//                           pairs: 0), dV += P^T dO, and the tile loads;
 //   gradient wave (w >= 4)  one block behind: dA = dO V^T, dS = dA SiLU'(x),
 //                           the bias-table gradients, dK += dS^T Q.
 // SiLU'(x) (fp32) and each pair's time bucket reach the gradient wave through
 // LDS. Each role's registers fit two waves per SIMD; the per-pair arithmetic
 // of the score wave overlaps the gradient wave's products and its
 // read-modify-write chains on the gradient tables. K (score) and V (gradient)
-// of the lane's key stay in registers as MFMA B operands; Q and dO blocks
-// stream through a ring of three LDS slots (block t + 1 loads while t and
-// t - 1 are read), with one barrier per block.
+// of the lane's key stay in registers as MFMA B operands; Q blocks stream
+// through four LDS slots (block t + 2 loads while t - 1 .. t + 1 are read),
+// dO blocks, timestamps and metadata through three (block t + 1 loads), with
+// one barrier per block.
 // ============================================================================
 constexpr int kKW = 8;                // waves of a key-pass workgroup
 constexpr int kKThreads = kKW * 64;
-constexpr int kKRing = 3;             // 32-row Q and dO slots
+constexpr int kKRing = 3;             // 32-row dO slots (and timestamps, metadata)
+constexpr int kQRing = 4;             // 32-row Q slots
+constexpr int kKIssue = 4;            // waves that issue the tile loads (the score waves)
 constexpr int kGFast = 32;            // time buckets summed in lane-private columns
 
 template <int DQK, int DV>
 struct KvLds {
-  __attribute__((aligned(16))) char q[kKRing][32 * DQK * 2];
+  __attribute__((aligned(16))) char q[kQRing][32 * DQK * 2];
   __attribute__((aligned(16))) char d[kKRing][32 * DV * 2];
   __attribute__((aligned(16))) int64_t t[kKRing][32];
   __attribute__((aligned(16))) BlockMeta m[kKRing];
@@ -287,14 +292,14 @@ struct KvLds {
 
 // Direct loads of one 32-row block of a row-major matrix with CH 16-byte
 // chunks per row, stored with the dual-read swizzle: instruction i fills LDS
-// slots [64 i, 64 i + 64) and is issued by wave i % kKW. Rows past the
+// slots [64 i, 64 i + 64) and is issued by wave i % kKIssue. Rows past the
 // sequence arrive as zeros.
 template <int CH>
 __device__ __forceinline__ void block_load_offsets(int w, int lane, int64_t ld, uint32_t* off) {
   constexpr int NI = CH / 2;
 #pragma unroll
-  for (int j = 0; j < (NI + kKW - 1) / kKW; ++j) {
-    const int s = (w + j * kKW) * 64 + lane;
+  for (int j = 0; j < (NI + kKIssue - 1) / kKIssue; ++j) {
+    const int s = (w + j * kKIssue) * 64 + lane;
     const int r = s / CH, c = (s % CH) ^ swz_dual<CH>(r);
     off[j] = static_cast<uint32_t>(r * ld * 2 + c * 16);
   }
@@ -307,22 +312,22 @@ __device__ __forceinline__ void issue_block(const char* base, int64_t ld, int n,
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + static_cast<int64_t>(r0) * ld * 2,
                                               static_cast<int64_t>(n - r0) * ld * 2);
 #pragma unroll
-  for (int j = 0; j < (NI + kKW - 1) / kKW; ++j) {
-    const int i = w + j * kKW;
+  for (int j = 0; j < (NI + kKIssue - 1) / kKIssue; ++j) {
+    const int i = w + j * kKIssue;
     if (i < NI) load_lds16(rs, dst + i * 1024, off[j]);
   }
 }
 
-// The 32 timestamps (wave kKW - 2; zeros without timestamps) and the
-// metadata record (wave kKW - 1) of the query block at row r0.
+// The 32 timestamps (wave kKIssue - 2; zeros without timestamps) and the
+// metadata record (wave kKIssue - 1) of the query block at row r0.
 __device__ __forceinline__ void issue_block_extras(const int64_t* tsbase, const BlockMeta* mbase, int n, int r0,
                                                    int w, int lane, int64_t* st, BlockMeta* sm) {
-  if (w == kKW - 2 && lane < 16) {
+  if (w == kKIssue - 2 && lane < 16) {
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(tsbase ? tsbase + r0 : nullptr,
                                                 tsbase ? static_cast<int64_t>(n - r0) * 8 : 0);
     load_lds16(rt, reinterpret_cast<char*>(st), lane * 16);
   }
-  if (w == kKW - 1 && lane < 2) {
+  if (w == kKIssue - 1 && lane < 2) {
     const int blk = r0 / 32, nblk = (n + 31) / 32;
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(mbase + blk, static_cast<int64_t>(nblk - blk) * 32);
     load_lds16(rm, reinterpret_cast<char*>(sm), lane * 16);
@@ -341,7 +346,7 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
   constexpr int KB = DQK / 16, VB = DV / 16;       // k-steps of S and dA
   constexpr int NQ = DQK / 32, NV = DV / 32;       // 32-column groups of dK and dV
   constexpr int QCH = DQK / 8, DCH = DV / 8;       // 16-byte chunks per Q / dO row
-  constexpr int QI = (QCH / 2 + kKW - 1) / kKW, DI = (DCH / 2 + kKW - 1) / kKW;
+  constexpr int QI = (QCH / 2 + kKIssue - 1) / kKIssue, DI = (DCH / 2 + kKIssue - 1) / kKIssue;
 
   const int item_idx = blockIdx.x;
   if (item_idx >= *a.item_count) return;
@@ -387,20 +392,23 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
   const int nqb = (n + 31) / 32 - qb0;       // >= 1
   // a block's pairs are all masked when its last row precedes the group's first key
   auto block_active = [&](int t) __attribute__((always_inline)) { return kw < n && (qb0 + t) * 32 + 31 >= kw; };
-  // Q, dO, timestamps and metadata of block t + 1 (their slot was released
-  // by the barrier that ended block t - 1)
+  // (score waves) Q of block t + 2 and dO, timestamps, metadata of block
+  // t + 1; their slots were released by the barrier that ended block t - 1
   auto issue = [&](int t, char* nq, char* nd, int64_t* nt, BlockMeta* nm) __attribute__((always_inline)) {
+    if (t + 2 < nqb) issue_block<QCH>(qbase, a.ldq, n, (qb0 + t + 2) * 32, w, qoff, nq);
     if (t + 1 < nqb) {
       const int r0 = (qb0 + t + 1) * 32;
-      issue_block<QCH>(qbase, a.ldq, n, r0, w, qoff, nq);
       issue_block<DCH>(dbase, g.lddo, n, r0, w, doff, nd);
       issue_block_extras(tsbase, meta_row, n, r0, w, lane, nt, nm);
     }
   };
 
-  issue_block<QCH>(qbase, a.ldq, n, qb0 * 32, w, qoff, lds.q[0]);
-  issue_block<DCH>(dbase, g.lddo, n, qb0 * 32, w, doff, lds.d[0]);
-  issue_block_extras(tsbase, meta_row, n, qb0 * 32, w, lane, lds.t[0], &lds.m[0]);
+  if (w < kKIssue) {
+    issue_block<QCH>(qbase, a.ldq, n, qb0 * 32, w, qoff, lds.q[0]);
+    if (nqb > 1) issue_block<QCH>(qbase, a.ldq, n, (qb0 + 1) * 32, w, qoff, lds.q[1]);
+    issue_block<DCH>(dbase, g.lddo, n, qb0 * 32, w, doff, lds.d[0]);
+    issue_block_extras(tsbase, meta_row, n, qb0 * 32, w, lane, lds.t[0], &lds.m[0]);
+  }
   wait_vmcnt(0);
   __syncthreads();   // also publishes the staged tables and the zeroed gradient tables
 
@@ -434,20 +442,37 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
     // Every LDS buffer comes in through a __restrict__ parameter: the step
     // reads block t's slots and fills block t + 1's, so the compiler does not
     // wait for the loads in flight before reading LDS.
-    auto step = [&](const char* __restrict__ rq, const char* __restrict__ rd, const int64_t* __restrict__ rt,
+    // S of block t (computed one step earlier)
+    f32x16_t s_cur = f32x16_t{};
+    auto s_block = [&](const char* rq) __attribute__((always_inline)) {
+      bf16x8_t qfr[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) qfr[kb] = *reinterpret_cast<const bf16x8_t*>(rq + q_row[kb]);
+      f32x16_t sb = f32x16_t{};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[kb], kf[kb], sb, 0, 0, 0);
+      return sb;
+    };
+    auto step = [&](const char* __restrict__ rq1, const char* __restrict__ rd, const int64_t* __restrict__ rt,
                     const BlockMeta* __restrict__ rm, f32x4_t* __restrict__ xg, u32x4_t* __restrict__ xb,
                     int* __restrict__ xinfo, char* __restrict__ nq, char* __restrict__ nd, int64_t* __restrict__ nt,
                     BlockMeta* __restrict__ nm, const float* __restrict__ spos, const float* __restrict__ stime,
                     int t) __attribute__((always_inline)) {
       issue(t, nq, nd, nt, nm);
+      f32x16_t s_next = f32x16_t{};
+      if (t + 1 < nqb && block_active(t + 1)) {
+        // S of block t + 1: products issued before this block's arithmetic
+        bf16x8_t qfr[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) qfr[kb] = *reinterpret_cast<const bf16x8_t*>(rq1 + q_row[kb]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[kb], kf[kb], s_next, 0, 0, 0);
+      }
+      const f32x16_t s = s_cur;
+      s_cur = s_next;
       if (!block_active(t)) return;
       const int qa = (qb0 + t) * 32;
-      bf16x8_t qfr[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) qfr[kb] = *reinterpret_cast<const bf16x8_t*>(rq + q_row[kb]);
-      f32x16_t s = f32x16_t{};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[kb], kf[kb], s, 0, 0, 0);
       // s[4g+e]: query row qa + 8g + 4lh + e, key `key`
       int64_t tq_min = 0, tq_max = 0;
       if (has_time) {
@@ -459,7 +484,11 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
       float p[16], dsl[16];
       int tb[16];
       int info = c.path | (c.tlo << 8);
-      if (c.path != kBGeneral) {
+      if (c.path == kBUniform) {
+        // one bias for every pair; the gradient wave needs no buckets
+#pragma unroll
+        for (int r = 0; r < 16; ++r) silu_and_grad(fmaf(s[r], alpha_l, c.clo), p[r], dsl[r]);
+      } else if (c.path == kBTwoTime) {
         const int64_t lim = tk + ((int64_t(1) << (c.tlo + 1)) - 1);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -492,12 +521,14 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
       for (int q4 = 0; q4 < 4; ++q4) {
         xg[q4 * 64 + lane] = f32x4_t{dsl[4 * q4], dsl[4 * q4 + 1], dsl[4 * q4 + 2], dsl[4 * q4 + 3]};
       }
-      u32x4_t tw;
+      if (c.path != kBUniform) {
+        u32x4_t tw;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        tw[q4] = static_cast<uint32_t>(tb[4 * q4]) | (static_cast<uint32_t>(tb[4 * q4 + 1]) << 8) |
-                 (static_cast<uint32_t>(tb[4 * q4 + 2]) << 16) | (static_cast<uint32_t>(tb[4 * q4 + 3]) << 24);
-      xb[lane] = tw;
+        for (int q4 = 0; q4 < 4; ++q4)
+          tw[q4] = static_cast<uint32_t>(tb[4 * q4]) | (static_cast<uint32_t>(tb[4 * q4 + 1]) << 8) |
+                   (static_cast<uint32_t>(tb[4 * q4 + 2]) << 16) | (static_cast<uint32_t>(tb[4 * q4 + 3]) << 24);
+        xb[lane] = tw;
+      }
       if (lane == 0) *xinfo = info;
       // dV += P^T dO over the block's 32 query rows (two 16-row steps)
 #pragma unroll
@@ -515,10 +546,16 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
       }
     };
 
+    // the fragments and timestamps above have landed: without this wait the
+    // compiler, counting loads in issue order, would wait inside the loop
+    // for the tile loads issued after them
+    wait_vmcnt(0);
+    if (block_active(0)) s_cur = s_block(lds.q[0]);
     for (int t = 0; t < nqb; ++t) {
       const int sl = t % kKRing, nx = (t + 1) % kKRing;
-      step(lds.q[sl], lds.d[sl], lds.t[sl], &lds.m[sl], &lds.xg[t & 1][grp][0][0], &lds.xb[t & 1][grp][0],
-           &lds.xinfo[t & 1][grp], lds.q[nx], lds.d[nx], lds.t[nx], &lds.m[nx], lds.pos, lds.time, t);
+      step(lds.q[(t + 1) % kQRing], lds.d[sl], lds.t[sl], &lds.m[sl], &lds.xg[t & 1][grp][0][0],
+           &lds.xb[t & 1][grp][0], &lds.xinfo[t & 1][grp], lds.q[(t + 2) % kQRing], lds.d[nx], lds.t[nx],
+           &lds.m[nx], lds.pos, lds.time, t);
       wait_vmcnt(0);
       tile_barrier();
     }
@@ -566,7 +603,6 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
       for (int vb = 0; vb < VB; ++vb) da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr[vb], vf[vb], da, 0, 0, 0);
       const int info = __builtin_amdgcn_readfirstlane(*xinfo);
       const int path = info & 3, tlo = (info >> 8) & 255;
-      const u32x4_t tw = xb[lane];
       float ds[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -575,8 +611,23 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
         for (int e = 0; e < 4; ++e) ds[4 * q4 + e] = da[4 * q4 + e] * v[e];
       }
       if (g.grad_stride > 0) {
-        if (path != kBGeneral) {
+        if (path == kBUniform) {
+          // every pair reads position bucket Bp - 1 and time bucket tlo
+          float sl = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sl += ds[r];
+          if (has_pos) far_acc += sl;
+          if (has_time) {
+            if (tlo < kGFast) {
+              gtime[64 * tlo] += sl;
+            } else {
+              const float s0 = wave_sum(sl);
+              if (lane == 0) gslow[tlo] += s0;
+            }
+          }
+        } else if (path == kBTwoTime) {
           // every pair reads position bucket Bp - 1 and time bucket tlo or tlo + 1
+          const u32x4_t tw = xb[lane];
           float slo = 0.f, shi = 0.f;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -598,6 +649,7 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
             }
           }
         } else {
+          const u32x4_t tw = xb[lane];
           if (has_time) {
             if (info & kInfoFastTime) {
 #pragma unroll
@@ -648,23 +700,18 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
       }
     };
 
-    // step t: block t - 1 (its SiLU' was written before the last barrier),
-    // then the loads of block t + 1 (the compiler would otherwise wait for
-    // them before the block's LDS reads)
+    wait_vmcnt(0);   // V fragments
+    // step t: block t - 1 (its SiLU' was written before the last barrier)
     for (int t = 0; t < nqb; ++t) {
-      if (t >= 1 && block_active(t - 1)) {
-        const int pv = (t - 1) % kKRing;
-        grad_block(lds.d[pv], lds.q[pv], &lds.xg[(t - 1) & 1][grp][0][0], &lds.xb[(t - 1) & 1][grp][0],
-                   &lds.xinfo[(t - 1) & 1][grp], lds.gpos[grp], &lds.gtime[grp][0][lane], lds.gslow[grp], t - 1);
-      }
-      const int nx = (t + 1) % kKRing;
-      issue(t, lds.q[nx], lds.d[nx], lds.t[nx], &lds.m[nx]);
-      wait_vmcnt(0);
+      if (t >= 1 && block_active(t - 1))
+        grad_block(lds.d[(t - 1) % kKRing], lds.q[(t - 1) % kQRing], &lds.xg[(t - 1) & 1][grp][0][0],
+                   &lds.xb[(t - 1) & 1][grp][0], &lds.xinfo[(t - 1) & 1][grp], lds.gpos[grp],
+                   &lds.gtime[grp][0][lane], lds.gslow[grp], t - 1);
       tile_barrier();
     }
     if (block_active(nqb - 1)) {
-      const int pv = (nqb - 1) % kKRing;
-      grad_block(lds.d[pv], lds.q[pv], &lds.xg[(nqb - 1) & 1][grp][0][0], &lds.xb[(nqb - 1) & 1][grp][0],
+      grad_block(lds.d[(nqb - 1) % kKRing], lds.q[(nqb - 1) % kQRing], &lds.xg[(nqb - 1) & 1][grp][0][0],
+                 &lds.xb[(nqb - 1) & 1][grp][0],
                  &lds.xinfo[(nqb - 1) & 1][grp], lds.gpos[grp], &lds.gtime[grp][0][lane], lds.gslow[grp], nqb - 1);
     }
 
