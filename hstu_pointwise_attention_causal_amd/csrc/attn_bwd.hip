@@ -40,6 +40,8 @@
 // Scores are kept in x' = log2(e) x units as in the forward (one exp2 and one
 // reciprocal per pair); P is stored to bf16 as log2(e) SiLU(x) and the output
 // scales remove the factor.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "common.h"
 #include "launch.h"
@@ -444,34 +446,32 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
     // wait for the loads in flight before reading LDS.
     // S of block t (computed one step earlier)
     f32x16_t s_cur = f32x16_t{};
-    auto s_block = [&](const char* rq) __attribute__((always_inline)) {
-      bf16x8_t qfr[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) qfr[kb] = *reinterpret_cast<const bf16x8_t*>(rq + q_row[kb]);
-      f32x16_t sb = f32x16_t{};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[kb], kf[kb], sb, 0, 0, 0);
-      return sb;
-    };
+    static_assert(KB <= 16, "at most one product per pair");
+
+    // One block per step. The products of S of block t + 1 are spread over
+    // the per-pair loop, one after each pair, so they run under the
+    // arithmetic (an unused S past the sequence or when block t + 1 is masked
+    // entirely); dV += P^T dO of block t follows the loop.
     auto step = [&](const char* __restrict__ rq1, const char* __restrict__ rd, const int64_t* __restrict__ rt,
                     const BlockMeta* __restrict__ rm, f32x4_t* __restrict__ xg, u32x4_t* __restrict__ xb,
                     int* __restrict__ xinfo, char* __restrict__ nq, char* __restrict__ nd, int64_t* __restrict__ nt,
                     BlockMeta* __restrict__ nm, const float* __restrict__ spos, const float* __restrict__ stime,
                     int t) __attribute__((always_inline)) {
       issue(t, nq, nd, nt, nm);
-      f32x16_t s_next = f32x16_t{};
-      if (t + 1 < nqb && block_active(t + 1)) {
-        // S of block t + 1: products issued before this block's arithmetic
-        bf16x8_t qfr[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) qfr[kb] = *reinterpret_cast<const bf16x8_t*>(rq1 + q_row[kb]);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[kb], kf[kb], s_next, 0, 0, 0);
-      }
       const f32x16_t s = s_cur;
-      s_cur = s_next;
-      if (!block_active(t)) return;
+      f32x16_t sn = f32x16_t{};
+      auto mf = [&](int k) __attribute__((always_inline)) {
+        if (k < KB) {
+          const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(rq1 + q_row[k]);
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[k], sn, 0, 0, 0);
+        }
+      };
+      if (!block_active(t)) {
+#pragma unroll
+        for (int k = 0; k < KB; ++k) mf(k);
+        s_cur = sn;
+        return;
+      }
       const int qa = (qb0 + t) * 32;
       // s[4g+e]: query row qa + 8g + 4lh + e, key `key`
       int64_t tq_min = 0, tq_max = 0;
@@ -481,85 +481,111 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
       }
       const BlockClass c =
           classify_block(qa, kw, n, has_pos, Bp, has_time, Bt, tq_min, tq_max, tk_min, tk_max, pos_last, stime);
-      float p[16], dsl[16];
-      int tb[16];
       int info = c.path | (c.tlo << 8);
+      // per pair r: SiLU' to LDS four at a time, P packed to bf16, the time
+      // bucket into byte r % 4 of word r / 4
+      bf16x8_t pa_cur[2];
+      u32x4_t tw = u32x4_t{0u, 0u, 0u, 0u};
+      float dq[4];
+      auto emit = [&](int r, float pl, float dl) __attribute__((always_inline)) {
+        pa_cur[r >> 3][r & 7] = static_cast<__bf16>(pl);
+        dq[r & 3] = dl;
+        if ((r & 3) == 3) xg[(r >> 2) * 64 + lane] = f32x4_t{dq[0], dq[1], dq[2], dq[3]};
+      };
+      auto emit_tb = [&](int r, int tbr) __attribute__((always_inline)) {
+        tw[r >> 2] |= static_cast<uint32_t>(tbr) << (8 * (r & 3));
+      };
+      // the pairs of a block off the diagonal's mask: a position bucket per
+      // pair, the time bucket from the low words when the block's gaps fit
+      // in int32 (zero tables stand in for missing ones)
+      auto general = [&](auto masked_c, auto narrow_c) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_c)::value, NARROW = decltype(narrow_c)::value;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int il = 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int i = qa + il, d = i - key;
+          int tbr;
+          if constexpr (NARROW) tbr = time_bucket_narrow(rt[il], tk, time_nb);
+          else tbr = time_bucket64(rt[il] - tk, time_nb);
+          const int pb = MASKED ? min(max(d, 0), pos_hi) : min(d, pos_hi);
+          float pl, dl;
+          silu_and_grad(fmaf(s[r], alpha_l, spos[pb] + stime[tbr]), pl, dl);
+          if constexpr (MASKED) {
+            const bool valid = d >= 0 && i < n && key < n;
+            emit(r, valid ? pl : 0.f, valid ? dl : 0.f);
+            // a masked pair adds 0 to bucket 0: a key past the sequence end
+            // reads timestamp 0, and its bucket is not bounded by the block's
+            emit_tb(r, valid ? tbr : 0);
+          } else {
+            emit(r, pl, dl);
+            emit_tb(r, tbr);
+          }
+          mf(r);
+        }
+      };
       if (c.path == kBUniform) {
         // one bias for every pair; the gradient wave needs no buckets
 #pragma unroll
-        for (int r = 0; r < 16; ++r) silu_and_grad(fmaf(s[r], alpha_l, c.clo), p[r], dsl[r]);
+        for (int r = 0; r < 16; ++r) {
+          float pl, dl;
+          silu_and_grad(fmaf(s[r], alpha_l, c.clo), pl, dl);
+          emit(r, pl, dl);
+          mf(r);
+        }
       } else if (c.path == kBTwoTime) {
         const int64_t lim = tk + ((int64_t(1) << (c.tlo + 1)) - 1);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int il = 8 * (r >> 2) + 4 * lh + (r & 3);
-          const bool hi = c.path == kBTwoTime && rt[il] >= lim;
-          silu_and_grad(fmaf(s[r], alpha_l, hi ? c.chi : c.clo), p[r], dsl[r]);
-          tb[r] = c.tlo + (hi ? 1 : 0);
+          const bool hi = rt[il] >= lim;
+          float pl, dl;
+          silu_and_grad(fmaf(s[r], alpha_l, hi ? c.chi : c.clo), pl, dl);
+          emit(r, pl, dl);
+          emit_tb(r, c.tlo + (hi ? 1 : 0));
+          mf(r);
         }
       } else {
-        // straight-line per pair: both table lookups (zero tables stand in
-        // for missing ones), the causal / sequence-end mask as selects
         if (!has_time || time_bucket64(tq_max - tk_min, Bt) < kGFast) info |= kInfoFastTime;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int il = 8 * (r >> 2) + 4 * lh + (r & 3);
-          const int i = qa + il;
-          const bool valid = i >= key && i < n && key < n;
-          const int pb = min(max(i - key, 0), pos_hi);
-          const int tbr = time_bucket64(rt[il] - tk, time_nb);
-          float pl, dl;
-          silu_and_grad(fmaf(s[r], alpha_l, spos[pb] + stime[tbr]), pl, dl);
-          p[r] = valid ? pl : 0.f;
-          dsl[r] = valid ? dl : 0.f;
-          // a masked pair adds 0 to bucket 0: a key past the sequence end
-          // reads timestamp 0, and its bucket is not bounded by the block's
-          tb[r] = valid ? tbr : 0;
-        }
+        const bool masked = kw + 31 > qa || qa + 31 >= n || kw + 31 >= n;
+        const bool narrow =
+            !has_time || (tq_max - tk_min <= int64_t(INT32_MAX) - 1 && tq_min - tk_max >= int64_t(INT32_MIN));
+        if (!masked && narrow) general(std::false_type{}, std::true_type{});
+        else if (narrow) general(std::true_type{}, std::true_type{});
+        else general(std::true_type{}, std::false_type{});
       }
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        xg[q4 * 64 + lane] = f32x4_t{dsl[4 * q4], dsl[4 * q4 + 1], dsl[4 * q4 + 2], dsl[4 * q4 + 3]};
-      }
-      if (c.path != kBUniform) {
-        u32x4_t tw;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          tw[q4] = static_cast<uint32_t>(tb[4 * q4]) | (static_cast<uint32_t>(tb[4 * q4 + 1]) << 8) |
-                   (static_cast<uint32_t>(tb[4 * q4 + 2]) << 16) | (static_cast<uint32_t>(tb[4 * q4 + 3]) << 24);
-        xb[lane] = tw;
-      }
+      if (c.path != kBUniform) xb[lane] = tw;
       if (lane == 0) *xinfo = info;
       // dV += P^T dO over the block's 32 query rows (two 16-row steps)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bf16x8_t pa;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pa[i] = static_cast<__bf16>(p[kk * 8 + i]);
         const char* dst = rd + kk * 16 * DCH * 16;
 #pragma unroll
         for (int nb = 0; nb < NV; ++nb) {
           const bf16x8_t ob =
               __builtin_shufflevector(tr_read(dst + d_tr0[nb]), tr_read(dst + d_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
-          dva[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, ob, dva[nb], 0, 0, 0);
+          dva[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_cur[kk], ob, dva[nb], 0, 0, 0);
         }
       }
+      s_cur = sn;
     };
 
     // the fragments and timestamps above have landed: without this wait the
     // compiler, counting loads in issue order, would wait inside the loop
     // for the tile loads issued after them
     wait_vmcnt(0);
-    if (block_active(0)) s_cur = s_block(lds.q[0]);
+    if (block_active(0)) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(lds.q[0] + q_row[kb]),
+                                                        kf[kb], s_cur, 0, 0, 0);
+    }
     for (int t = 0; t < nqb; ++t) {
       const int sl = t % kKRing, nx = (t + 1) % kKRing;
-      step(lds.q[(t + 1) % kQRing], lds.d[sl], lds.t[sl], &lds.m[sl], &lds.xg[t & 1][grp][0][0],
-           &lds.xb[t & 1][grp][0], &lds.xinfo[t & 1][grp], lds.q[(t + 2) % kQRing], lds.d[nx], lds.t[nx],
-           &lds.m[nx], lds.pos, lds.time, t);
+      step(lds.q[(t + 1) % kQRing], lds.d[sl], lds.t[sl], &lds.m[sl], &lds.xg[t & 1][grp][0][0], &lds.xb[t & 1][grp][0],
+           &lds.xinfo[t & 1][grp], lds.q[(t + 2) % kQRing], lds.d[nx], lds.t[nx], &lds.m[nx], lds.pos, lds.time, t);
       wait_vmcnt(0);
       tile_barrier();
     }
-
     // ---- dV: accumulator [i][r] holds key kw + 8(r/4) + 4 lh + r%4, column 32 i + lr
     const float sv = inv_n / kLog2e;
     __bf16* dvp = static_cast<__bf16*>(g.dv) + (seq0 + kw) * g.lddv + h * DV + lr;
