@@ -250,37 +250,50 @@ __device__ __forceinline__ float wave_sum(float v) {
 // diagonal to the end of the sequence. Waves w and w + 4 of the workgroup run
 // on one SIMD and share a group of 32 keys (kw = k0 + 32 (w & 3), one key per
 // lane as the column of S), in two roles:
-//   score wave (w < 4)      S = Q K^T one block ahead (its products run under
-//                           the current block's arithmetic), the bias,
-//                           P = SiLU(x) and SiLU'(x) of every pair (masked
-//                           pairs: 0), dV += P^T dO, and the tile loads;
-//   gradient wave (w >= 4)  one block behind: dA = dO V^T, dS = dA SiLU'(x),
-//                           the bias-table gradients, dK += dS^T Q.
-// SiLU'(x) (fp32) and each pair's time bucket reach the gradient wave through
-// LDS. Each role's registers fit two waves per SIMD; the per-pair arithmetic
-// of the score wave overlaps the gradient wave's products and its
-// read-modify-write chains on the gradient tables. K (score) and V (gradient)
-// of the lane's key stay in registers as MFMA B operands; Q blocks stream
-// through four LDS slots (block t + 2 loads while t - 1 .. t + 1 are read),
-// dO blocks, timestamps and metadata through three (block t + 1 loads), with
-// one barrier per block.
+//   score wave (w < 4)      S = Q K^T one block ahead (its products spread
+//                           over the current block's per-pair loop), the
+//                           bias, P = SiLU(x) and SiLU'(x) of every pair
+//                           (masked pairs: 0), dV += P^T dO;
+//   gradient wave (w >= 4)  the tile loads, the block classes (64 blocks at a
+//                           time, one per lane), and one block behind the
+//                           score wave: dA = dO V^T, dS = dA SiLU'(x), the
+//                           bias-table gradients and dK += dS^T Q.
+// SiLU'(x) (fp16), each pair's time bucket and the block classes pass
+// through LDS. Each role's registers fit two waves per SIMD, and the work
+// that does not depend on the per-pair arithmetic runs on the gradient wave.
+// K (score) and V (gradient) of the lane's key stay in registers as MFMA B
+// operands; Q, dO, the timestamps and the metadata of block t + 2 load into
+// a ring of four LDS slots while block t is processed, one barrier per block.
 // ============================================================================
 constexpr int kKW = 8;                // waves of a key-pass workgroup
 constexpr int kKThreads = kKW * 64;
-constexpr int kKRing = 3;             // 32-row dO slots (and timestamps, metadata)
-constexpr int kQRing = 4;             // 32-row Q slots
-constexpr int kKIssue = 4;            // waves that issue the tile loads (the score waves)
+constexpr int kKRing = 4;             // 32-row block slots (Q, dO, timestamps, metadata)
+constexpr int kKIssue = 4;            // waves that issue the tile loads (the gradient waves)
 constexpr int kGFast = 32;            // time buckets summed in lane-private columns
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// Class of a (query block, key group) pair, written by the gradient waves
+// for 64 blocks at a time: the path (bits 0-1), the low time bucket of a one-
+// or two-bucket block (bits 8-15), and flags.
+constexpr int kInfoFastTime = 1 << 16;   // every time bucket of the block is below kGFast
+constexpr int kInfoMasked = 1 << 17;     // causal or sequence-end mask inside the block
+constexpr int kInfoNarrow = 1 << 18;     // every gap of the block fits in int32
+struct KvClass {
+  int info;
+  float clo, chi;   // x'-unit bias of the pairs in bucket tlo / tlo + 1
+  int pad;
+};
 
 template <int DQK, int DV>
 struct KvLds {
-  __attribute__((aligned(16))) char q[kQRing][32 * DQK * 2];
+  __attribute__((aligned(16))) char q[kKRing][32 * DQK * 2];
   __attribute__((aligned(16))) char d[kKRing][32 * DV * 2];
   __attribute__((aligned(16))) int64_t t[kKRing][32];
   __attribute__((aligned(16))) BlockMeta m[kKRing];
-  f32x4_t xg[2][4][4][64];      // SiLU'(x) of a block: [buffer][key group][r / 4][lane]
+  f16x8_t xg[2][4][2][64];      // SiLU' of a block: [buffer][key group][r / 8][lane]
   u32x4_t xb[2][4][64];         // time bucket of pair r in byte r % 4 of word r / 4: [buffer][key group][lane]
-  int xinfo[2][4];              // block class of a block: [buffer][key group]
+  KvClass cls[2][4][64];        // [(block / 64) % 2][key group][block % 64]
   // Bias-table gradients, one table per gradient wave. Position buckets:
   // plain adds of diagonal sums. Time buckets below kGFast: one column per
   // lane ([wave][bucket][lane]), as most pairs of a block near the diagonal
@@ -294,52 +307,47 @@ struct KvLds {
 
 // Direct loads of one 32-row block of a row-major matrix with CH 16-byte
 // chunks per row, stored with the dual-read swizzle: instruction i fills LDS
-// slots [64 i, 64 i + 64) and is issued by wave i % kKIssue. Rows past the
-// sequence arrive as zeros.
+// slots [64 i, 64 i + 64) and is issued by gradient wave i % kKIssue. Rows
+// past the sequence arrive as zeros.
 template <int CH>
-__device__ __forceinline__ void block_load_offsets(int w, int lane, int64_t ld, uint32_t* off) {
+__device__ __forceinline__ void block_load_offsets(int wi, int lane, int64_t ld, uint32_t* off) {
   constexpr int NI = CH / 2;
 #pragma unroll
   for (int j = 0; j < (NI + kKIssue - 1) / kKIssue; ++j) {
-    const int s = (w + j * kKIssue) * 64 + lane;
+    const int s = (wi + j * kKIssue) * 64 + lane;
     const int r = s / CH, c = (s % CH) ^ swz_dual<CH>(r);
     off[j] = static_cast<uint32_t>(r * ld * 2 + c * 16);
   }
 }
 
 template <int CH>
-__device__ __forceinline__ void issue_block(const char* base, int64_t ld, int n, int r0, int w, const uint32_t* off,
+__device__ __forceinline__ void issue_block(const char* base, int64_t ld, int n, int r0, int wi, const uint32_t* off,
                                             char* dst) {
   constexpr int NI = CH / 2;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + static_cast<int64_t>(r0) * ld * 2,
                                               static_cast<int64_t>(n - r0) * ld * 2);
 #pragma unroll
   for (int j = 0; j < (NI + kKIssue - 1) / kKIssue; ++j) {
-    const int i = w + j * kKIssue;
+    const int i = wi + j * kKIssue;
     if (i < NI) load_lds16(rs, dst + i * 1024, off[j]);
   }
 }
 
-// The 32 timestamps (wave kKIssue - 2; zeros without timestamps) and the
-// metadata record (wave kKIssue - 1) of the query block at row r0.
+// The 32 timestamps (gradient wave 2; zeros without timestamps) and the
+// metadata record (gradient wave 3) of the query block at row r0.
 __device__ __forceinline__ void issue_block_extras(const int64_t* tsbase, const BlockMeta* mbase, int n, int r0,
-                                                   int w, int lane, int64_t* st, BlockMeta* sm) {
-  if (w == kKIssue - 2 && lane < 16) {
+                                                   int wi, int lane, int64_t* st, BlockMeta* sm) {
+  if (wi == kKIssue - 2 && lane < 16) {
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(tsbase ? tsbase + r0 : nullptr,
                                                 tsbase ? static_cast<int64_t>(n - r0) * 8 : 0);
     load_lds16(rt, reinterpret_cast<char*>(st), lane * 16);
   }
-  if (w == kKIssue - 1 && lane < 2) {
+  if (wi == kKIssue - 1 && lane < 2) {
     const int blk = r0 / 32, nblk = (n + 31) / 32;
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(mbase + blk, static_cast<int64_t>(nblk - blk) * 32);
     load_lds16(rm, reinterpret_cast<char*>(sm), lane * 16);
   }
 }
-
-// xinfo word: bits 0-1 the path, bits 8-15 the low time bucket of a uniform
-// or two-bucket block, bit 16 set when every time bucket of the block is
-// below kGFast.
-constexpr int kInfoFastTime = 1 << 16;
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g) {
@@ -349,6 +357,7 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
   constexpr int NQ = DQK / 32, NV = DV / 32;       // 32-column groups of dK and dV
   constexpr int QCH = DQK / 8, DCH = DV / 8;       // 16-byte chunks per Q / dO row
   constexpr int QI = (QCH / 2 + kKIssue - 1) / kKIssue, DI = (DCH / 2 + kKIssue - 1) / kKIssue;
+  static_assert(KB <= 16, "at most one product per pair");
 
   const int item_idx = blockIdx.x;
   if (item_idx >= *a.item_count) return;
@@ -377,61 +386,127 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
   const BlockMeta* meta_row =
       static_cast<const BlockMeta*>(a.meta) + h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * a.tile_base[b];
 
-  for (int i = tid; i <= pos_hi; i += kKThreads) lds.pos[i] = has_pos ? kLog2e * a.pos_table[h * Bp + i] : 0.f;
-  for (int i = tid; i < time_nb; i += kKThreads) lds.time[i] = has_time ? kLog2e * a.time_table[h * Bt + i] : 0.f;
-  for (int i = tid; i < 4 * kBwdPosMax; i += kKThreads) (&lds.gpos[0][0])[i] = 0.f;
-  for (int i = tid; i < 4 * kGFast * 64; i += kKThreads) (&lds.gtime[0][0][0])[i] = 0.f;
-  for (int i = tid; i < 4 * kBwdTimeSlots; i += kKThreads) (&lds.gslow[0][0])[i] = 0.f;
-
-  uint32_t qoff[QI], doff[DI];
-  block_load_offsets<QCH>(w, lane, a.ldq, qoff);
-  block_load_offsets<DCH>(w, lane, g.lddo, doff);
-  const char* qbase = static_cast<const char*>(a.q) + (seq0 * a.ldq + h * DQK) * 2;
-  const char* dbase = static_cast<const char*>(g.d_o) + (seq0 * g.lddo + h * DV) * 2;
-  const int64_t* tsbase = has_time ? a.ts + seq0 : nullptr;
-
+  // ---- prologue: every global load is issued before the first wait (a
+  // work item's set-up is exposed: one workgroup fills a compute unit)
   const int qb0 = k0 / 32;                   // first query block: key group 0's diagonal
   const int nqb = (n + 31) / 32 - qb0;       // >= 1
   // a block's pairs are all masked when its last row precedes the group's first key
   auto block_active = [&](int t) __attribute__((always_inline)) { return kw < n && (qb0 + t) * 32 + 31 >= kw; };
-  // (score waves) Q of block t + 2 and dO, timestamps, metadata of block
-  // t + 1; their slots were released by the barrier that ended block t - 1
-  auto issue = [&](int t, char* nq, char* nd, int64_t* nt, BlockMeta* nm) __attribute__((always_inline)) {
-    if (t + 2 < nqb) issue_block<QCH>(qbase, a.ldq, n, (qb0 + t + 2) * 32, w, qoff, nq);
-    if (t + 1 < nqb) {
-      const int r0 = (qb0 + t + 1) * 32;
-      issue_block<DCH>(dbase, g.lddo, n, r0, w, doff, nd);
-      issue_block_extras(tsbase, meta_row, n, r0, w, lane, nt, nm);
+
+  // K (score waves) or V (gradient waves) rows of this lane's key: the MFMA
+  // B operands of S = Q K^T and dA = dO V^T
+  static_assert(KB == VB, "one fragment count for both roles");
+  bf16x8_t frag[KB];
+  {
+    const __bf16* src = w < 4 ? static_cast<const __bf16*>(a.k) + (seq0 + key) * a.ldk + h * DQK
+                              : static_cast<const __bf16*>(a.v) + (seq0 + key) * a.ldv + h * DV;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      frag[kb] = key < n ? *reinterpret_cast<const bf16x8_t*>(src + kb * 16 + lh * 8) : bf16x8_t{};
+  }
+  const int64_t tk = (has_time && key < n) ? a.ts[seq0 + key] : 0;
+  int64_t tk_min = 0, tk_max = 0;
+  if (has_time && kw < n) {
+    tk_min = uniform_i64(meta_row[kw / 32].tmin);
+    tk_max = uniform_i64(meta_row[kw / 32].tmax);
+  }
+  const float pos_last = has_pos ? kLog2e * a.pos_table[h * Bp + Bp - 1] : 0.f;
+  // the bias tables (up to kBwdPosMax = 2 kKThreads and kBwdTimeSlots entries)
+  static_assert(kBwdPosMax <= 2 * kKThreads && kBwdTimeSlots <= kKThreads, "two table loads per thread");
+  // (buffer loads, zero past the table: no branch, so the wait for them is
+  // not placed right after each load)
+  const __amdgpu_buffer_rsrc_t rpos = make_rsrc(has_pos ? a.pos_table + h * Bp : nullptr, has_pos ? Bp * 4 : 0);
+  const __amdgpu_buffer_rsrc_t rtim = make_rsrc(has_time ? a.time_table + h * Bt : nullptr, has_time ? time_nb * 4 : 0);
+  const float pos0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpos, tid * 4, 0, 0));
+  const float pos1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpos, (tid + kKThreads) * 4, 0, 0));
+  const float time0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rtim, tid * 4, 0, 0));
+  // (gradient waves) the metadata of query block qb0 + lane, for the first classes
+  int64_t cq_min = 0, cq_max = 0;
+  if (w >= kKIssue && has_time && lane < nqb) {
+    cq_min = meta_row[qb0 + lane].tmin;
+    cq_max = meta_row[qb0 + lane].tmax;
+  }
+
+  // (gradient waves) the loads of the blocks in order, block t into ring
+  // slot t % kKRing; the buffer descriptors advance by one block per call
+  const int wi = w - kKIssue;
+  uint32_t qoff[QI], doff[DI];
+  const int64_t qstep = int64_t(32) * a.ldq * 2, dstep = int64_t(32) * g.lddo * 2;
+  const char* qnext = static_cast<const char*>(a.q) + ((seq0 + qb0 * 32) * a.ldq + h * DQK) * 2;
+  const char* dnext = static_cast<const char*>(g.d_o) + ((seq0 + qb0 * 32) * g.lddo + h * DV) * 2;
+  const int64_t* tnext = has_time ? a.ts + seq0 + qb0 * 32 : nullptr;
+  const BlockMeta* mnext = meta_row + qb0;
+  int64_t qleft = int64_t(n - qb0 * 32) * a.ldq * 2, dleft = int64_t(n - qb0 * 32) * g.lddo * 2;
+  int64_t rows_left = n - qb0 * 32, blocks_left = (n + 31) / 32 - qb0;
+  int issued = 0;
+  auto issue_next = [&](char* nq, char* nd, int64_t* nt, BlockMeta* nm) __attribute__((always_inline)) {
+    if (issued < nqb) {
+      constexpr int NQI = QCH / 2, NDI = DCH / 2;
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(qnext, qleft), rd = make_rsrc(dnext, dleft);
+#pragma unroll
+      for (int j = 0; j < QI; ++j)
+        if (wi + j * kKIssue < NQI) load_lds16(rq, nq + (wi + j * kKIssue) * 1024, qoff[j]);
+#pragma unroll
+      for (int j = 0; j < DI; ++j)
+        if (wi + j * kKIssue < NDI) load_lds16(rd, nd + (wi + j * kKIssue) * 1024, doff[j]);
+      if (wi == kKIssue - 2 && lane < 16)
+        load_lds16(make_rsrc(tnext, tnext ? rows_left * 8 : 0), reinterpret_cast<char*>(nt), lane * 16);
+      if (wi == kKIssue - 1 && lane < 2)
+        load_lds16(make_rsrc(mnext, blocks_left * 32), reinterpret_cast<char*>(nm), lane * 16);
+      qnext += qstep;
+      dnext += dstep;
+      qleft -= qstep;
+      dleft -= dstep;
+      if (tnext) tnext += 32;
+      rows_left -= 32;
+      ++mnext;
+      --blocks_left;
+      ++issued;
     }
   };
+  // (gradient waves) classes of blocks [c0, c0 + 64) for this key group, one
+  // block per lane (tq_min, tq_max: its query block's timestamp range), into
+  // out[block - c0]
+  auto classify_chunk = [&](int c0, int64_t tq_min, int64_t tq_max, const float* stime, KvClass* out)
+                            __attribute__((always_inline)) {
+    const int t = c0 + lane;
+    if (t >= nqb) return;
+    const int qa = (qb0 + t) * 32;
+    const BlockClass c =
+        classify_block(qa, kw, n, has_pos, Bp, has_time, Bt, tq_min, tq_max, tk_min, tk_max, pos_last, stime);
+    int info = c.path | (c.tlo << 8);
+    if (c.path == kBGeneral) {
+      if (!has_time || time_bucket64(tq_max - tk_min, Bt) < kGFast) info |= kInfoFastTime;
+      if (kw + 31 > qa || qa + 31 >= n || kw + 31 >= n) info |= kInfoMasked;
+      if (!has_time || (tq_max - tk_min <= int64_t(INT32_MAX) - 1 && tq_min - tk_max >= int64_t(INT32_MIN)))
+        info |= kInfoNarrow;
+    }
+    out[lane] = KvClass{info, c.clo, c.chi, 0};
+  };
 
-  if (w < kKIssue) {
-    issue_block<QCH>(qbase, a.ldq, n, qb0 * 32, w, qoff, lds.q[0]);
-    if (nqb > 1) issue_block<QCH>(qbase, a.ldq, n, (qb0 + 1) * 32, w, qoff, lds.q[1]);
-    issue_block<DCH>(dbase, g.lddo, n, qb0 * 32, w, doff, lds.d[0]);
-    issue_block_extras(tsbase, meta_row, n, qb0 * 32, w, lane, lds.t[0], &lds.m[0]);
+  if (w >= kKIssue) {
+    block_load_offsets<QCH>(wi, lane, a.ldq, qoff);
+    block_load_offsets<DCH>(wi, lane, g.lddo, doff);
+    issue_next(lds.q[0], lds.d[0], lds.t[0], &lds.m[0]);
+    issue_next(lds.q[1], lds.d[1], lds.t[1], &lds.m[1]);
   }
+  for (int i = tid; i < 4 * kBwdPosMax; i += kKThreads) (&lds.gpos[0][0])[i] = 0.f;
+  for (int i = tid; i < 4 * kGFast * 64; i += kKThreads) (&lds.gtime[0][0][0])[i] = 0.f;
+  for (int i = tid; i < 4 * kBwdTimeSlots; i += kKThreads) (&lds.gslow[0][0])[i] = 0.f;
   wait_vmcnt(0);
-  __syncthreads();   // also publishes the staged tables and the zeroed gradient tables
+  if (tid <= pos_hi) lds.pos[tid] = kLog2e * pos0;   // one 0 without the table
+  if (tid + kKThreads <= pos_hi) lds.pos[tid + kKThreads] = kLog2e * pos1;
+  if (tid < time_nb) lds.time[tid] = kLog2e * time0;
+  __syncthreads();   // the staged tables (read by the classification)
+  if (w >= kKIssue) classify_chunk(0, cq_min, cq_max, lds.time, &lds.cls[0][grp][0]);
+  __syncthreads();   // also publishes the first classes and the zeroed gradient tables
 
   const float inv_n = a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n);
 
   if (w < 4) {
     // ======================= score wave =======================
-    const __bf16* kp = static_cast<const __bf16*>(a.k);
-    bf16x8_t kf[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      kf[kb] = key < n ? *reinterpret_cast<const bf16x8_t*>(kp + (seq0 + key) * a.ldk + h * DQK + kb * 16 + lh * 8)
-                       : bf16x8_t{};
-    const int64_t tk = (has_time && key < n) ? a.ts[seq0 + key] : 0;
-    int64_t tk_min = 0, tk_max = 0;
-    if (has_time && kw < n) {
-      tk_min = uniform_i64(meta_row[kw / 32].tmin);
-      tk_max = uniform_i64(meta_row[kw / 32].tmax);
-    }
+    const bf16x8_t* kf = frag;
     const float alpha_l = a.alpha * kLog2e;
-    const float pos_last = has_pos ? kLog2e * a.pos_table[h * Bp + Bp - 1] : 0.f;
     uint32_t q_row[KB], d_tr0[NV], d_tr1[NV];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) q_row[kb] = row_read_offset<QCH>(lr, lh, kb);
@@ -440,24 +515,19 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
     f32x16_t dva[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) dva[i] = f32x16_t{};
-
-    // Every LDS buffer comes in through a __restrict__ parameter: the step
-    // reads block t's slots and fills block t + 1's, so the compiler does not
-    // wait for the loads in flight before reading LDS.
     // S of block t (computed one step earlier)
     f32x16_t s_cur = f32x16_t{};
-    static_assert(KB <= 16, "at most one product per pair");
 
     // One block per step. The products of S of block t + 1 are spread over
     // the per-pair loop, one after each pair, so they run under the
     // arithmetic (an unused S past the sequence or when block t + 1 is masked
-    // entirely); dV += P^T dO of block t follows the loop.
+    // entirely); dV += P^T dO of block t follows the loop. Every LDS buffer
+    // comes in through a __restrict__ parameter, so the compiler does not
+    // wait for the loads in flight before reading LDS.
     auto step = [&](const char* __restrict__ rq1, const char* __restrict__ rd, const int64_t* __restrict__ rt,
-                    const BlockMeta* __restrict__ rm, f32x4_t* __restrict__ xg, u32x4_t* __restrict__ xb,
-                    int* __restrict__ xinfo, char* __restrict__ nq, char* __restrict__ nd, int64_t* __restrict__ nt,
-                    BlockMeta* __restrict__ nm, const float* __restrict__ spos, const float* __restrict__ stime,
-                    int t) __attribute__((always_inline)) {
-      issue(t, nq, nd, nt, nm);
+                    const KvClass* __restrict__ rc, f16x8_t* __restrict__ xg, u32x4_t* __restrict__ xb,
+                    const float* __restrict__ spos, const float* __restrict__ stime, int t)
+                    __attribute__((always_inline)) {
       const f32x16_t s = s_cur;
       f32x16_t sn = f32x16_t{};
       auto mf = [&](int k) __attribute__((always_inline)) {
@@ -474,30 +544,26 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
       }
       const int qa = (qb0 + t) * 32;
       // s[4g+e]: query row qa + 8g + 4lh + e, key `key`
-      int64_t tq_min = 0, tq_max = 0;
-      if (has_time) {
-        tq_min = uniform_i64(rm->tmin);
-        tq_max = uniform_i64(rm->tmax);
-      }
-      const BlockClass c =
-          classify_block(qa, kw, n, has_pos, Bp, has_time, Bt, tq_min, tq_max, tk_min, tk_max, pos_last, stime);
-      int info = c.path | (c.tlo << 8);
-      // per pair r: SiLU' to LDS four at a time, P packed to bf16, the time
-      // bucket into byte r % 4 of word r / 4
-      bf16x8_t pa_cur[2];
+      const int info = __builtin_amdgcn_readfirstlane(rc->info);
+      const int path = info & 3, tlo = (info >> 8) & 255;
+      const float clo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(rc->clo)));
+      const float chi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(rc->chi)));
+      // per pair r: SiLU' (fp16) and P (bf16) packed eight at a time, the
+      // time bucket into byte r % 4 of word r / 4
+      bf16x8_t pa[2];
+      f16x8_t gq;
       u32x4_t tw = u32x4_t{0u, 0u, 0u, 0u};
-      float dq[4];
       auto emit = [&](int r, float pl, float dl) __attribute__((always_inline)) {
-        pa_cur[r >> 3][r & 7] = static_cast<__bf16>(pl);
-        dq[r & 3] = dl;
-        if ((r & 3) == 3) xg[(r >> 2) * 64 + lane] = f32x4_t{dq[0], dq[1], dq[2], dq[3]};
+        pa[r >> 3][r & 7] = static_cast<__bf16>(pl);
+        gq[r & 7] = static_cast<_Float16>(dl);
+        if ((r & 7) == 7) xg[(r >> 3) * 64 + lane] = gq;
       };
       auto emit_tb = [&](int r, int tbr) __attribute__((always_inline)) {
         tw[r >> 2] |= static_cast<uint32_t>(tbr) << (8 * (r & 3));
       };
-      // the pairs of a block off the diagonal's mask: a position bucket per
-      // pair, the time bucket from the low words when the block's gaps fit
-      // in int32 (zero tables stand in for missing ones)
+      // the pairs of a block with varying position buckets or a mask: a
+      // bucket per pair, the time bucket from the timestamps' low words when
+      // the block's gaps fit in int32 (zero tables stand in for missing ones)
       auto general = [&](auto masked_c, auto narrow_c) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_c)::value, NARROW = decltype(narrow_c)::value;
 #pragma unroll
@@ -523,38 +589,35 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
           mf(r);
         }
       };
-      if (c.path == kBUniform) {
+      if (path == kBUniform) {
         // one bias for every pair; the gradient wave needs no buckets
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pl, dl;
-          silu_and_grad(fmaf(s[r], alpha_l, c.clo), pl, dl);
+          silu_and_grad(fmaf(s[r], alpha_l, clo), pl, dl);
           emit(r, pl, dl);
           mf(r);
         }
-      } else if (c.path == kBTwoTime) {
-        const int64_t lim = tk + ((int64_t(1) << (c.tlo + 1)) - 1);
+      } else if (path == kBTwoTime) {
+        const int64_t lim = tk + ((int64_t(1) << (tlo + 1)) - 1);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int il = 8 * (r >> 2) + 4 * lh + (r & 3);
           const bool hi = rt[il] >= lim;
           float pl, dl;
-          silu_and_grad(fmaf(s[r], alpha_l, hi ? c.chi : c.clo), pl, dl);
+          silu_and_grad(fmaf(s[r], alpha_l, hi ? chi : clo), pl, dl);
           emit(r, pl, dl);
-          emit_tb(r, c.tlo + (hi ? 1 : 0));
+          emit_tb(r, tlo + (hi ? 1 : 0));
           mf(r);
         }
+      } else if (!(info & kInfoMasked) && (info & kInfoNarrow)) {
+        general(std::false_type{}, std::true_type{});
+      } else if (info & kInfoNarrow) {
+        general(std::true_type{}, std::true_type{});
       } else {
-        if (!has_time || time_bucket64(tq_max - tk_min, Bt) < kGFast) info |= kInfoFastTime;
-        const bool masked = kw + 31 > qa || qa + 31 >= n || kw + 31 >= n;
-        const bool narrow =
-            !has_time || (tq_max - tk_min <= int64_t(INT32_MAX) - 1 && tq_min - tk_max >= int64_t(INT32_MIN));
-        if (!masked && narrow) general(std::false_type{}, std::true_type{});
-        else if (narrow) general(std::true_type{}, std::true_type{});
-        else general(std::true_type{}, std::false_type{});
+        general(std::true_type{}, std::false_type{});
       }
-      if (c.path != kBUniform) xb[lane] = tw;
-      if (lane == 0) *xinfo = info;
+      if (path != kBUniform) xb[lane] = tw;
       // dV += P^T dO over the block's 32 query rows (two 16-row steps)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -563,16 +626,12 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
         for (int nb = 0; nb < NV; ++nb) {
           const bf16x8_t ob =
               __builtin_shufflevector(tr_read(dst + d_tr0[nb]), tr_read(dst + d_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
-          dva[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_cur[kk], ob, dva[nb], 0, 0, 0);
+          dva[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], ob, dva[nb], 0, 0, 0);
         }
       }
       s_cur = sn;
     };
 
-    // the fragments and timestamps above have landed: without this wait the
-    // compiler, counting loads in issue order, would wait inside the loop
-    // for the tile loads issued after them
-    wait_vmcnt(0);
     if (block_active(0)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -580,12 +639,12 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
                                                         kf[kb], s_cur, 0, 0, 0);
     }
     for (int t = 0; t < nqb; ++t) {
-      const int sl = t % kKRing, nx = (t + 1) % kKRing;
-      step(lds.q[(t + 1) % kQRing], lds.d[sl], lds.t[sl], &lds.m[sl], &lds.xg[t & 1][grp][0][0], &lds.xb[t & 1][grp][0],
-           &lds.xinfo[t & 1][grp], lds.q[(t + 2) % kQRing], lds.d[nx], lds.t[nx], &lds.m[nx], lds.pos, lds.time, t);
-      wait_vmcnt(0);
+      const int sl = t % kKRing;
+      step(lds.q[(t + 1) % kKRing], lds.d[sl], lds.t[sl], &lds.cls[(t >> 6) & 1][grp][t & 63], &lds.xg[t & 1][grp][0][0],
+           &lds.xb[t & 1][grp][0], lds.pos, lds.time, t);
       tile_barrier();
     }
+
     // ---- dV: accumulator [i][r] holds key kw + 8(r/4) + 4 lh + r%4, column 32 i + lr
     const float sv = inv_n / kLog2e;
     __bf16* dvp = static_cast<__bf16*>(g.dv) + (seq0 + kw) * g.lddv + h * DV + lr;
@@ -599,12 +658,7 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
     }
   } else {
     // ====================== gradient wave ======================
-    const __bf16* vp = static_cast<const __bf16*>(a.v);
-    bf16x8_t vf[VB];
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
-      vf[vb] = key < n ? *reinterpret_cast<const bf16x8_t*>(vp + (seq0 + key) * a.ldv + h * DV + vb * 16 + lh * 8)
-                       : bf16x8_t{};
+    const bf16x8_t* vf = frag;
     uint32_t d_row[VB], q_tr0[NQ], q_tr1[NQ];
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb) d_row[vb] = row_read_offset<DCH>(lr, lh, vb);
@@ -614,27 +668,48 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
 #pragma unroll
     for (int i = 0; i < NQ; ++i) dka[i] = f32x16_t{};
     float far_acc = 0.f;   // dS' of the pairs that read position bucket Bp - 1
+    float* gpos = lds.gpos[grp];
+    float* gtime = &lds.gtime[grp][0][lane];
+    float* gslow = lds.gslow[grp];
 
-    // Block t: dA, dS, the gradient-table updates and dK. Its buffers come in
-    // through __restrict__ parameters (as in the score wave's step).
-    auto grad_block = [&](const char* __restrict__ rd, const char* __restrict__ rq, const f32x4_t* __restrict__ xg,
-                          const u32x4_t* __restrict__ xb, const int* __restrict__ xinfo, float* __restrict__ gpos,
-                          float* __restrict__ gtime, float* __restrict__ gslow, int t) __attribute__((always_inline)) {
-      const int qa = (qb0 + t) * 32;
+    // Step t: the loads of block t + 2, at t = 64 k + 1 the classes of blocks
+    // [64 (k + 1), 64 (k + 2)) (into the table half that held blocks
+    // [64 (k - 1), 64 k), whose last reader was step 64 k), then block t - 1
+    // (its SiLU' was written before
+    // the last barrier): dA, dS, the gradient-table updates and dK. Every LDS
+    // buffer comes in through a __restrict__ parameter (as in the score
+    // wave's step).
+    auto step = [&](const char* __restrict__ rd, const char* __restrict__ rq, const f16x8_t* __restrict__ xg,
+                    const u32x4_t* __restrict__ xb, const KvClass* __restrict__ rc, KvClass* __restrict__ wc,
+                    char* __restrict__ nq, char* __restrict__ nd, int64_t* __restrict__ nt,
+                    BlockMeta* __restrict__ nm, const float* __restrict__ stime, float* __restrict__ gp,
+                    float* __restrict__ gt, float* __restrict__ gsl, int t) __attribute__((always_inline)) {
+      issue_next(nq, nd, nt, nm);
+      if ((t & 63) == 1 && t + 63 < nqb) {
+        int64_t q_min = 0, q_max = 0;
+        if (has_time && t + 63 + lane < nqb) {
+          q_min = meta_row[qb0 + t + 63 + lane].tmin;
+          q_max = meta_row[qb0 + t + 63 + lane].tmax;
+        }
+        classify_chunk(t + 63, q_min, q_max, stime, wc);
+      }
+      const int tb_ = t - 1;
+      if (tb_ < 0 || !block_active(tb_)) return;
+      const int qa = (qb0 + tb_) * 32;
       bf16x8_t dfr[VB];
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) dfr[vb] = *reinterpret_cast<const bf16x8_t*>(rd + d_row[vb]);
       f32x16_t da = f32x16_t{};
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr[vb], vf[vb], da, 0, 0, 0);
-      const int info = __builtin_amdgcn_readfirstlane(*xinfo);
+      const int info = __builtin_amdgcn_readfirstlane(rc->info);
       const int path = info & 3, tlo = (info >> 8) & 255;
       float ds[16];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4_t v = xg[q4 * 64 + lane];
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const f16x8_t v = xg[h8 * 64 + lane];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ds[4 * q4 + e] = da[4 * q4 + e] * v[e];
+        for (int e = 0; e < 8; ++e) ds[8 * h8 + e] = da[8 * h8 + e] * static_cast<float>(v[e]);
       }
       if (g.grad_stride > 0) {
         if (path == kBUniform) {
@@ -645,10 +720,10 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
           if (has_pos) far_acc += sl;
           if (has_time) {
             if (tlo < kGFast) {
-              gtime[64 * tlo] += sl;
+              gt[64 * tlo] += sl;
             } else {
               const float s0 = wave_sum(sl);
-              if (lane == 0) gslow[tlo] += s0;
+              if (lane == 0) gsl[tlo] += s0;
             }
           }
         } else if (path == kBTwoTime) {
@@ -664,13 +739,13 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
           if (has_pos) far_acc += slo + shi;
           if (has_time) {
             if (tlo + 1 < kGFast) {
-              gtime[64 * tlo] += slo;
-              if (path == kBTwoTime) gtime[64 * (tlo + 1)] += shi;
+              gt[64 * tlo] += slo;
+              gt[64 * (tlo + 1)] += shi;
             } else {
               const float s0 = wave_sum(slo), s1 = wave_sum(shi);
               if (lane == 0) {
-                gslow[tlo] += s0;
-                if (path == kBTwoTime) gslow[tlo + 1] += s1;
+                gsl[tlo] += s0;
+                gsl[tlo + 1] += s1;
               }
             }
           }
@@ -679,13 +754,13 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
           if (has_time) {
             if (info & kInfoFastTime) {
 #pragma unroll
-              for (int r = 0; r < 16; ++r) gtime[64 * ((tw[r >> 2] >> (8 * (r & 3))) & 255)] += ds[r];
+              for (int r = 0; r < 16; ++r) gt[64 * ((tw[r >> 2] >> (8 * (r & 3))) & 255)] += ds[r];
             } else {
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int tbr = (tw[r >> 2] >> (8 * (r & 3))) & 255;
-                if (tbr < kGFast) gtime[64 * tbr] += ds[r];
-                else lds_add_f32(&gslow[tbr], ds[r]);
+                if (tbr < kGFast) gt[64 * tbr] += ds[r];
+                else lds_add_f32(&gsl[tbr], ds[r]);
               }
             }
           }
@@ -701,10 +776,10 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
               diagonal_sums(ds, lr, lh, dpos, dneg);
               if (lh == 0) {
                 const int bpos = qa - kw + lr, bneg = bpos - 32;
-                if (bpos < Bp - 1) gpos[bpos] += dpos;
+                if (bpos < Bp - 1) gp[bpos] += dpos;
                 else far_acc += dpos;
                 if (bneg >= Bp - 1) far_acc += dneg;
-                else if (bneg >= 0) gpos[bneg] += dneg;
+                else if (bneg >= 0) gp[bneg] += dneg;
               }
             }
           }
@@ -726,19 +801,15 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
       }
     };
 
-    wait_vmcnt(0);   // V fragments
-    // step t: block t - 1 (its SiLU' was written before the last barrier)
-    for (int t = 0; t < nqb; ++t) {
-      if (t >= 1 && block_active(t - 1))
-        grad_block(lds.d[(t - 1) % kKRing], lds.q[(t - 1) % kQRing], &lds.xg[(t - 1) & 1][grp][0][0],
-                   &lds.xb[(t - 1) & 1][grp][0], &lds.xinfo[(t - 1) & 1][grp], lds.gpos[grp],
-                   &lds.gtime[grp][0][lane], lds.gslow[grp], t - 1);
-      tile_barrier();
-    }
-    if (block_active(nqb - 1)) {
-      grad_block(lds.d[(nqb - 1) % kKRing], lds.q[(nqb - 1) % kQRing], &lds.xg[(nqb - 1) & 1][grp][0][0],
-                 &lds.xb[(nqb - 1) & 1][grp][0],
-                 &lds.xinfo[(nqb - 1) & 1][grp], lds.gpos[grp], &lds.gtime[grp][0][lane], lds.gslow[grp], nqb - 1);
+    for (int t = 0; t <= nqb; ++t) {
+      // slots: block t - 1 (dO, Q), t + 2 (loads)
+      const int pv = (t + kKRing - 1) % kKRing, n2 = (t + 2) % kKRing;
+      const int tp = t > 0 ? t - 1 : 0;
+      step(lds.d[pv], lds.q[pv], &lds.xg[(t + 1) & 1][grp][0][0], &lds.xb[(t + 1) & 1][grp][0],
+           &lds.cls[(tp >> 6) & 1][grp][tp & 63], &lds.cls[((t >> 6) + 1) & 1][grp][0], lds.q[n2], lds.d[n2],
+           lds.t[n2], &lds.m[n2], lds.time, gpos, gtime, gslow, t);
+      wait_vmcnt(0);
+      if (t < nqb) tile_barrier();
     }
 
     // ---- dK: accumulator [i][r] holds key kw + 8(r/4) + 4 lh + r%4, column 32 i + lr
@@ -754,7 +825,7 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
     }
     if (g.grad_stride > 0 && has_pos) {
       const float f = wave_sum(far_acc);
-      if (lane == 0) lds.gpos[grp][Bp - 1] += f;
+      if (lane == 0) gpos[Bp - 1] += f;
     }
   }
 

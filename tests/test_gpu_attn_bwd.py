@@ -129,6 +129,16 @@ def test_large_position_table_and_wide_gaps(hstu):
     _compare(got, ref, "Bp=1024, wide gaps")
 
 
+def test_long_sequence(hstu):
+    """A 4160-token sequence: a key tile walks 130 query blocks, so the key
+    pass refills its table of block classes (64 blocks at a time) twice, and
+    the time gaps grow past 2^22 seconds (buckets up to 22)."""
+    args = _synthetic([4160, 65], 1, 128, seed=17)
+    got = _gpu_bwd(hstu, _dev(*args))
+    ref = _oracle_bwd(*args)
+    _compare(got, ref, "n=4160")
+
+
 def test_large_scores(hstu):
     """Scores of a few tens (q, k ~ N(0, 1)): SiLU' saturates on both sides."""
     args = _synthetic([300, 200], 2, 64, seed=13, qkv_std=1.0)
