@@ -12,8 +12,10 @@ Also on the line:
   roofline      the attention kernel's own average launch time, taken with HIP
                 events that the library records around each launch on the
                 launch stream (hstu_timing_enable), against the bf16 MFMA peak;
-                HBM traffic from the committed rocprofv3 counter summary when
-                it was taken on the current kernel source, else null;
+                HBM traffic (bytes per launch, and over this run's launch
+                time as hbm_gbs) and the MFMA-busy fraction (mfma_util) from
+                the committed rocprofv3 counter summary when it was taken on
+                the current kernel source, else null;
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload;
   secondary     tokens/s per layer of the 4-layer stack (8 x 1024 tokens) and
                 of one layer over the 64-sequence jagged batch, and the
@@ -43,7 +45,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "HSTU attention causal-effective TFLOP/s + tokens/s/layer, jagged bf16, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_c3_traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_fwd_c3_counters.json")
 KERNEL_SRCS = [os.path.join(ROOT, "hstu_pointwise_attention_causal_amd", "csrc", f)
                for f in ("attn_fwd.hip", "attn_common.h", "common.h")]
 LAUNCH_H = os.path.join(ROOT, "hstu_pointwise_attention_causal_amd", "csrc", "launch.h")
@@ -74,17 +76,18 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the attention kernel source changed since it was taken."""
+def _counters():
+    """The committed rocprofv3 counter summary of the attention forward on
+    this workload (MFMA busy fraction, HBM bytes per launch, ...), or None
+    when the kernel source changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTERS_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_sha256_16") != kernel_hash():
         return None
-    return t.get("bytes_per_launch")
+    return t
 
 
 # Kernels the counter summary reports, by a substring of their symbol name.
@@ -591,6 +594,7 @@ def main():
     flops = wl.attn_fwd_flops()
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (kern * 1e-3) / 1e12
+    ctr = _counters()
 
     res = {
         "metric": METRIC,
@@ -624,7 +628,12 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": _traffic(),
+            "traffic": ctr["bytes_per_launch"] if ctr else None,
+            # from the same counter summary (null once the kernel changed):
+            # MFMA-busy cycles over all SIMDs' cycles, and the HBM bytes per
+            # launch over this run's average launch time
+            "mfma_util": ctr["mfma_busy_frac"] if ctr else None,
+            "hbm_gbs": round(ctr["bytes_per_launch"] / (kern * 1e-3) / 1e9, 1) if ctr else None,
             "kernel": f"attn_fwd_bf16_kernel<{wl.dqk},{wl.dv}>",
             "algorithmic_flops_per_launch": flops,
             "avg_launch_ms": round(kern, 5),
