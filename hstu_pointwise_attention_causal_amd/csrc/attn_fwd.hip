@@ -241,6 +241,13 @@ __global__ __launch_bounds__(SPLIT ? 2 * kThreads : kThreads, SPLIT ? 1 : 2) voi
     qf[kb] = qrow < n ? *reinterpret_cast<const bf16x8_t*>(qp + (seq0 + qrow) * a.ldq + h * DQK + kb * 16 + lh * 8)
                       : bf16x8_t{};
 
+  // (issued before the table staging below, whose wait then covers them)
+  const int64_t tq = (has_time && qrow < n) ? a.ts[seq0 + qrow] : 0;
+  int64_t wq_min = 0, wq_max = 0;   // timestamps of this wave's query rows (metadata of its block)
+  if (has_time && qa < n) {
+    wq_min = uniform_i64(meta_row[qa / 32].tmin);
+    wq_max = uniform_i64(meta_row[qa / 32].tmax);
+  }
   if (has_pos) {
     for (int i = tid; i < min(Bp, kPosLdsFast); i += kT) sm.pos[i] = kLog2e * a.pos_table[h * Bp + i];
   }
@@ -249,21 +256,28 @@ __global__ __launch_bounds__(SPLIT ? 2 * kThreads : kThreads, SPLIT ? 1 : 2) voi
   }
   const float pos_last = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(
       has_pos ? kLog2e * a.pos_table[h * Bp + Bp - 1] : 0.f)));   // bias of far pairs
-  // |bias| <= cmax for every pair: max |L P[h][.]| + max |L Tt[h][.]| (NaN propagates)
+  __syncthreads();   // the staged tables
+  // |bias| <= cmax for every pair: max |L P[h][.]| + max |L Tt[h][.]| (NaN
+  // propagates), from the staged tables (and the position entries past them)
+  const int np_lds = has_pos ? min(Bp, kPosLdsFast) : 0, nt_lds = has_time ? min(Bt, kTimeLds) : 0;
   float pmax = 0.f, tmax_ = 0.f;
   bool bad = false;
+  for (int i = lane; i < np_lds; i += 64) {
+    const float x = fabsf(sm.pos[i]);
+    pmax = fmaxf(pmax, x);
+    bad |= !(x == x);
+  }
   if (has_pos)
-    for (int i = lane; i < Bp; i += 64) {
+    for (int i = kPosLdsFast + lane; i < Bp; i += 64) {
       const float x = fabsf(kLog2e * a.pos_table[h * Bp + i]);
       pmax = fmaxf(pmax, x);
       bad |= !(x == x);
     }
-  if (has_time)
-    for (int i = lane; i < min(Bt, kTimeLds); i += 64) {
-      const float x = fabsf(kLog2e * a.time_table[h * Bt + i]);
-      tmax_ = fmaxf(tmax_, x);
-      bad |= !(x == x);
-    }
+  for (int i = lane; i < nt_lds; i += 64) {
+    const float x = fabsf(sm.time[i]);
+    tmax_ = fmaxf(tmax_, x);
+    bad |= !(x == x);
+  }
   // wave-uniform values live in scalar registers
   const float cmax = __builtin_amdgcn_ballot_w64(bad) ? __builtin_nanf("")
                                                       : wave_max_uniform(pmax) + wave_max_uniform(tmax_);
@@ -279,12 +293,6 @@ __global__ __launch_bounds__(SPLIT ? 2 * kThreads : kThreads, SPLIT ? 1 : 2) voi
   const float qbound_max =
       __builtin_amdgcn_ballot_w64(qbound != qbound) ? __builtin_nanf("") : wave_max_uniform(qbound);
   const float qbound_min = wave_min_uniform(qrow < n ? qbound : __builtin_inff());   // smallest row bound
-  const int64_t tq = (has_time && qrow < n) ? a.ts[seq0 + qrow] : 0;
-  int64_t wq_min = 0, wq_max = 0;   // timestamps of this wave's query rows (metadata of its block)
-  if (has_time && qa < n) {
-    wq_min = uniform_i64(meta_row[qa / 32].tmin);
-    wq_max = uniform_i64(meta_row[qa / 32].tmax);
-  }
 
   f32x16_t oacc[NB];
 #pragma unroll
