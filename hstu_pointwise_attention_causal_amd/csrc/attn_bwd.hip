@@ -868,15 +868,43 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
 
 // ============================================================================
 // query pass: dQ
+//
+// A work item owns 128 query rows and walks the 32-key blocks from the
+// sequence start to its last row. Waves w and w + 4 run on one SIMD and share
+// a group of 32 query rows (qa = q0 + 32 (w & 3), one query per lane as the
+// column of S^T), in two roles as in the key pass:
+//   score wave (w < 4)      S^T = K Q^T one block ahead (its products spread
+//                           over the current block's per-pair loop), the bias
+//                           and SiLU'(x) of every pair (masked pairs: 0);
+//   gradient wave (w >= 4)  the tile loads, the block classes (64 blocks at a
+//                           time, one per lane), and one block behind the
+//                           score wave: dA^T = V dO^T, dS = dA SiLU'(x) and
+//                           dQ += dS K.
+// SiLU'(x) passes through LDS as fp16. Q (score) and dO (gradient) of the
+// lane's query stay in registers as MFMA B operands; K, V and the key
+// timestamps of block t + 2 load into a ring of four LDS
+// slots while block t is processed, one barrier per block.
 // ============================================================================
 template <int DQK, int DV>
-__global__ __launch_bounds__(kBThreads, 2) void attn_bwd_q_kernel(AttnBwdArgs g) {
+struct QLds {
+  __attribute__((aligned(16))) char k[kKRing][32 * DQK * 2];
+  __attribute__((aligned(16))) char v[kKRing][32 * DV * 2];
+  __attribute__((aligned(16))) int64_t t[kKRing][32];
+  f16x8_t xg[2][4][2][64];      // SiLU' of a block: [buffer][query group][r / 8][lane]
+  KvClass cls[2][4][64];        // [(block / 64) % 2][query group][block % 64]
+  float pos[kBwdPosMax];        // log2(e) P[h][.] (one 0 without the table)
+  float time[kBwdTimeSlots];    // log2(e) Tt[h][.] (one 0 without the table)
+};
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(kKThreads, 1) void attn_bwd_q_kernel(AttnBwdArgs g) {
   static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims");
   const AttnArgs& a = g.f;
   constexpr int KB = DQK / 16, VB = DV / 16;       // k-steps of S^T and dA^T
   constexpr int NQ = DQK / 32;                     // 32-column groups of dQ
-  constexpr int KCH = DQK / 8, VCH = DV / 8;
-  constexpr int KI = (KCH + kBW - 1) / kBW, VI = (VCH + kBW - 1) / kBW;
+  constexpr int KCH = DQK / 8, VCH = DV / 8;       // 16-byte chunks per K / V row
+  constexpr int KI = (KCH / 2 + kKIssue - 1) / kKIssue, VI = (VCH / 2 + kKIssue - 1) / kKIssue;
+  static_assert(KB <= 16 && KB == VB, "at most one product per pair; one fragment count for both roles");
 
   const int item_idx = blockIdx.x;
   if (item_idx >= *a.item_count) return;
@@ -886,207 +914,299 @@ __global__ __launch_bounds__(kBThreads, 2) void attn_bwd_q_kernel(AttnBwdArgs g)
   const int n = static_cast<int>(a.off[b + 1] - seq0);
   const int q0 = qt * kAttnBM;
 
-  __shared__ BwdSmem<DQK, DV> sm;
+  __shared__ QLds<DQK, DV> lds;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
-  const int qa = q0 + 32 * w;
-  const int qrow = qa + lr;
+  const int grp = w & 3;
+  const int qa = q0 + 32 * grp;   // first query row of this wave's group
+  const int qrow = qa + lr;       // this lane's query (column of S^T)
   const bool has_time = a.time_table != nullptr, has_pos = a.pos_table != nullptr;
   const int Bp = a.pos_buckets, Bt = a.time_buckets;
+  const int pos_hi = has_pos ? Bp - 1 : 0, time_nb = has_time ? min(Bt, kBwdTimeSlots) : 1;
   const BlockMeta* meta_row =
       static_cast<const BlockMeta*>(a.meta) + h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * a.tile_base[b];
 
-  if (has_pos)
-    for (int i = tid; i < Bp; i += kBThreads) sm.pos[i] = kLog2e * a.pos_table[h * Bp + i];
-  if (has_time)
-    for (int i = tid; i < min(Bt, kBwdTimeSlots); i += kBThreads) sm.time[i] = kLog2e * a.time_table[h * Bt + i];
-  const float pos_last = has_pos ? kLog2e * a.pos_table[h * Bp + Bp - 1] : 0.f;
+  // ---- prologue: every global load is issued before the first wait
+  const int kv_end = min(n, q0 + kAttnBM);
+  const int nkb = (kv_end + 31) / 32;        // key blocks of the walk (>= 1)
+  // a block's pairs are all masked when its first key follows the group's last row
+  auto block_active = [&](int t) __attribute__((always_inline)) { return qa < n && 32 * t <= qa + 31; };
 
-  // Q and dO rows of this lane's query: B operands of S^T = K Q^T, dA^T = V dO^T
-  const __bf16* qp = static_cast<const __bf16*>(a.q);
-  const __bf16* dop = static_cast<const __bf16*>(g.d_o);
-  bf16x8_t qf[KB], df[VB];
+  // Q (score waves) or dO (gradient waves) row of this lane's query: the MFMA
+  // B operands of S^T = K Q^T and dA^T = V dO^T
+  bf16x8_t frag[KB];
+  {
+    const __bf16* src = w < 4 ? static_cast<const __bf16*>(a.q) + (seq0 + qrow) * a.ldq + h * DQK
+                              : static_cast<const __bf16*>(g.d_o) + (seq0 + qrow) * g.lddo + h * DV;
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-    qf[kb] = qrow < n ? *reinterpret_cast<const bf16x8_t*>(qp + (seq0 + qrow) * a.ldq + h * DQK + kb * 16 + lh * 8)
-                      : bf16x8_t{};
-#pragma unroll
-  for (int vb = 0; vb < VB; ++vb)
-    df[vb] = qrow < n ? *reinterpret_cast<const bf16x8_t*>(dop + (seq0 + qrow) * g.lddo + h * DV + vb * 16 + lh * 8)
-                      : bf16x8_t{};
+    for (int kb = 0; kb < KB; ++kb)
+      frag[kb] = qrow < n ? *reinterpret_cast<const bf16x8_t*>(src + kb * 16 + lh * 8) : bf16x8_t{};
+  }
   const int64_t tq = (has_time && qrow < n) ? a.ts[seq0 + qrow] : 0;
   int64_t tq_min = 0, tq_max = 0;
   if (has_time && qa < n) {
     tq_min = uniform_i64(meta_row[qa / 32].tmin);
     tq_max = uniform_i64(meta_row[qa / 32].tmax);
   }
-  const float alpha_l = a.alpha * kLog2e;
+  const float pos_last = has_pos ? kLog2e * a.pos_table[h * Bp + Bp - 1] : 0.f;
+  static_assert(kBwdPosMax <= 2 * kKThreads && kBwdTimeSlots <= kKThreads, "two table loads per thread");
+  const __amdgpu_buffer_rsrc_t rpos = make_rsrc(has_pos ? a.pos_table + h * Bp : nullptr, has_pos ? Bp * 4 : 0);
+  const __amdgpu_buffer_rsrc_t rtim = make_rsrc(has_time ? a.time_table + h * Bt : nullptr, has_time ? time_nb * 4 : 0);
+  const float pos0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpos, tid * 4, 0, 0));
+  const float pos1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpos, (tid + kKThreads) * 4, 0, 0));
+  const float time0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rtim, tid * 4, 0, 0));
+  // (gradient waves) the metadata of key block lane, for the first classes
+  int64_t ck_min = 0, ck_max = 0;
+  if (w >= kKIssue && has_time && lane < nkb) {
+    ck_min = meta_row[lane].tmin;
+    ck_max = meta_row[lane].tmax;
+  }
 
-  f32x16_t dqa[NQ];
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) dqa[i] = f32x16_t{};
-
+  // (gradient waves) the loads of the key blocks in order, block t into ring
+  // slot t % kKRing; the buffer descriptors advance by one block per call
+  const int wi = w - kKIssue;
   uint32_t koff[KI], voff[VI];
-  tile_load_offsets<KCH>(w, lane, a.ldk, koff);
-  tile_load_offsets<VCH>(w, lane, a.ldv, voff);
-  const char* kbase = static_cast<const char*>(a.k) + (seq0 * a.ldk + h * DQK) * 2;
-  const char* vbase = static_cast<const char*>(a.v) + (seq0 * a.ldv + h * DV) * 2;
-  const int64_t* tsbase = has_time ? a.ts + seq0 : nullptr;
-  uint32_t k_row[KB], v_row[VB];
+  const int64_t kstep = int64_t(32) * a.ldk * 2, vstep = int64_t(32) * a.ldv * 2;
+  const char* knext = static_cast<const char*>(a.k) + (seq0 * a.ldk + h * DQK) * 2;
+  const char* vnext = static_cast<const char*>(a.v) + (seq0 * a.ldv + h * DV) * 2;
+  const int64_t* tnext = has_time ? a.ts + seq0 : nullptr;
+  int64_t kleft = int64_t(n) * a.ldk * 2, vleft = int64_t(n) * a.ldv * 2;
+  int64_t rows_left = n;
+  int issued = 0;
+  auto issue_next = [&](char* nk, char* nv, int64_t* nt) __attribute__((always_inline)) {
+    if (issued < nkb) {
+      constexpr int NKI = KCH / 2, NVI = VCH / 2;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(knext, kleft), rv = make_rsrc(vnext, vleft);
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) k_row[kb] = row_read_offset<KCH>(lr, lh, kb);
+      for (int j = 0; j < KI; ++j)
+        if (wi + j * kKIssue < NKI) load_lds16(rk, nk + (wi + j * kKIssue) * 1024, koff[j]);
 #pragma unroll
-  for (int vb = 0; vb < VB; ++vb) v_row[vb] = row_read_offset<VCH>(lr, lh, vb);
-  uint32_t k_tr0[NQ], k_tr1[NQ];
-#pragma unroll
-  for (int nb = 0; nb < NQ; ++nb) tr_read_offsets<KCH>(lane, nb, k_tr0[nb], k_tr1[nb]);
+      for (int j = 0; j < VI; ++j)
+        if (wi + j * kKIssue < NVI) load_lds16(rv, nv + (wi + j * kKIssue) * 1024, voff[j]);
+      if (wi == kKIssue - 2 && lane < 16)
+        load_lds16(make_rsrc(tnext, tnext ? rows_left * 8 : 0), reinterpret_cast<char*>(nt), lane * 16);
+      knext += kstep;
+      vnext += vstep;
+      kleft -= kstep;
+      vleft -= vstep;
+      if (tnext) tnext += 32;
+      rows_left -= 32;
+      ++issued;
+    }
+  };
+  // (gradient waves) classes of key blocks [c0, c0 + 64) for this query
+  // group, one block per lane (tk_min, tk_max: its timestamp range), into
+  // out[block - c0]
+  auto classify_chunk = [&](int c0, int64_t tk_min, int64_t tk_max, const float* stime, KvClass* out)
+                            __attribute__((always_inline)) {
+    const int t = c0 + lane;
+    if (t >= nkb) return;
+    const int ka = 32 * t;
+    const BlockClass c =
+        classify_block(qa, ka, n, has_pos, Bp, has_time, Bt, tq_min, tq_max, tk_min, tk_max, pos_last, stime);
+    int info = c.path | (c.tlo << 8);
+    if (c.path == kBGeneral) {
+      if (ka + 31 > qa || qa + 31 >= n || ka + 31 >= n) info |= kInfoMasked;
+      if (!has_time || (tq_max - tk_min <= int64_t(INT32_MAX) - 1 && tq_min - tk_max >= int64_t(INT32_MIN)))
+        info |= kInfoNarrow;
+    }
+    out[lane] = KvClass{info, c.clo, c.chi, 0};
+  };
 
-  const int kv_end = min(n, q0 + kAttnBM);
-  const int ntk = (kv_end + kBBN - 1) / kBBN;
+  if (w >= kKIssue) {
+    block_load_offsets<KCH>(wi, lane, a.ldk, koff);
+    block_load_offsets<VCH>(wi, lane, a.ldv, voff);
+    issue_next(lds.k[0], lds.v[0], lds.t[0]);
+    issue_next(lds.k[1], lds.v[1], lds.t[1]);
+  }
+  wait_vmcnt(0);
+  if (tid <= pos_hi) lds.pos[tid] = kLog2e * pos0;   // one 0 without the table
+  if (tid + kKThreads <= pos_hi) lds.pos[tid + kKThreads] = kLog2e * pos1;
+  if (tid < time_nb) lds.time[tid] = kLog2e * time0;
+  __syncthreads();   // the staged tables (read by the classification)
+  if (w >= kKIssue) classify_chunk(0, ck_min, ck_max, lds.time, &lds.cls[0][grp][0]);
+  __syncthreads();   // also publishes the first classes
 
-  auto step = [&] __device__(const char* __restrict__ rk, const char* __restrict__ rv,
-                             const int64_t* __restrict__ rt, const BlockMeta* __restrict__ rm,
-                             char* __restrict__ nk, char* __restrict__ nv, int64_t* __restrict__ nt,
-                             BlockMeta* __restrict__ nm, const float* __restrict__ spos,
-                             const float* __restrict__ stime, int t) {
-    const int k0 = t * kBBN;
-    if (t + 1 < ntk)
-      issue_rows_tile<KCH, VCH>(kbase, vbase, a.ldk, a.ldv, tsbase, meta_row, n, k0 + kBBN, w, lane, koff, voff, nk,
-                                nv, nt, nm);
+  if (w < 4) {
+    // ======================= score wave =======================
+    const bf16x8_t* qf = frag;
+    const float alpha_l = a.alpha * kLog2e;
+    uint32_t k_row[KB];
 #pragma unroll
-    for (int kvb = 0; kvb < 2; ++kvb) {
-      const int ka = k0 + 32 * kvb;
-      const bool active = qa < n && ka < n && ka <= qa + 31;
-      f32x16_t s = f32x16_t{}, da = f32x16_t{};
-      const char* kblk = rk + kvb * 32 * KCH * 16;
-      const char* vblk = rv + kvb * 32 * VCH * 16;
+    for (int kb = 0; kb < KB; ++kb) k_row[kb] = row_read_offset<KCH>(lr, lh, kb);
+    // S^T of block t (computed one step earlier)
+    f32x16_t s_cur = f32x16_t{};
+
+    // One block per step; the products of S^T of block t + 1 (unused past
+    // the walk or when block t + 1 is masked entirely) are spread over the
+    // per-pair loop; a block masked entirely ends the wave's work. Every LDS buffer comes in through a __restrict__
+    // parameter, so the compiler does not wait for the loads in flight.
+    auto step = [&](const char* __restrict__ rk1, const int64_t* __restrict__ rt, const KvClass* __restrict__ rc,
+                    f16x8_t* __restrict__ xg, const float* __restrict__ spos, const float* __restrict__ stime,
+                    int t) __attribute__((always_inline)) {
+      const f32x16_t s = s_cur;
+      f32x16_t sn = f32x16_t{};
+      auto mf = [&](int k) __attribute__((always_inline)) {
+        if (k < KB) {
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(rk1 + k_row[k]);
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[k], sn, 0, 0, 0);
+        }
+      };
+      if (!block_active(t)) return;   // and every later block
+      const int ka = 32 * t;
+      // s[4g+e]: key ka + 8g + 4lh + e, query qrow
+      const int info = __builtin_amdgcn_readfirstlane(rc->info);
+      const int path = info & 3, tlo = (info >> 8) & 255;
+      const float clo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(rc->clo)));
+      const float chi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(rc->chi)));
+      // SiLU' (fp16) packed eight at a time
+      f16x8_t gq;
+      auto emit = [&](int r, float dl) __attribute__((always_inline)) {
+        gq[r & 7] = static_cast<_Float16>(dl);
+        if ((r & 7) == 7) xg[(r >> 3) * 64 + lane] = gq;
+      };
+      // pairs with varying position buckets or a mask: a bucket per pair, the
+      // time bucket from the timestamps' low words when the block's gaps fit
+      // in int32 (zero tables stand in for missing ones)
+      auto general = [&](auto masked_c, auto narrow_c) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_c)::value, NARROW = decltype(narrow_c)::value;
 #pragma unroll
-      for (int kb = 0; kb < (KB > VB ? KB : VB); ++kb) {
-        if (kb < KB)
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(kblk + k_row[kb]), qf[kb], s,
-                                                      0, 0, 0);
-        if (kb < VB)
-          da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(vblk + v_row[kb]), df[kb],
-                                                       da, 0, 0, 0);
-      }
-      // s[4g+e], da[4g+e]: key ka + 8g + 4lh + e, query qrow
-      float ds[16];
-      if (!active) {
+        for (int r = 0; r < 16; ++r) {
+          const int il = 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int kv = ka + il, d = qrow - kv;
+          int tbr;
+          if constexpr (NARROW) tbr = time_bucket_narrow(tq, rt[il], time_nb);
+          else tbr = time_bucket64(tq - rt[il], time_nb);
+          const int pb = MASKED ? min(max(d, 0), pos_hi) : min(d, pos_hi);
+          float pl, dl;
+          silu_and_grad(fmaf(s[r], alpha_l, spos[pb] + stime[tbr]), pl, dl);
+          if constexpr (MASKED) {
+            const bool valid = d >= 0 && kv < n && qrow < n;
+            emit(r, valid ? dl : 0.f);
+          } else {
+            emit(r, dl);
+          }
+          mf(r);
+        }
+      };
+      if (path == kBUniform) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ds[r] = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float pl, dl;
+          silu_and_grad(fmaf(s[r], alpha_l, clo), pl, dl);
+          emit(r, dl);
+          mf(r);
+        }
+      } else if (path == kBTwoTime) {
+        // the key's timestamp at most tq - (2^(tlo+1) - 1): bucket tlo + 1
+        const int64_t lim = tq - ((int64_t(1) << (tlo + 1)) - 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int il = 8 * (r >> 2) + 4 * lh + (r & 3);
+          const bool hi = rt[il] <= lim;
+          float pl, dl;
+          silu_and_grad(fmaf(s[r], alpha_l, hi ? chi : clo), pl, dl);
+          emit(r, dl);
+          mf(r);
+        }
+      } else if (!(info & kInfoMasked) && (info & kInfoNarrow)) {
+        general(std::false_type{}, std::true_type{});
+      } else if (info & kInfoNarrow) {
+        general(std::true_type{}, std::true_type{});
       } else {
-        int64_t tk_min = 0, tk_max = 0;
-        if (has_time) {
-          tk_min = uniform_i64(rm[kvb].tmin);
-          tk_max = uniform_i64(rm[kvb].tmax);
-        }
-        const BlockClass c =
-            classify_block(qa, ka, n, has_pos, Bp, has_time, Bt, tq_min, tq_max, tk_min, tk_max, pos_last, stime);
-        if (c.path != kBGeneral) {
-          const int64_t lim = tq - ((int64_t(1) << (c.tlo + 1)) - 1);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kl = kvb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            const bool hi = c.path == kBTwoTime && rt[kl] <= lim;
-            const float x = fmaf(s[r], alpha_l, hi ? c.chi : c.clo);
-            float pl, dsl;
-            silu_and_grad(x, pl, dsl);
-            ds[r] = da[r] * dsl;
-          }
-        } else {
-          // Per-pair buckets in two halves of 8 pairs, each issuing all its
-          // lookups before the first is used; one or two time buckets across
-          // the block's valid pairs take a compare-and-select instead (as in
-          // the key pass).
-          TimeSpan tsp{0, 0, false};
-          if (has_time) tsp = time_span(tq_min - tk_max, tq_max - tk_min, Bt);
-          const int64_t lim = tq - ((int64_t(1) << (tsp.lo + 1)) - 1);
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            float cb[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = 8 * hf + e;
-              const int kv = k0 + kvb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-              cb[e] = has_pos ? spos[min(max(qrow - kv, 0), Bp - 1)] : 0.f;
-            }
-            if (has_time) {
-              if (tsp.hi - tsp.lo <= 1) {
-                const float vlo = stime[tsp.lo], vhi = stime[tsp.hi];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                  const int r = 8 * hf + e;
-                  cb[e] += tsp.hi > tsp.lo && rt[kvb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)] <= lim ? vhi : vlo;
-                }
-              } else if (tsp.narrow) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                  const int r = 8 * hf + e;
-                  cb[e] += stime[time_bucket_narrow(tq, rt[kvb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)], Bt)];
-                }
-              } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                  const int r = 8 * hf + e;
-                  cb[e] += stime[time_bucket64(tq - rt[kvb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)], Bt)];
-                }
-              }
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = 8 * hf + e;
-              const int kv = k0 + kvb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-              const bool valid = kv <= qrow && kv < n && qrow < n;
-              const float x = fmaf(s[r], alpha_l, cb[e]);
-              float pl, dsl;
-              silu_and_grad(x, pl, dsl);
-              ds[r] = valid ? da[r] * dsl : 0.f;
-            }
-          }
-        }
+        general(std::true_type{}, std::false_type{});
       }
+      s_cur = sn;
+    };
+
+    if (block_active(0)) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(lds.k[0] + k_row[kb]),
+                                                        qf[kb], s_cur, 0, 0, 0);
+    }
+    for (int t = 0; t < nkb; ++t) {
+      step(lds.k[(t + 1) % kKRing], lds.t[t % kKRing], &lds.cls[(t >> 6) & 1][grp][t & 63],
+           &lds.xg[t & 1][grp][0][0], lds.pos, lds.time, t);
+      tile_barrier();
+    }
+  } else {
+    // ====================== gradient wave ======================
+    const bf16x8_t* df = frag;
+    uint32_t v_row[VB], k_tr0[NQ], k_tr1[NQ];
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) v_row[vb] = row_read_offset<VCH>(lr, lh, vb);
+#pragma unroll
+    for (int nb = 0; nb < NQ; ++nb) tr_read_offsets<KCH>(lane, nb, k_tr0[nb], k_tr1[nb]);
+    f32x16_t dqa[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) dqa[i] = f32x16_t{};
+
+    // Step t: the loads of block t + 2, at t = 64 k + 1 the classes of blocks
+    // [64 (k + 1), 64 (k + 2)) (into the table half whose last reader was
+    // step 64 k), then block t - 1 (its SiLU' was written before the last
+    // barrier): dA^T, dS and dQ += dS K. Every LDS buffer comes in through a
+    // __restrict__ parameter (as in the score wave's step).
+    auto step = [&](const char* __restrict__ rk, const char* __restrict__ rv, const f16x8_t* __restrict__ xg,
+                    KvClass* __restrict__ wc, char* __restrict__ nk, char* __restrict__ nv,
+                    int64_t* __restrict__ nt, const float* __restrict__ stime,
+                    int t) __attribute__((always_inline)) {
+      issue_next(nk, nv, nt);
+      if ((t & 63) == 1 && t + 63 < nkb) {
+        int64_t k_min = 0, k_max = 0;
+        if (has_time && t + 63 + lane < nkb) {
+          k_min = meta_row[t + 63 + lane].tmin;
+          k_max = meta_row[t + 63 + lane].tmax;
+        }
+        classify_chunk(t + 63, k_min, k_max, stime, wc);
+      }
+      const int tb_ = t - 1;
+      if (tb_ < 0 || !block_active(tb_)) return;
+      bf16x8_t vfr[VB];
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) vfr[vb] = *reinterpret_cast<const bf16x8_t*>(rv + v_row[vb]);
+      f32x16_t da = f32x16_t{};
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[vb], df[vb], da, 0, 0, 0);
       // dQ += dS K over the block's 32 keys (two 16-key steps)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
+        const f16x8_t gv = xg[kk * 64 + lane];
         bf16x8_t sa;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sa[i] = static_cast<__bf16>(ds[kk * 8 + i]);
-        const char* kst = kblk + kk * 16 * KCH * 16;
+        for (int i = 0; i < 8; ++i) sa[i] = static_cast<__bf16>(da[kk * 8 + i] * static_cast<float>(gv[i]));
+        const char* kst = rk + kk * 16 * KCH * 16;
 #pragma unroll
         for (int nb = 0; nb < NQ; ++nb) {
-          const bf16x8_t kb16 = __builtin_shufflevector(tr_read(kst + k_tr0[nb]), tr_read(kst + k_tr1[nb]), 0, 1, 2,
-                                                        3, 4, 5, 6, 7);
+          const bf16x8_t kb16 =
+              __builtin_shufflevector(tr_read(kst + k_tr0[nb]), tr_read(kst + k_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
           dqa[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, kb16, dqa[nb], 0, 0, 0);
         }
       }
+    };
+
+    for (int t = 0; t <= nkb; ++t) {
+      // slots: block t - 1 (K, V), t + 2 (loads)
+      const int pv = (t + kKRing - 1) % kKRing, n2 = (t + 2) % kKRing;
+      step(lds.k[pv], lds.v[pv], &lds.xg[(t + 1) & 1][grp][0][0], &lds.cls[((t >> 6) + 1) & 1][grp][0], lds.k[n2],
+           lds.v[n2], lds.t[n2], lds.time, t);
+      wait_vmcnt(0);
+      if (t < nkb) tile_barrier();
     }
-  };
 
-  if (ntk > 0)
-    issue_rows_tile<KCH, VCH>(kbase, vbase, a.ldk, a.ldv, tsbase, meta_row, n, 0, w, lane, koff, voff, sm.a[0],
-                              sm.b[0], sm.t[0], sm.m[0]);
-  wait_vmcnt(0);
-  __syncthreads();
-  for (int t = 0; t < ntk; ++t) {
-    const int buf = t & 1;
-    step(sm.a[buf], sm.b[buf], sm.t[buf], sm.m[buf], sm.a[buf ^ 1], sm.b[buf ^ 1], sm.t[buf ^ 1], sm.m[buf ^ 1],
-         sm.pos, sm.time, t);
-    wait_vmcnt(0);
-    tile_barrier();
-  }
-
-  // ---- dQ: accumulator [i][r] holds query qa + 8(r/4) + 4 lh + r%4, column 32 i + lr
-  const float inv_n = a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n);
-  const float sq = a.alpha * inv_n;
-  __bf16* dqp = static_cast<__bf16*>(g.dq) + (seq0 + qa) * g.lddq + h * DQK + lr;
+    // ---- dQ: accumulator [i][r] holds query qa + 8(r/4) + 4 lh + r%4, column 32 i + lr
+    const float inv_n = a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n);
+    const float sq = a.alpha * inv_n;
+    __bf16* dqp = static_cast<__bf16*>(g.dq) + (seq0 + qa) * g.lddq + h * DQK + lr;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int qr = 8 * (r >> 2) + 4 * lh + (r & 3);
-    if (qa + qr < n) {
+    for (int r = 0; r < 16; ++r) {
+      const int qr = 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (qa + qr < n) {
 #pragma unroll
-      for (int nb = 0; nb < NQ; ++nb) dqp[qr * g.lddq + nb * 32] = static_cast<__bf16>(dqa[nb][r] * sq);
+        for (int nb = 0; nb < NQ; ++nb) dqp[qr * g.lddq + nb * 32] = static_cast<__bf16>(dqa[nb][r] * sq);
+      }
     }
   }
 }
@@ -1156,7 +1276,7 @@ hipError_t launch_bwd_dims(const AttnBwdArgs& g, hipStream_t stream) {
   if (e != hipSuccess) return e;
   {
     TimedScope timed(kTimedAttnBwdQ, stream);
-    e = launch_bwd_items(attn_bwd_q_kernel<D, D>, kBThreads, g, stream);
+    e = launch_bwd_items(attn_bwd_q_kernel<D, D>, kKThreads, g, stream);
   }
   if (e != hipSuccess) return e;
   if (g.grad_stride > 0) {
