@@ -27,12 +27,18 @@
 //   which is the A-operand layout of the two updates when the rows of a 16-row
 //   step are taken in the order {4h..4h+3, 8+4h..8+4h+3} (h = lane / 32); the
 //   transposed reads of dO and Q use the same order. Bias-table gradients are
-//   summed per wave in LDS (one table per wave, so no two waves race) and
-//   written as one partial row per key tile.
+//   summed per gradient wave in LDS (one table per wave, so no two waves race)
+//   and written as one partial row per key tile.
 //
 //   query pass (attn_bwd_q_kernel): a work item owns 128 query rows, as in the
-//   forward, and recomputes S^T = K Q^T and dA^T = V dO^T per key tile to form
-//   dQ[i][d] += dS K with K read transposed from LDS.
+//   forward, and recomputes S^T = K Q^T and dA^T = V dO^T per key block to
+//   form dQ[i][d] += dS K with K read transposed from LDS.
+//
+//   Both passes run eight waves per workgroup in two roles on each SIMD: a
+//   score wave (S, the bias, SiLU and SiLU' of every pair, one block ahead)
+//   and a gradient wave (the tile loads, the block classes, dA, dS and the
+//   products that use them); SiLU' and the classes pass between the two
+//   through LDS (see each kernel's comment).
 //
 //   bias reduction (attn_bwd_bias_reduce_kernel): sums the partial rows of
 //   each head in tile order.
