@@ -368,9 +368,9 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
   const int item_idx = blockIdx.x;
   if (item_idx >= *a.item_count) return;
   const WorkItem item = reinterpret_cast<const WorkItem*>(a.items)[item_idx];
-  const int b = item.seq, h = item_head(item);
-  const int64_t seq0 = a.off[b];
-  const int n = static_cast<int>(a.off[b + 1] - seq0);
+  const int h = item_head(item);
+  const int64_t seq0 = item.seq0;
+  const int n = item.n;
   // the list orders tiles by query-pass cost (tile index + 1); the key pass
   // costs (tiles - key tile), so tile qt of the list is key tile tiles-1-qt
   const int ntl = (n + kAttnBM - 1) / kAttnBM;
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
   // index bounds of the staged tables (a missing table is one zero entry)
   const int pos_hi = has_pos ? Bp - 1 : 0, time_nb = has_time ? min(Bt, kBwdTimeSlots) : 1;
   const BlockMeta* meta_row =
-      static_cast<const BlockMeta*>(a.meta) + h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * a.tile_base[b];
+      static_cast<const BlockMeta*>(a.meta) + h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * item.tile_base;
 
   // ---- prologue: every global load is issued before the first wait (a
   // work item's set-up is exposed: one workgroup fills a compute unit)
@@ -839,7 +839,7 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
   if (g.grad_stride > 0) {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the asm adds have landed
     __syncthreads();
-    float* prow = g.partial + (static_cast<int64_t>(h) * g.tile_rows + a.tile_base[b] + kt) * g.grad_stride;
+    float* prow = g.partial + (static_cast<int64_t>(h) * g.tile_rows + item.tile_base + kt) * g.grad_stride;
     if (has_pos)
       for (int i = tid; i < Bp; i += kKThreads) {
         float s = 0.f;
@@ -915,9 +915,9 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_q_kernel(AttnBwdArgs g)
   const int item_idx = blockIdx.x;
   if (item_idx >= *a.item_count) return;
   const WorkItem item = reinterpret_cast<const WorkItem*>(a.items)[item_idx];
-  const int b = item.seq, qt = item_qtile(item), h = item_head(item);
-  const int64_t seq0 = a.off[b];
-  const int n = static_cast<int>(a.off[b + 1] - seq0);
+  const int qt = item_qtile(item), h = item_head(item);
+  const int64_t seq0 = item.seq0;
+  const int n = item.n;
   const int q0 = qt * kAttnBM;
 
   __shared__ QLds<DQK, DV> lds;
@@ -932,7 +932,7 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_q_kernel(AttnBwdArgs g)
   const int Bp = a.pos_buckets, Bt = a.time_buckets;
   const int pos_hi = has_pos ? Bp - 1 : 0, time_nb = has_time ? min(Bt, kBwdTimeSlots) : 1;
   const BlockMeta* meta_row =
-      static_cast<const BlockMeta*>(a.meta) + h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * a.tile_base[b];
+      static_cast<const BlockMeta*>(a.meta) + h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * item.tile_base;
 
   // ---- prologue: every global load is issued before the first wait
   const int kv_end = min(n, q0 + kAttnBM);

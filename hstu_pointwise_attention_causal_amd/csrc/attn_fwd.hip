@@ -198,9 +198,9 @@ __global__ __launch_bounds__(SPLIT ? 2 * kThreads : kThreads, SPLIT ? 1 : 2) voi
   const int item_idx = blockIdx.x;
   if (item_idx >= *a.item_count) return;
   const WorkItem item = reinterpret_cast<const WorkItem*>(a.items)[item_idx];
-  const int b = item.seq, qt = item_qtile(item), h = item_head(item);
-  const int64_t seq0 = a.off[b];
-  const int n = static_cast<int>(a.off[b + 1] - seq0);
+  const int qt = item_qtile(item), h = item_head(item);
+  const int64_t seq0 = item.seq0;
+  const int n = item.n;
   const int q0 = qt * kAttnBM;
 
   __shared__ Smem sm;
@@ -215,9 +215,10 @@ __global__ __launch_bounds__(SPLIT ? 2 * kThreads : kThreads, SPLIT ? 1 : 2) voi
   const bool has_pos = a.pos_table != nullptr;
   const int Bp = a.pos_buckets, Bt = a.time_buckets;
   const bool pos_in_lds = Bp <= kPosLdsFast;
-  // metadata row of (head h, sequence b): its 32-key blocks start at kMetaPerTile * tile_base[b]
+  // metadata row of (head h, the item's sequence): its 32-key blocks start at
+  // kMetaPerTile times the sequence's first query tile in the list numbering
   const BlockMeta* meta_row =
-      static_cast<const BlockMeta*>(a.meta) + h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * a.tile_base[b];
+      static_cast<const BlockMeta*>(a.meta) + h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * item.tile_base;
 
   // The loads of the prologue go out first, so that their latencies overlap
   // with the table staging and the reductions below: key tile 0 and this
@@ -635,9 +636,9 @@ __global__ __launch_bounds__(kMetaPerTile * 64) void attn_block_meta_kernel(Attn
   const int item_idx = blockIdx.x;
   if (item_idx >= *a.item_count) return;
   const WorkItem item = reinterpret_cast<const WorkItem*>(a.items)[item_idx];
-  const int b = item.seq, qt = item_qtile(item), h = item_head(item);
-  const int64_t seq0 = a.off[b];
-  const int n = static_cast<int>(a.off[b + 1] - seq0);
+  const int qt = item_qtile(item), h = item_head(item);
+  const int64_t seq0 = item.seq0;
+  const int n = item.n;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int jb = qt * kMetaPerTile + w;       // 32-key block of this wave
   const int key = jb * 32 + (lane >> 1);      // two lanes per key, half the dims each
@@ -677,7 +678,7 @@ __global__ __launch_bounds__(kMetaPerTile * 64) void attn_block_meta_kernel(Attn
     m.tmin = tmin;
     m.tmax = tmax;
     m.pad1 = 0;
-    static_cast<BlockMeta*>(a.meta)[h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * a.tile_base[b] + jb] = m;
+    static_cast<BlockMeta*>(a.meta)[h * a.meta_blocks + static_cast<int64_t>(kMetaPerTile) * item.tile_base + jb] = m;
   }
 }
 
@@ -692,9 +693,9 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32_kernel(AttnArgs a) {
   const int item_idx = blockIdx.x;
   if (item_idx >= *a.item_count) return;
   const WorkItem item = reinterpret_cast<const WorkItem*>(a.items)[item_idx];
-  const int b = item.seq, qt = item_qtile(item), h = item_head(item);
-  const int64_t seq0 = a.off[b];
-  const int n = static_cast<int>(a.off[b + 1] - seq0);
+  const int qt = item_qtile(item), h = item_head(item);
+  const int64_t seq0 = item.seq0;
+  const int n = item.n;
   const int q0 = qt * kAttnBM;
   const float inv_div = a.divisor > 0.f ? 1.0f / a.divisor : 1.0f / static_cast<float>(n);
 

@@ -16,10 +16,15 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Work item of the attention kernels: one (sequence, head, query tile).
+// Work item of the attention kernels: one (sequence, head, query tile), with
+// the sequence's start and length (clamped offsets; T < 2^27, so they fit in
+// 32 bits) and its first query tile in the list's per-sequence numbering, so
+// that a workgroup needs a single 16-byte load to begin.
 struct WorkItem {
-  int32_t seq;
+  int32_t seq0;
+  int32_t n;
   int32_t packed;  // q_tile | head << 20
+  int32_t tile_base;
 };
 __device__ __forceinline__ int item_qtile(WorkItem w) { return w.packed & 0xFFFFF; }
 __device__ __forceinline__ int item_head(WorkItem w) { return w.packed >> 20; }

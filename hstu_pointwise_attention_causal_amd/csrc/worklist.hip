@@ -174,10 +174,15 @@ __global__ __launch_bounds__(kBuildThreads) void build_worklist_kernel(
     int qt = f - tile_base[b];
     int slot = atomicAdd(&fill[qt], 1);
     int base = level_start[qt] + slot * H;
+    const int64_t s0 = off[b];
+    const int n = static_cast<int>(off[b + 1] - s0);
+    const int tb = tile_base[b];
     for (int h = 0; h < H; ++h) {
       WorkItem w;
-      w.seq = b;
+      w.seq0 = static_cast<int32_t>(s0);
+      w.n = n;
       w.packed = qt | (h << 20);
+      w.tile_base = tb;
       items[base + h] = w;
     }
   }
