@@ -72,6 +72,25 @@ __device__ __forceinline__ void issue_rows64(const char* base, int64_t ld, int r
   }
 }
 
+// Smallest / largest int over each row of 16 lanes (every lane of the row
+// gets it): DPP quad permutations, then the half-row and row mirrors.
+template <int CTRL>
+__device__ __forceinline__ int dpp_int(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int row16_min(int v) {
+  v = min(v, dpp_int<0xB1>(v));
+  v = min(v, dpp_int<0x4E>(v));
+  v = min(v, dpp_int<0x141>(v));
+  return min(v, dpp_int<0x140>(v));
+}
+__device__ __forceinline__ int row16_max(int v) {
+  v = max(v, dpp_int<0xB1>(v));
+  v = max(v, dpp_int<0x4E>(v));
+  v = max(v, dpp_int<0x141>(v));
+  return max(v, dpp_int<0x140>(v));
+}
+
 // Sequence whose chunk range holds global chunk g: the last b with base[b] <= g.
 __device__ __forceinline__ int chunk_seq(const int64_t* base, int num_seqs, int64_t g) {
   int lo = 0, hi = num_seqs;   // base[lo] <= g < base[hi]
@@ -261,13 +280,38 @@ __global__ __launch_bounds__(kCWaves * 64, 2) void attn_cand_kernel(CandArgs a) 
                                   int64_t* __restrict__ dt, const float* __restrict__ spos,
                                   const float* __restrict__ stime, int t) __attribute__((always_inline)) {
     if (t + 1 < ntiles) issue_hist(t + 1, dk, dv, dt);
-    // timestamp range of each 32-key block (lanes 0-31: block 0, 32-63: block 1)
-    int64_t kmin = INT64_MAX, kmax = INT64_MIN;
-    if (has_time && t * kCBN + lane < n) kmin = kmax = rt[lane];
-    for (int o = 1; o < 32; o <<= 1) {
-      const int64_t y0 = __shfl_xor(kmin, o, 64), y1 = __shfl_xor(kmax, o, 64);
-      kmin = y0 < kmin ? y0 : kmin;
-      kmax = y1 > kmax ? y1 : kmax;
+    // timestamp range of each 32-key block (lanes 0-31: block 0, 32-63:
+    // block 1). When every key of the tile is within 2^31 of its first key,
+    // as offsets from that key in 32-bit DPP reductions; otherwise 64-bit
+    // cross-lane reductions.
+    int64_t bmin2[2] = {INT64_MAX, INT64_MAX}, bmax2[2] = {INT64_MIN, INT64_MIN};
+    if (has_time) {
+      const bool valid = t * kCBN + lane < n;
+      const int64_t tv = valid ? rt[lane] : 0;
+      const int64_t base = uniform_i64(rt[0]);   // key t * kCBN, inside the history
+      const int64_t d = tv - base;
+      const bool near = !valid || (d >= int64_t(INT32_MIN) && d <= int64_t(INT32_MAX));
+      if (__builtin_amdgcn_ballot_w64(!near) == 0) {
+        const int mn = row16_min(valid ? static_cast<int>(d) : INT32_MAX);
+        const int mx = row16_max(valid ? static_cast<int>(d) : INT32_MIN);
+#pragma unroll
+        for (int kvb = 0; kvb < 2; ++kvb) {
+          bmin2[kvb] = base + min(__builtin_amdgcn_readlane(mn, 32 * kvb), __builtin_amdgcn_readlane(mn, 32 * kvb + 16));
+          bmax2[kvb] = base + max(__builtin_amdgcn_readlane(mx, 32 * kvb), __builtin_amdgcn_readlane(mx, 32 * kvb + 16));
+        }
+      } else {
+        int64_t kmin = valid ? tv : INT64_MAX, kmax = valid ? tv : INT64_MIN;
+        for (int o = 1; o < 32; o <<= 1) {
+          const int64_t y0 = __shfl_xor(kmin, o, 64), y1 = __shfl_xor(kmax, o, 64);
+          kmin = y0 < kmin ? y0 : kmin;
+          kmax = y1 > kmax ? y1 : kmax;
+        }
+#pragma unroll
+        for (int kvb = 0; kvb < 2; ++kvb) {
+          bmin2[kvb] = uniform_i64(__shfl(kmin, 32 * kvb, 64));
+          bmax2[kvb] = uniform_i64(__shfl(kmax, 32 * kvb, 64));
+        }
+      }
     }
 #pragma unroll
     for (int kvb = 0; kvb < 2; ++kvb) {
@@ -280,7 +324,7 @@ __global__ __launch_bounds__(kCWaves * 64, 2) void attn_cand_kernel(CandArgs a) 
       int tlo = 0, thi = 0;
       bool time_const = true, narrow = false;
       if (has_time) {
-        const int64_t bmin = uniform_i64(__shfl(kmin, 32 * kvb, 64)), bmax = uniform_i64(__shfl(kmax, 32 * kvb, 64));
+        const int64_t bmin = bmin2[kvb], bmax = bmax2[kvb];
         tlo = __builtin_amdgcn_readfirstlane(time_bucket64(tc_min - bmax, Bt));
         thi = __builtin_amdgcn_readfirstlane(time_bucket64(tc_max - bmin, Bt));
         time_const = tlo == thi;
