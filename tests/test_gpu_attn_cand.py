@@ -78,18 +78,29 @@ def test_bias_subsets_scale_and_divisor(hstu, pos, time):
 
 def test_full_size_sampled_candidates(hstu):
     """16 histories log-uniform in [1024, 8192] with 1024 candidates each: the
-    GPU scores all 16384; 4 candidates of every sequence (first, last, two in
-    between) are checked against the oracle."""
+    GPU scores all 16384; 32 candidates of every sequence (both ends of each
+    128-candidate workgroup tile, the rest drawn with a fixed seed) are
+    checked against the oracle, which scores each candidate on its own (the
+    full oracle takes minutes)."""
     wl = make_workload("c6")
     got = _gpu(hstu, wl)
     c = wl.cand
     coff = c["offsets"]
+    rng = np.random.default_rng(61)
     pick = []
+    per = []
     for b in range(coff.size - 1):
         lo, hi = int(coff[b]), int(coff[b + 1])
-        pick += sorted({lo, lo + (hi - lo) // 3, lo + 2 * (hi - lo) // 3, hi - 1})
+        chosen = {lo, hi - 1}
+        for t0 in range(lo, hi, 128):
+            chosen |= {t0, min(t0 + 127, hi - 1)}
+        chosen = sorted(chosen)[:18]
+        rest = np.setdiff1d(np.arange(lo, hi), chosen)
+        chosen = sorted(set(chosen) | set(rng.choice(rest, size=32 - len(chosen), replace=False).tolist()))
+        pick += chosen
+        per.append(len(chosen))
     pick = np.array(pick)
-    per = np.array([4] * (coff.size - 1))
+    per = np.array(per)
     sub = dict(offsets=offsets_from_lengths(per), q=c["q"][pick], k=c["k"][pick], v=c["v"][pick],
                timestamps=c["timestamps"][pick])
     ref = _ref(wl, c=sub)
