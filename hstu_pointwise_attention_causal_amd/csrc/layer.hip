@@ -29,6 +29,20 @@ namespace hstu {
 namespace {
 
 constexpr int GBK = 64;            // K per stage of K-major operands, and the K granularity of row-major ones
+constexpr int kStoreNonTemporal = 2;   // buffer store cache policy: the nt bit
+// Outputs at least this large are stored with the non-temporal hint. Measured
+// on the jagged layer (49404 tokens, 200 MB of G): its UVQK GEMM 162 -> 146
+// us and the layer 5% faster; on the 8192-token stack (34 MB of G, which the
+// attention then reads back) the hint made the layer 1% slower, so smaller
+// outputs keep the default policy.
+constexpr int64_t kStreamOutBytes = int64_t(96) << 20;
+
+// One 16-byte store, with the non-temporal hint when NT.
+template <bool NT, class V>
+__device__ __forceinline__ void store16(V* p, V v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 
 __device__ __forceinline__ uint32_t clamp_u32(int64_t bytes) {
   return bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes));
@@ -175,6 +189,10 @@ __device__ __forceinline__ void read_frags(FragSet<S>& f, const char* __restrict
 // products they overlap (the compiler would otherwise sink each read to its
 // first use). All buffers arrive as __restrict__ pointers, so the compiler
 // knows the reads never touch the stage being filled.
+//
+// With `pre` (the overlapped epilogue of the previous tile requested this
+// tile's first two stages, then issued its MB * 4 stores), step 0 issues no
+// loads and waits for stage 1 with those stores still allowed in flight.
 template <class S>
 __device__ __forceinline__ void gemm_step(const GemmArgs& g, const char* __restrict__ rs_a,
                                           const char* __restrict__ rs_b, char* __restrict__ ds_a,
@@ -183,8 +201,9 @@ __device__ __forceinline__ void gemm_step(const GemmArgs& g, const char* __restr
                                           int k_end, const char* abase, int arows, const char* bbase, int brows,
                                           int w, int lane, const Frag<S::kAT, S::ACH> (&af_)[S::MB],
                                           const Frag<S::kBT, S::BCH> (&bf_)[S::NB], FragSet<S>& cur,
-                                          f32x16_t (&acc)[S::MB][S::NB]) {
-  if (kt + S::kStagesAhead < nsteps) {
+                                          f32x16_t (&acc)[S::MB][S::NB], bool pre = false) {
+  const bool pre0 = pre && kt == 0;
+  if (kt + S::kStagesAhead < nsteps && !pre0) {
     const int k0 = kbase_elems + (kt + S::kStagesAhead) * S::kBK;
     issue_operand<S, S::kAT, S::ACH, S::kAPer>(operand_rsrc<S::kAT>(abase, g.lda, arows, arows, k0, k_end, g.K),
                                               g.lda, w, lane, ds_a);
@@ -202,7 +221,9 @@ __device__ __forceinline__ void gemm_step(const GemmArgs& g, const char* __restr
       // The next stage must have landed; the ones issued since may stay in flight.
       asm volatile("" ::: "memory");
       const int ahead = nsteps - 1 - (kt + 1);   // stages issued beyond the next one, capped below
-      if (ahead >= S::kStagesAhead - 1) {
+      if (pre0) {
+        wait_vm_lgkm0<S::MB * 4>();
+      } else if (ahead >= S::kStagesAhead - 1) {
         if constexpr (S::kStagesAhead == 3) wait_vm_lgkm0<2 * S::kLoadsPerStage>();
         else if constexpr (S::kStagesAhead == 2) wait_vm_lgkm0<S::kLoadsPerStage>();
         else wait_vm_lgkm0<0>();
@@ -226,11 +247,21 @@ __device__ __forceinline__ void gemm_step(const GemmArgs& g, const char* __restr
   }
 }
 
-template <int EPI, int BM, int BN, int WM, int WN, int ST, bool AT, bool BT, int BK>
+template <int EPI, int BM, int BN, int WM, int WN, int ST, bool AT, bool BT, int BK, bool OVL, bool NT>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 2) void gemm_kernel(GemmArgs g) {
   using S = GemmShape<BM, BN, WM, WN, ST, AT, BT, BK>;
+  // OVL (looping workgroups, bf16 outputs rounded once): the epilogue stages
+  // bf16 values in an area of its own, so the stage buffers are free once the
+  // last K step has passed its barrier. The next tile's first stage is then
+  // requested before this tile's epilogue, and the barrier that publishes it
+  // waits for those loads only (vmcnt counts the epilogue's stores, issued
+  // after them, as still in flight): the epilogue hides the load latency and
+  // the stores drain under the next tile's first products.
+  static_assert(!OVL || ((EPI == kEpiNone || EPI == kEpiSilu) && !AT && !BT && ST == 2 && WN == 64),
+                "overlapped epilogue: row-major operands, two stages, bf16 output rounded once");
   __shared__ __attribute__((aligned(16))) char sa[ST][BM * BK * 2];
   __shared__ __attribute__((aligned(16))) char sb[ST][BN * BK * 2];
+  __shared__ __attribute__((aligned(16))) char so[OVL ? S::kWaves * 32 * WN * 2 : 16];
 
   // Workgroups are dealt to the 8 XCDs in turn (block b to XCD b % 8). Tile t
   // of the row-major tile order goes to a block on XCD t / ceil-share, so each
@@ -243,21 +274,27 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 2) void gemm_kernel(Gem
   // a tile's stores drain while the next tile's products run.
   const int tiles_n = (g.N + BN - 1) / BN;
   const int tiles = ((g.M + BM - 1) / BM) * tiles_n, q = tiles / 8, r = tiles % 8;
+  auto tile_origin = [&](int vb_, int& m0_, int& n0_) __attribute__((always_inline)) {
+    const int xcd = vb_ % 8;
+    const int t = xcd * q + min(xcd, r) + vb_ / 8;
+    int tm, tn;
+    if (g.group_m > 1) {
+      const int tiles_m = (g.M + BM - 1) / BM;
+      const int band = t / (g.group_m * tiles_n), idx = t - band * g.group_m * tiles_n;
+      const int rows = min(g.group_m, tiles_m - band * g.group_m);
+      tm = band * g.group_m + idx % rows;
+      tn = idx / rows;
+    } else {
+      tm = t / tiles_n;
+      tn = t % tiles_n;
+    }
+    m0_ = tm * BM;
+    n0_ = tn * BN;
+  };
+  bool stage0_ready = false;   // OVL: this tile's first stage was requested and has landed
   for (int vb = blockIdx.x; vb < tiles; vb += gridDim.x) {
-  const int xcd = vb % 8;
-  const int t = xcd * q + min(xcd, r) + vb / 8;
-  int tm, tn;
-  if (g.group_m > 1) {
-    const int tiles_m = (g.M + BM - 1) / BM;
-    const int band = t / (g.group_m * tiles_n), idx = t - band * g.group_m * tiles_n;
-    const int rows = min(g.group_m, tiles_m - band * g.group_m);
-    tm = band * g.group_m + idx % rows;
-    tn = idx / rows;
-  } else {
-    tm = t / tiles_n;
-    tn = t % tiles_n;
-  }
-  const int m0 = tm * BM, n0 = tn * BN;
+  int m0, n0;
+  tile_origin(vb, m0, n0);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
@@ -288,20 +325,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 2) void gemm_kernel(Gem
 #pragma unroll
   for (int nb = 0; nb < S::NB; ++nb) bf_[nb].init(wn * WN + nb * 32, lane);
 
-  // stages 0 .. ST-2 in flight, wait for stage 0
+  if (!stage0_ready) {
+    // stages 0 .. ST-2 in flight, wait for stage 0
 #pragma unroll
-  for (int s_ = 0; s_ < ST - 1; ++s_)
-    if (s_ < nsteps) {
-      const int k0 = kbase_elems + s_ * BK;
-      issue_operand<S, AT, S::ACH, S::kAPer>(operand_rsrc<AT>(abase, g.lda, arows, arows, k0, k_end, g.K), g.lda, w,
-                                            lane, sa[s_]);
-      issue_operand<S, BT, S::BCH, S::kBPer>(operand_rsrc<BT>(bbase, g.ldb, brows, brows, k0, k_end, g.K), g.ldb, w,
-                                            lane, sb[s_]);
-    }
-  // wait for stage 0 only; the later ones stay in flight
-  if (nsteps >= ST - 1) wait_vm_lgkm0<(ST - 2) * S::kLoadsPerStage>();
-  else wait_vm_lgkm0<0>();
-  __syncthreads();
+    for (int s_ = 0; s_ < ST - 1; ++s_)
+      if (s_ < nsteps) {
+        const int k0 = kbase_elems + s_ * BK;
+        issue_operand<S, AT, S::ACH, S::kAPer>(operand_rsrc<AT>(abase, g.lda, arows, arows, k0, k_end, g.K), g.lda,
+                                              w, lane, sa[s_]);
+        issue_operand<S, BT, S::BCH, S::kBPer>(operand_rsrc<BT>(bbase, g.ldb, brows, brows, k0, k_end, g.K), g.ldb,
+                                              w, lane, sb[s_]);
+      }
+    // wait for stage 0 only; the later ones stay in flight
+    if (nsteps >= ST - 1) wait_vm_lgkm0<(ST - 2) * S::kLoadsPerStage>();
+    else wait_vm_lgkm0<0>();
+    __syncthreads();
+  }
   // stages rotate statically; step t reads stage t % ST, fills (t + ST - 1) % ST
   // and ends with the first fragments of stage (t + 1) % ST in registers
   FragSet<S> cur;
@@ -312,8 +351,95 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 2) void gemm_kernel(Gem
       if (kt + u >= nsteps) break;
       gemm_step<S>(g, sa[u], sb[u], sa[(u + ST - 1) % ST], sb[(u + ST - 1) % ST], sa[(u + 1) % ST],
                    sb[(u + 1) % ST], kt + u, nsteps, kbase_elems, k_end, abase, arows, bbase, brows, w, lane, af_,
-                   bf_, cur, acc);
+                   bf_, cur, acc, OVL && stage0_ready);
     }
+  }
+
+  if constexpr (OVL) {
+    // (the bias loads go out before the next stage's, so that waiting for
+    // them does not wait for the stage)
+    float bias[S::NB][4][4];
+#pragma unroll
+    for (int nb = 0; nb < S::NB; ++nb)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const int n = n0 + wn * WN + nb * 32 + 8 * jq + 4 * lh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bias[nb][jq][i] = (g.bias && n + i < g.N) ? g.bias[n + i] : 0.f;
+      }
+    // The last K step ended with a barrier after every wave's final fragment
+    // reads, so both stage buffers are free: request the next tile's first two
+    // stages now, stage s into buffer s. (An odd step count would leave the
+    // first stage in buffer 1: those tiles take the plain prologue.)
+    const int vn = vb + static_cast<int>(gridDim.x);
+    stage0_ready = vn < tiles && nsteps > 0 && nsteps % ST == 0;
+    if (stage0_ready) {
+      int m1, n1;
+      tile_origin(vn, m1, n1);
+      const char* a1 = static_cast<const char*>(g.a) + static_cast<int64_t>(m1) * g.lda * 2;
+      const char* b1 = static_cast<const char*>(g.b) + static_cast<int64_t>(n1) * g.ldb * 2;
+#pragma unroll
+      for (int s_ = 0; s_ < ST; ++s_) {
+        const int k0 = kbase_elems + s_ * BK;
+        issue_operand<S, false, S::ACH, S::kAPer>(
+            operand_rsrc<false>(a1, g.lda, g.M - m1, g.M - m1, k0, k_end, g.K), g.lda, w, lane, sa[s_]);
+        issue_operand<S, false, S::BCH, S::kBPer>(
+            operand_rsrc<false>(b1, g.ldb, g.N - n1, g.N - n1, k0, k_end, g.K), g.ldb, w, lane, sb[s_]);
+      }
+    }
+    // Epilogue: acc[mb][nb][4 jq + i] holds C[m][n + i] for m = 32 mb + lr,
+    // n = 32 nb + 8 jq + 4 lh (wave-tile coordinates; the products ran as
+    // B A^T). Each 32-row slice is rounded to bf16 once, staged in the wave's
+    // 32 x 64 area (8-byte pieces, 16-byte chunks XOR-swizzled by row / 2) and
+    // read back as one 16-byte chunk per lane, 8 rows per store. The stores
+    // are buffer stores, issued by every lane (an index outside the tile's
+    // rows or columns is past the resource and dropped), so each wave issues
+    // exactly MB * 4 of them, which the wait below counts. With NT they
+    // carry the non-temporal hint: the retrieval head's logits are written
+    // once and not read back here, and without the hint they drained 22%
+    // slower.
+    char* stg = so + w * (32 * WN * 2);
+    const int rows_here = min(BM, g.M - m0);
+    const int64_t span = static_cast<int64_t>(rows_here - 1) * g.ldc * 2 + static_cast<int64_t>(g.N) * 2;
+    const uint32_t oob = clamp_u32(span);
+    const __amdgpu_buffer_rsrc_t rc_out = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char*>(g.c) + static_cast<int64_t>(m0) * g.ldc * 2, 0, static_cast<int>(oob), kRsrcFlags);
+    const int rr = lane >> 3, rc = lane & 7;
+#pragma unroll
+    for (int mb = 0; mb < S::MB; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < S::NB; ++nb)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          bf16x4_t x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = acc[mb][nb][4 * jq + i] + bias[nb][jq][i];
+            if (EPI == kEpiSilu) v = silu_f32(v);
+            x[i] = static_cast<__bf16>(v);
+          }
+          const int c16 = nb * 4 + jq;
+          *reinterpret_cast<bf16x4_t*>(stg + lr * (WN * 2) + ((c16 ^ ((lr >> 1) & 7)) << 4) + lh * 8) = x;
+        }
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int row = rr + 8 * it;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + row * (WN * 2) + ((rc ^ ((row >> 1) & 7)) << 4));
+        const int ml = wm * WM + mb * 32 + row, n = n0 + wn * WN + 8 * rc;
+        const uint32_t off = (ml < rows_here && n < g.N)
+                                 ? static_cast<uint32_t>((static_cast<int64_t>(ml) * g.ldc + n) * 2)
+                                 : oob;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rc_out, off, 0, NT ? kStoreNonTemporal : 0);
+      }
+    }
+    if (stage0_ready) {
+      // the next tile's first stage has landed (its second stage and the
+      // stores may stay in flight); the barrier publishes it
+      wait_vm_lgkm0<S::MB * 4 + S::kLoadsPerStage>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    continue;
   }
 
   // Epilogue. The products ran as B A^T, so acc[mb][nb][4 jq + i] holds
@@ -365,8 +491,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 2) void gemm_kernel(Gem
       if constexpr (EPI == kEpiF32) {
         float* op = reinterpret_cast<float*>(cp) + static_cast<int64_t>(blockIdx.y) * g.split_stride +
                     static_cast<int64_t>(m) * g.ldc + n;
-        *reinterpret_cast<f32x4_t*>(op) = lo;
-        *reinterpret_cast<f32x4_t*>(op + 4) = hi;
+        store16<NT>(reinterpret_cast<f32x4_t*>(op), lo);
+        store16<NT>(reinterpret_cast<f32x4_t*>(op + 4), hi);
         continue;
       }
       float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -383,12 +509,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 2) void gemm_kernel(Gem
           pre[i] = static_cast<__bf16>(x[i]);
           out[i] = static_cast<__bf16>(silu_f32(x[i]));
         }
-        *reinterpret_cast<bf16x8_t*>(static_cast<char*>(g.c2) + (static_cast<int64_t>(m) * g.ldc2 + n) * 2) = pre;
+        store16<NT>(reinterpret_cast<bf16x8_t*>(static_cast<char*>(g.c2) + (static_cast<int64_t>(m) * g.ldc2 + n) * 2),
+                    pre);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) out[i] = static_cast<__bf16>(x[i]);
       }
-      *reinterpret_cast<bf16x8_t*>(cp + (static_cast<int64_t>(m) * g.ldc + n) * 2) = out;
+      store16<NT>(reinterpret_cast<bf16x8_t*>(cp + (static_cast<int64_t>(m) * g.ldc + n) * 2), out);
     }
   }
   // the staging area (A stage buffers) is read back before the next tile's loads refill it
@@ -456,17 +583,22 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(LnArgs a) {
 }  // namespace
 
 namespace {
-template <int EPI, int BM, int BN, int WM, int WN, int ST, bool AT, bool BT, int BK = 64>
+template <int EPI, int BM, int BN, int WM, int WN, int ST, bool AT, bool BT, int BK = 64, bool OVL = false,
+          bool NT = false>
 hipError_t launch_gemm_shape(const GemmArgs& g, int splits, hipStream_t stream) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   const int grid = g.blocks > 0 && g.blocks < tiles ? g.blocks : tiles;
-  hipLaunchKernelGGL((gemm_kernel<EPI, BM, BN, WM, WN, ST, AT, BT, BK>), dim3(grid, splits),
+  hipLaunchKernelGGL((gemm_kernel<EPI, BM, BN, WM, WN, ST, AT, BT, BK, OVL, NT>), dim3(grid, splits),
                      dim3((BM / WM) * (BN / WN) * 64), 0, stream, g);
   return hipGetLastError();
 }
 template <int EPI, bool AT, bool BT>
 hipError_t launch_gemm_epi(const GemmArgs& g, int splits, hipStream_t stream) {
-  // wide outputs: 256 x 256 tiles, 8 waves of 128 x 64; narrow ones: 128 x 128, 4 waves of 64 x 64
+  // wide outputs: 256 x 256 tiles, 8 waves of 128 x 64; narrow ones: 128 x 128, 4 waves of 64 x 64.
+  // Large SiLU outputs (the UVQK projection's G and Z) take the non-temporal stores.
+  if constexpr ((EPI == kEpiSilu || EPI == kEpiSiluPair) && !AT && !BT)
+    if (g.N >= 1024 && g.stream_out)
+      return launch_gemm_shape<EPI, 256, 256, 128, 64, 2, AT, BT, 64, false, true>(g, splits, stream);
   if (g.N >= 1024) return launch_gemm_shape<EPI, 256, 256, 128, 64, 2, AT, BT>(g, splits, stream);
   return launch_gemm_shape<EPI, 128, 128, 64, 64, 2, AT, BT>(g, splits, stream);
 }
@@ -492,9 +624,12 @@ hipError_t check_gemm(const GemmArgs& g, int epi, bool a_kmajor, bool b_kmajor, 
 }
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& g, int epi, bool a_kmajor, bool b_kmajor, int splits, hipStream_t stream) {
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  if (hipError_t e = check_gemm(g, epi, a_kmajor, b_kmajor, splits); e != hipSuccess) return e;
+hipError_t launch_gemm(const GemmArgs& g_in, int epi, bool a_kmajor, bool b_kmajor, int splits, hipStream_t stream) {
+  if (g_in.M <= 0 || g_in.N <= 0) return hipSuccess;
+  if (hipError_t e = check_gemm(g_in, epi, a_kmajor, b_kmajor, splits); e != hipSuccess) return e;
+  GemmArgs g = g_in;
+  // (split partials are read back at once by the sum: they keep the default policy)
+  g.stream_out = epi != kEpiF32 && static_cast<int64_t>(g.M) * g.N * 2 >= kStreamOutBytes;
   TimedScope timed(epi == kEpiResidual ? kTimedGemmOut : kTimedGemmUvqk, stream);
   if (!a_kmajor && !b_kmajor) {
     switch (epi) {
@@ -514,10 +649,15 @@ hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream) {
   return launch_gemm(g, epi, false, false, 1, stream);
 }
 
-hipError_t launch_head_gemm(const GemmArgs& g, hipStream_t stream) {
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  if (hipError_t e = check_gemm(g, kEpiNone, false, false, 1); e != hipSuccess) return e;
+hipError_t launch_head_gemm(const GemmArgs& g_in, hipStream_t stream) {
+  if (g_in.M <= 0 || g_in.N <= 0) return hipSuccess;
+  if (hipError_t e = check_gemm(g_in, kEpiNone, false, false, 1); e != hipSuccess) return e;
+  GemmArgs g = g_in;
+  g.stream_out = static_cast<int64_t>(g.M) * g.N * 2 >= kStreamOutBytes;
   TimedScope timed(kTimedHeadGemm, stream);
+  // wide outputs loop over 256 x 256 tiles with the overlapped epilogue
+  if (g.N >= 1024 && g.blocks > 0 && g.ldc <= (int64_t(1) << 22))
+    return launch_gemm_shape<kEpiNone, 256, 256, 128, 64, 2, false, false, 64, true, true>(g, 1, stream);
   return launch_gemm_epi<kEpiNone, false, false>(g, 1, stream);
 }
 

@@ -137,3 +137,28 @@ def test_dim_1024_with_strided_rows_and_logits(hstu):
     print(f"dim 1024 strided err {err:.2e}")
     assert err <= TOL_BF16
     assert bool((out_buf[:, vocab:] == -5.0).all())   # padding untouched
+
+
+def test_looping_workgroups_ragged_rows_and_padded_logits(hstu):
+    """600 rows x 24008 items at dim 512: 3 x 94 tiles of 256 x 256, more
+    than the compute units, so workgroups loop over tiles and request the next
+    tile's first stage before storing the current one; rows and items ragged
+    against the tiles, logits written into rows padded past the vocabulary.
+    Every logit against the oracle."""
+    import torch
+    rng = np.random.default_rng(83)
+    rows, dim, vocab = 600, 512, 24008
+    x = (rng.standard_normal((rows, dim)) * rng.uniform(0.1, 4.0, (rows, 1))).astype(np.float32)
+    table = (0.02 * rng.standard_normal((vocab, dim))).astype(np.float32)
+    gamma = (1.0 + 0.1 * rng.standard_normal(dim)).astype(np.float32)
+    xd = to_dev(x, torch.bfloat16)
+    td = to_dev(table, torch.bfloat16)
+    out_buf = torch.full((rows, vocab + 40), -5.0, dtype=torch.bfloat16, device="cuda:0")
+    out = out_buf[:, :vocab]
+    hstu.head_fwd(xd, td, gamma=to_dev(gamma, torch.float32), eps=1e-6, out=out)
+    torch.cuda.synchronize()
+    ref = orc.head_fwd(xd.float().cpu().numpy(), td.float().cpu().numpy(), gamma, 1e-6)
+    err = rel_err(out.float().cpu().numpy(), ref)
+    print(f"looping head err {err:.2e}")
+    assert err <= TOL_BF16
+    assert bool((out_buf[:, vocab:] == -5.0).all())   # padding untouched
