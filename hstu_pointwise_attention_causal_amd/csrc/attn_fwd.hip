@@ -641,25 +641,40 @@ __global__ __launch_bounds__(kMetaPerTile * 64) void attn_block_meta_kernel(Attn
   const int n = item.n;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int jb = qt * kMetaPerTile + w;       // 32-key block of this wave
-  const int key = jb * 32 + (lane >> 1);      // two lanes per key, half the dims each
   if (jb * 32 >= n) return;
-  const bool inside = key < n;
-  float sq = 0.f;
-  if (inside) {
-    const __bf16* kp = static_cast<const __bf16*>(a.k) + (seq0 + key) * a.ldk + h * DQK + (lane & 1) * (DQK / 2);
+  // Each load instruction covers RPI whole key rows (16-byte chunk lane % CPR
+  // of row lane / CPR), so every instruction reads contiguous row segments;
+  // a row's sum of squares is then reduced over its CPR lanes.
+  constexpr int CPR = DQK / 8, RPI = 64 / CPR, NI = 32 / RPI;
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "key row of 4, 8 or 16 chunks");
+  const int c = lane % CPR, rsub = lane / CPR;
+  bf16x8_t x[NI];
 #pragma unroll
-    for (int c = 0; c < DQK / 16; ++c) {
-      const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(kp + c * 8);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sq = fmaf(static_cast<float>(x[i]), static_cast<float>(x[i]), sq);
-    }
+  for (int i = 0; i < NI; ++i) {
+    const int key = jb * 32 + i * RPI + rsub;
+    x[i] = key < n ? *reinterpret_cast<const bf16x8_t*>(static_cast<const __bf16*>(a.k) + (seq0 + key) * a.ldk +
+                                                        h * DQK + c * 8)
+                   : bf16x8_t{};
   }
-  sq += __shfl_xor(sq, 1, 64);
-  float kn = __builtin_sqrtf(sq);
-  for (int o = 2; o < 64; o <<= 1) kn = fmaxf(kn, __shfl_xor(kn, o, 64));
+  float kn = 0.f;
+  bool nan_seen = false;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sq = fmaf(static_cast<float>(x[i][e]), static_cast<float>(x[i][e]), sq);
+    sq += dpp_row<0xB1>(sq);                         // quad [1,0,3,2]
+    sq += dpp_row<0x4E>(sq);                         // quad [2,3,0,1]
+    if constexpr (CPR >= 8) sq += dpp_row<0x141>(sq);   // half-row mirror
+    if constexpr (CPR >= 16) sq += dpp_row<0x140>(sq);  // row mirror
+    nan_seen |= sq != sq;
+    kn = fmaxf(kn, __builtin_sqrtf(sq));
+  }
+  for (int o = CPR; o < 64; o <<= 1) kn = fmaxf(kn, __shfl_xor(kn, o, 64));
   // a NaN norm must keep the polynomial path off: max() drops NaN, so propagate it explicitly
-  const uint64_t nan_lanes = __builtin_amdgcn_ballot_w64(sq != sq);
-  if (nan_lanes) kn = __builtin_nanf("");
+  if (__builtin_amdgcn_ballot_w64(nan_seen)) kn = __builtin_nanf("");
+  const int key = jb * 32 + (lane >> 1);
+  const bool inside = key < n;
   int64_t tmin = INT64_MAX, tmax = INT64_MIN;
   if (a.ts) {
     const int64_t t = inside ? a.ts[seq0 + key] : 0;
