@@ -8,9 +8,10 @@
 //   sl_offsets_kernel   new_offsets = exclusive scan of min(n_b, L) (one block)
 //   sl_select_kernel    one block per sequence: the L-th smallest key by a
 //                       three-pass radix select (11 + 11 + 10 bits, LDS
-//                       histograms), then a compaction pass in position order
-//                       that keeps keys below it and the first ones equal to
-//                       it, writing the kept tokens' input positions; a
+//                       histograms), then a compaction in position order (per-
+//                       wave ballot counts, one barrier, a placing walk) that
+//                       keeps keys below it and the first ones equal to it,
+//                       writing the kept tokens' input positions; a
 //                       sequence of up to 16384 tokens works on an LDS copy
 //                       of its keys
 //   gather_rows_kernel  dst row r = src row index[r] (a wave per wide row, a
@@ -141,29 +142,52 @@ __device__ __forceinline__ void select_compact(const uint32_t* __restrict__ key,
 
   // ---- compaction in position order. A kept token's output position is the
   // number of keys below kstar before it plus min(equal keys before it,
-  // take_eq): one block scan of packed counts (below in the low 16 bits,
-  // equal in the high 16; a block holds at most 1024 of each) gives both.
-  uint32_t lt_carry = 0, eq_carry = 0;
-  for (int c0 = 0; c0 < nn; c0 += kSelThreads) {
-    const int i = c0 + tid;
-    const bool valid = i < nn;
-    const uint32_t kv = valid ? key[i] : 0u;
-    const bool lt = valid && kv < kstar, eq = valid && kv == kstar;
-    uint32_t total;
-    const uint32_t before = block_excl((lt ? 1u : 0u) | (eq ? 0x10000u : 0u), wtot, total);
-    const uint32_t lt_before = lt_carry + (before & 0xFFFFu), eq_before = eq_carry + (before >> 16);
+  // take_eq). Wave w owns a contiguous run of positions: it counts its keys
+  // below and equal to kstar (ballots), one barrier publishes the per-wave
+  // counts, and a second walk over the run places each kept token from its
+  // wave's starting counts and the ballot bits of the lanes before it.
+  const int lane = tid & 63, w = tid >> 6;
+  constexpr int kWaves = kSelThreads / 64;
+  const int per = (((nn + kWaves - 1) / kWaves) + 63) & ~63;
+  const int lo = min(nn, w * per), hi = min(nn, lo + per);
+  uint32_t nlt = 0, neq = 0;
+  for (int i0 = lo; i0 < hi; i0 += 64) {
+    const int i = i0 + lane;
+    const uint32_t kv = i < hi ? key[i] : 0u;
+    nlt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < hi && kv < kstar));
+    neq += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < hi && kv == kstar));
+  }
+  if (lane == 0) {
+    wtot[w] = nlt;
+    wtot[kWaves + w] = neq;
+  }
+  __syncthreads();
+  uint32_t lt_run = 0, eq_run = 0;
+  for (int j = 0; j < w; ++j) {
+    lt_run += wtot[j];
+    eq_run += wtot[kWaves + j];
+  }
+  for (int i0 = lo; i0 < hi; i0 += 64) {
+    const int i = i0 + lane;
+    const uint32_t kv = i < hi ? key[i] : 0u;
+    const bool lt = i < hi && kv < kstar, eq = i < hi && kv == kstar;
+    const uint64_t bl = __builtin_amdgcn_ballot_w64(lt), be = __builtin_amdgcn_ballot_w64(eq);
+    const uint32_t lt_before = lt_run + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bl >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bl), 0u));
+    const uint32_t eq_before = eq_run + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(be >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(be), 0u));
     if (lt || (eq && eq_before < take_eq)) {
       const int64_t pos = static_cast<int64_t>(lt_before) + min(eq_before, take_eq);
       if (base + pos < T) out[base + pos] = s + i;
     }
-    lt_carry += total & 0xFFFFu;
-    eq_carry += total >> 16;
+    lt_run += __builtin_popcountll(bl);
+    eq_run += __builtin_popcountll(be);
   }
 }
 
 __global__ __launch_bounds__(kSelThreads) void sl_select_kernel(SlArgs a) {
   __shared__ uint32_t hist[2048];
-  __shared__ uint32_t wtot[kSelThreads / 64];
+  __shared__ uint32_t wtot[2 * (kSelThreads / 64)];
   __shared__ uint32_t sel[2];
   __shared__ uint32_t skeys[kSelLdsKeys];
   const int b = blockIdx.x, tid = threadIdx.x;
