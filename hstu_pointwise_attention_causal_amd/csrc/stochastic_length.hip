@@ -206,8 +206,20 @@ __global__ __launch_bounds__(kSelThreads) void sl_select_kernel(SlArgs a) {
   const int nn = static_cast<int>(n);   // n < T < 2^31
   const uint32_t cap = static_cast<uint32_t>(a.max_len);   // < n
   if (nn <= kSelLdsKeys) {
-    // one read of the keys from memory; the four passes over them then run from LDS
-    for (int i = tid; i < nn; i += kSelThreads) skeys[i] = key[i];
+    // one read of the keys from memory (every load in flight before the
+    // first LDS store); the passes over them then run from LDS
+    constexpr int kPer = kSelLdsKeys / kSelThreads;
+    uint32_t kr[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + j * kSelThreads;
+      kr[j] = i < nn ? key[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + j * kSelThreads;
+      if (i < nn) skeys[i] = kr[j];
+    }
     __syncthreads();
     select_compact(skeys, nn, cap, s, base, T, out, hist, wtot, sel);
   } else {
