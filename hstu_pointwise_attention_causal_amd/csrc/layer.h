@@ -36,7 +36,7 @@ struct GemmArgs {
   int M, N, K;
   int group_m;         // > 1: tile order in bands of group_m tile rows, column by column
   int blocks;          // > 0: that many workgroups (a multiple of 8), each looping over tiles; 0: one per tile
-  int stream_out;      // set by launch_gemm: outputs stored with the non-temporal hint (large outputs)
+  int stream_out;      // set by launch_gemm: large SiLU outputs stored with the non-temporal hint
 };
 
 // y = LN(x) * gamma + beta (optionally * gate), rows of `width` features, bf16 in/out.

@@ -30,11 +30,13 @@ namespace {
 
 constexpr int GBK = 64;            // K per stage of K-major operands, and the K granularity of row-major ones
 constexpr int kStoreNonTemporal = 2;   // buffer store cache policy: the nt bit
-// Outputs at least this large are stored with the non-temporal hint. Measured
-// on the jagged layer (49404 tokens, 200 MB of G): its UVQK GEMM 162 -> 146
-// us and the layer 5% faster; on the 8192-token stack (34 MB of G, which the
-// attention then reads back) the hint made the layer 1% slower, so smaller
-// outputs keep the default policy.
+// SiLU outputs (G of the UVQK projection) at least this large are stored with
+// the non-temporal hint. Measured on the jagged layer (49404 tokens, 200 MB of
+// G): its UVQK GEMM 162 -> 146 us and the layer 5% faster; on the 8192-token
+// stack (34 MB of G, which the attention then reads back) the hint made the
+// layer 1% slower, so smaller outputs keep the default policy, as do the other
+// epilogues (the residual projection's output is smaller than G, split
+// partials are read back at once by their sum).
 constexpr int64_t kStreamOutBytes = int64_t(96) << 20;
 
 // One 16-byte store, with the non-temporal hint when NT.
@@ -595,8 +597,8 @@ hipError_t launch_gemm_shape(const GemmArgs& g, int splits, hipStream_t stream) 
 template <int EPI, bool AT, bool BT>
 hipError_t launch_gemm_epi(const GemmArgs& g, int splits, hipStream_t stream) {
   // wide outputs: 256 x 256 tiles, 8 waves of 128 x 64; narrow ones: 128 x 128, 4 waves of 64 x 64.
-  // Large SiLU outputs (the UVQK projection's G and Z) take the non-temporal stores.
-  if constexpr ((EPI == kEpiSilu || EPI == kEpiSiluPair) && !AT && !BT)
+  // Large SiLU outputs (the forward UVQK projection's G) take the non-temporal stores.
+  if constexpr (EPI == kEpiSilu && !AT && !BT)
     if (g.N >= 1024 && g.stream_out)
       return launch_gemm_shape<EPI, 256, 256, 128, 64, 2, AT, BT, 64, false, true>(g, splits, stream);
   if (g.N >= 1024) return launch_gemm_shape<EPI, 256, 256, 128, 64, 2, AT, BT>(g, splits, stream);
@@ -628,8 +630,7 @@ hipError_t launch_gemm(const GemmArgs& g_in, int epi, bool a_kmajor, bool b_kmaj
   if (g_in.M <= 0 || g_in.N <= 0) return hipSuccess;
   if (hipError_t e = check_gemm(g_in, epi, a_kmajor, b_kmajor, splits); e != hipSuccess) return e;
   GemmArgs g = g_in;
-  // (split partials are read back at once by the sum: they keep the default policy)
-  g.stream_out = epi != kEpiF32 && static_cast<int64_t>(g.M) * g.N * 2 >= kStreamOutBytes;
+  g.stream_out = epi == kEpiSilu && static_cast<int64_t>(g.M) * g.N * 2 >= kStreamOutBytes;
   TimedScope timed(epi == kEpiResidual ? kTimedGemmOut : kTimedGemmUvqk, stream);
   if (!a_kmajor && !b_kmajor) {
     switch (epi) {
