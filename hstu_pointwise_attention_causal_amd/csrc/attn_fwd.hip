@@ -634,8 +634,13 @@ __global__ __launch_bounds__(SPLIT ? 2 * kThreads : kThreads, SPLIT ? 1 : 2) voi
 template <int DQK>
 __global__ __launch_bounds__(kMetaPerTile * 64) void attn_block_meta_kernel(AttnArgs a) {
   const int item_idx = blockIdx.x;
-  if (item_idx >= *a.item_count) return;
+  // the entry is read together with the count (the grid is the list's
+  // capacity, so the read stays inside the list); the empty asm keeps the
+  // compiler from sinking the entry's load below the branch
+  const int count = *a.item_count;
   const WorkItem item = reinterpret_cast<const WorkItem*>(a.items)[item_idx];
+  asm volatile("" ::"s"(item.seq0), "s"(item.n), "s"(item.packed), "s"(item.tile_base));
+  if (item_idx >= count) return;
   const int qt = item_qtile(item), h = item_head(item);
   const int64_t seq0 = item.seq0;
   const int n = item.n;
