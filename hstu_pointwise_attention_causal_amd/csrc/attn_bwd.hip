@@ -1102,8 +1102,12 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_q_kernel(AttnBwdArgs g)
           float pl, dl;
           silu_and_grad(fmaf(s[r], alpha_l, spos[pb] + stime[tbr]), pl, dl);
           if constexpr (MASKED) {
-            const bool valid = d >= 0 && kv < n && qrow < n;
-            emit(r, valid ? dl : 0.f);
+            // the mask is opaque to the compiler, which otherwise moved each
+            // pair's bucket lookups and SiLU' into a branch of its own (one
+            // exec-masked region per pair, its LDS reads serialised)
+            int keep = (d >= 0 && kv < n && qrow < n) ? -1 : 0;
+            asm("" : "+v"(keep));
+            emit(r, __int_as_float(__float_as_int(dl) & keep));
           } else {
             emit(r, dl);
           }
