@@ -641,12 +641,13 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const char* dst = rd + kk * 16 * DCH * 16;
+        bf16x8_t ob[NV];   // every fragment of the step read before the first product
 #pragma unroll
-        for (int nb = 0; nb < NV; ++nb) {
-          const bf16x8_t ob =
-              __builtin_shufflevector(tr_read(dst + d_tr0[nb]), tr_read(dst + d_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
-          dva[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], ob, dva[nb], 0, 0, 0);
-        }
+        for (int nb = 0; nb < NV; ++nb)
+          ob[nb] = __builtin_shufflevector(tr_read(dst + d_tr0[nb]), tr_read(dst + d_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
+        __builtin_amdgcn_sched_barrier(0);   // keeps the reads ahead: the scheduler sank each to its product
+#pragma unroll
+        for (int nb = 0; nb < NV; ++nb) dva[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], ob[nb], dva[nb], 0, 0, 0);
       }
       s_cur = sn;
     };
@@ -811,12 +812,13 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_kv_kernel(AttnBwdArgs g
 #pragma unroll
         for (int i = 0; i < 8; ++i) sa[i] = static_cast<__bf16>(ds[kk * 8 + i]);
         const char* qst = rq + kk * 16 * QCH * 16;
+        bf16x8_t qt[NQ];   // every fragment of the step read before the first product
 #pragma unroll
-        for (int nb = 0; nb < NQ; ++nb) {
-          const bf16x8_t qt =
-              __builtin_shufflevector(tr_read(qst + q_tr0[nb]), tr_read(qst + q_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
-          dka[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, qt, dka[nb], 0, 0, 0);
-        }
+        for (int nb = 0; nb < NQ; ++nb)
+          qt[nb] = __builtin_shufflevector(tr_read(qst + q_tr0[nb]), tr_read(qst + q_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
+        __builtin_amdgcn_sched_barrier(0);   // keeps the reads ahead: the scheduler sank each to its product
+#pragma unroll
+        for (int nb = 0; nb < NQ; ++nb) dka[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, qt[nb], dka[nb], 0, 0, 0);
       }
     };
 
@@ -1201,12 +1203,13 @@ __global__ __launch_bounds__(kKThreads, 1) void attn_bwd_q_kernel(AttnBwdArgs g)
 #pragma unroll
         for (int i = 0; i < 8; ++i) sa[i] = static_cast<__bf16>(da[kk * 8 + i] * static_cast<float>(gv[i]));
         const char* kst = rk + kk * 16 * KCH * 16;
+        bf16x8_t kb16[NQ];   // every fragment of the step read before the first product
 #pragma unroll
-        for (int nb = 0; nb < NQ; ++nb) {
-          const bf16x8_t kb16 =
-              __builtin_shufflevector(tr_read(kst + k_tr0[nb]), tr_read(kst + k_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
-          dqa[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, kb16, dqa[nb], 0, 0, 0);
-        }
+        for (int nb = 0; nb < NQ; ++nb)
+          kb16[nb] = __builtin_shufflevector(tr_read(kst + k_tr0[nb]), tr_read(kst + k_tr1[nb]), 0, 1, 2, 3, 4, 5, 6, 7);
+        __builtin_amdgcn_sched_barrier(0);   // keeps the reads ahead: the scheduler sank each to its product
+#pragma unroll
+        for (int nb = 0; nb < NQ; ++nb) dqa[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, kb16[nb], dqa[nb], 0, 0, 0);
       }
     };
 
