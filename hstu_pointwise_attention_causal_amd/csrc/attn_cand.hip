@@ -246,13 +246,14 @@ __global__ __launch_bounds__(kCWaves * 64, 2) void attn_cand_kernel(CandArgs a) 
 #pragma unroll
       for (int i = 0; i < 8; ++i) pa[i] = static_cast<__bf16>(p[kk * 8 + i]);
       const char* vb0 = vbuf + (kvb * 32 + kk * 16) * CH * 16;
+      bf16x8_t vf[NB];   // every fragment of the step read before the first product
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8_t vf =
-            __builtin_shufflevector(tr_read(vb0 + v_lds[nb]), tr_read(vb0 + v_lds[nb] + 8 * CH * 16), 0, 1, 2, 3, 4, 5,
-                                    6, 7);
-        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vf, oacc[nb], 0, 0, 0);
-      }
+      for (int nb = 0; nb < NB; ++nb)
+        vf[nb] = __builtin_shufflevector(tr_read(vb0 + v_lds[nb]), tr_read(vb0 + v_lds[nb] + 8 * CH * 16), 0, 1, 2, 3,
+                                         4, 5, 6, 7);
+      __builtin_amdgcn_sched_barrier(0);   // keeps the reads ahead: the scheduler sank each to its product
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vf[nb], oacc[nb], 0, 0, 0);
     }
   };
 
